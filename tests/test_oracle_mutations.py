@@ -1,0 +1,150 @@
+"""Planted mistakes in the oracle (on the CPU) must be caught by its pins.
+
+Each mutation is a plausible slip: a wrong slot order, an off-by-one, a dropped
+term, an unapplied weight, a flipped sign, a wrong tie-break, a wrong operand.
+For each one we swap the mutated function into the `oracle` package and run
+the pin tests; at least one of them has to fail.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import moe
+from tests import test_oracle_pins as pins
+
+
+def _route_major_layout(idx, e, capacity):
+    # slots handed out to every token's first route, then every second route, ...
+    L = moe.dispatch_layout(idx, e, capacity)
+    s, k = idx.shape
+    seen = np.zeros(e, np.int64)
+    dst = -np.ones((s, k), np.int64)
+    src = -np.ones(L.rows, np.int64)
+    for j in range(k):
+        for t in range(s):
+            x = int(idx[t, j])
+            q = seen[x]
+            seen[x] += 1
+            if capacity > 0 and q >= capacity:
+                continue
+            dst[t, j] = L.offsets[x] + q
+            src[dst[t, j]] = t
+    L.dst = dst.astype(np.int32)
+    L.src = src.astype(np.int32)
+    return L
+
+
+def _slot_off_by_one(idx, e, capacity):
+    L = moe.dispatch_layout(idx, e, capacity)
+    dst = L.dst.copy()
+    dst[dst >= 0] += 1
+    dst[dst >= L.rows] = -1
+    L.dst = dst
+    return L
+
+
+def _combine_drops_last_route(layout, E, w, dtype):
+    w = np.array(w, np.float32).copy()
+    w[:, -1] = 0
+    return moe.combine(layout, E, w, dtype)
+
+
+def _combine_ignores_weights(layout, E, w, dtype):
+    return moe.combine(layout, E, np.ones_like(np.asarray(w, np.float32)), dtype)
+
+
+def _gate_bwd_sign(idx, w, gw, e):
+    return -moe.gate_topk_backward(idx, w, gw, e)
+
+
+def _gate_bwd_no_centering(idx, w, gw, e):
+    return moe.gate_topk_backward(idx, w, gw, e) + _selected_scatter(idx, w, gw, e)
+
+
+def _selected_scatter(idx, w, gw, e):
+    # adds back w*dot, i.e. forgets to subtract the weighted mean
+    s, k = idx.shape
+    out = np.zeros((s, e), np.float32)
+    dot = (w.astype(np.float64) * gw).sum(1)
+    for j in range(k):
+        out[np.arange(s), idx[:, j]] += (w[:, j] * dot).astype(np.float32)
+    return out
+
+
+def _gate_ties_high(logits, k):
+    l32 = np.asarray(logits, np.float32)
+    rev = l32[:, ::-1]
+    idx, w = moe.gate_topk(rev, k)
+    return (l32.shape[1] - 1 - idx).astype(np.int32), w
+
+
+def _combine_bwd_wrong_row(layout, gy, E, w, dtype):
+    gE, gw = moe.combine_backward(layout, gy, E, w, dtype)
+    return gE, np.roll(gw, 1, axis=1)
+
+
+def _combine_bwd_unweighted(layout, gy, E, w, dtype):
+    return moe.combine_backward(layout, gy, E, np.ones_like(np.asarray(w, np.float32)), dtype)
+
+
+def _dispatch_bwd_first_route(layout, G, dtype):
+    L2 = moe.Layout(**{**layout.__dict__})
+    L2.dst = layout.dst.copy()
+    L2.dst[:, 1:] = -1
+    return moe.dispatch_backward(L2, G, dtype)
+
+
+def _bf16_truncates(a32, dtype):
+    if dtype != "bf16":
+        return moe.from_f32(a32, dtype)
+    u = np.ascontiguousarray(a32, np.float32).view(np.uint32)
+    return (u >> np.uint32(16)).astype(np.uint16)
+
+
+MUTATIONS = {
+    "route_major_slots": ("dispatch_layout", _route_major_layout),
+    "slot_off_by_one": ("dispatch_layout", _slot_off_by_one),
+    "combine_drops_last_route": ("combine", _combine_drops_last_route),
+    "combine_ignores_weights": ("combine", _combine_ignores_weights),
+    "gate_bwd_sign": ("gate_topk_backward", _gate_bwd_sign),
+    "gate_bwd_no_centering": ("gate_topk_backward", _gate_bwd_no_centering),
+    "gate_ties_high": ("gate_topk", _gate_ties_high),
+    "combine_bwd_wrong_row": ("combine_backward", _combine_bwd_wrong_row),
+    "combine_bwd_unweighted": ("combine_backward", _combine_bwd_unweighted),
+    "dispatch_bwd_first_route": ("dispatch_backward", _dispatch_bwd_first_route),
+    "bf16_truncates": ("from_f32", _bf16_truncates),
+}
+
+PINS = [
+    pins.test_golden_layout,
+    pins.test_golden_combine_and_backward,
+    pins.test_golden_gate,
+    lambda: pins.test_gate_indices_brute_force_with_ties(0),
+    lambda: pins.test_gate_backward_finite_differences(),
+    lambda: pins.test_index_path_matches_dense_einsum(3, 6),
+    lambda: pins.test_unit_weight_round_trip_is_exact("bf16", 3),
+    lambda: pins.test_adjoint_identities(2),
+    pins.test_weight_gradient_matches_finite_difference_of_dense_combine,
+    pins.test_identity_expert_closed_forms,
+    pins.test_bf16_rounding_brute_force,
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(oracle, attr, fn)
+    caught = []
+    for pin in PINS:
+        try:
+            pin()
+        except AssertionError:
+            caught.append(pin)
+        except (IndexError, ValueError):
+            caught.append(pin)
+    assert caught, f"no pin caught the planted mistake {name!r}"
+
+
+def test_unmutated_oracle_passes_every_pin():
+    for pin in PINS:
+        pin()

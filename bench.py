@@ -1,0 +1,243 @@
+"""Benchmark of the MoE gate / dispatch / combine hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is one pass of the whole path over one batch of resident synthetic input:
+gate top-k, dispatch layout, dispatch, weighted combine, dispatch replay from the
+saved layout (activation-checkpoint recompute), combine backward, dispatch backward
+and gate backward. W untimed steps, then K timed steps bracketed by
+torch.cuda.synchronize(). Every launch of a step goes to the current HIP stream;
+HIP events recorded on that stream around each call give per-kernel durations over
+the same timed region.
+
+Prints ONE JSON line. `value` is tokens/s of the whole step. The dispatch+combine
+figures (tokens/s and achieved HBM GB/s of the forward pair, the headline metric)
+are in "dispatch_combine"; "roofline" covers the kernel with the largest share of
+the step; "cpu_baseline" times the CPU oracle on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads as W  # noqa: E402
+
+METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (s=8192,m=4096,e=128,k=8)"
+HBM_PEAK_GBPS = 8000.0
+OPS = ["gate", "layout", "dispatch", "combine", "replay", "combine_bwd", "dispatch_bwd", "gate_bwd"]
+
+
+def algorithmic_bytes(w: W.Workload, kept_routes: int) -> dict:
+    """Bytes each call must move (zero padding counts: it is part of the output).
+
+    b = element size; K = placed routes. Routing metadata is int32/float32.
+    """
+    s, m, e, k, b = w.s, w.m, w.e, w.k, W.ELEM_BYTES[w.dtype]
+    rows = w.rows
+    K = kept_routes
+    row = m * b
+    return {
+        "gate": s * e * 4 + s * k * 8,
+        # count + place read the ids twice; dst, route copy, src written; tile tables
+        "layout": 2 * s * k * 4 + 2 * s * k * 4 + rows * 4,
+        "dispatch": s * row + rows * row + s * k * 4,
+        "combine": K * row + s * k * 8 + s * row,
+        # the replay also compares the routing with the saved copy
+        "replay": s * row + rows * row + s * k * 4 + 2 * s * k * 4,
+        "combine_bwd": s * row + K * row + rows * row + s * k * 12,
+        "dispatch_bwd": K * row + s * k * 4 + s * row,
+        "gate_bwd": s * k * 12 + s * e * 4,
+    }
+
+
+def to_dev(a, dtype, dev):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def run_gpu(w: W.Workload, steps: int, warmup: int):
+    import torch
+
+    import combine_moe_gate_amd as M
+
+    if not os.path.exists(M.LIB_PATH):
+        from combine_moe_gate_amd import _build
+        _build.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = W.make_inputs(w)
+    logits = to_dev(inp.logits, "f32", dev)
+    x = to_dev(inp.x, w.dtype, dev)
+    gy = to_dev(inp.grad_y, w.dtype, dev)
+    tdt = x.dtype
+    s, k, e, m, rows = w.s, w.k, w.e, w.m, w.rows
+    idx = torch.empty((s, k), dtype=torch.int32, device=dev)
+    wt = torch.empty((s, k), dtype=torch.float32, device=dev)
+    ws = torch.empty(M.workspace_bytes(s, e, k, w.capacity), dtype=torch.uint8, device=dev)
+    buf = torch.empty((rows, m), dtype=tdt, device=dev)
+    rep = torch.empty((rows, m), dtype=tdt, device=dev)
+    y = torch.empty((s, m), dtype=tdt, device=dev)
+    gE = torch.empty((rows, m), dtype=tdt, device=dev)
+    gw = torch.empty((s, k), dtype=torch.float32, device=dev)
+    gx = torch.empty((s, m), dtype=tdt, device=dev)
+    gl = torch.empty((s, e), dtype=torch.float32, device=dev)
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        M.moe_gate_topk(logits, k, idx_out=idx, w_out=wt)
+        mark(1)
+        L = M.moe_dispatch_layout(idx, e, w.capacity, workspace=ws)
+        mark(2)
+        M.moe_dispatch(L, x, out=buf)
+        mark(3)
+        M.moe_combine(L, buf, wt, out=y)
+        mark(4)
+        M.moe_dispatch_replay(L, x, idx, out=rep)  # checkpoint recompute from the saved layout
+        mark(5)
+        M.moe_combine_backward(L, gy, rep, wt, grad_expert_out=gE, grad_w=gw)
+        mark(6)
+        M.moe_dispatch_backward(L, gE, out=gx)
+        mark(7)
+        M.moe_gate_topk_backward(idx, wt, gw, e, out=gl)
+        mark(8)
+        return L
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(OPS) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        L = step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    per_op = {op: [] for op in OPS}
+    for ev in events:
+        for j, op in enumerate(OPS):
+            per_op[op].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)  # microseconds
+    kept = int(L.kept.sum().item())
+    flags, _ = M.moe_layout_read(L)
+    if flags != 0:
+        raise RuntimeError(f"layout flags {flags} on a valid workload")
+    return elapsed, per_op, kept
+
+
+def run_cpu_baseline(w: W.Workload, target_s: float = 12.0, sample_tokens: int = 1024):
+    """The oracle, as it stands, over the first `sample_tokens` tokens of the workload."""
+    import oracle
+
+    inp = W.make_inputs(w)
+    n = min(sample_tokens, w.s)
+    logits = inp.logits[:n]
+    x = inp.x[:n]
+    gy = inp.grad_y[:n]
+    cap = w.capacity
+    if cap > 0:  # keep the capacity factor of the workload on the sample
+        cap = max(1, -(-cap * n // w.s))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        idx, wt = oracle.gate_topk(logits, w.k)
+        L = oracle.dispatch_layout(idx, w.e, cap)
+        E = oracle.dispatch(L, x)
+        oracle.combine(L, E, wt, w.dtype)
+        E2, _ = oracle.dispatch_replay(L, x, idx)
+        gE, gw = oracle.combine_backward(L, gy, E2, wt, w.dtype)
+        oracle.dispatch_backward(L, gE, w.dtype)
+        oracle.gate_topk_backward(idx, wt, gw, w.e)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            break
+    return {
+        "value": n * reps / el,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"first {n} of {w.s} tokens of {w.name} (same m, e, k, dtype"
+                   f"{', capacity scaled to ' + str(cap) if w.capacity > 0 else ''}), whole step, "
+                   f"{reps} passes in {el:.1f} s, single-threaded numpy"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=W.HEADLINE, choices=sorted(W.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(this path has no multi-GPU exchange)", file=sys.stderr)
+        sys.exit(2)
+
+    w = W.WORKLOADS[args.workload]
+    elapsed, per_op, kept = run_gpu(w, args.steps, args.warmup)
+    ms_per_step = elapsed / args.steps * 1e3
+    abytes = algorithmic_bytes(w, kept)
+    kernels = {}
+    for op in OPS:
+        us = float(np.mean(per_op[op]))
+        kernels[op] = {"us": round(us, 2), "us_median": round(float(np.median(per_op[op])), 2),
+                       "bytes": abytes[op], "GBps": round(abytes[op] / us / 1e3, 1)}
+    dc_us = kernels["dispatch"]["us"] + kernels["combine"]["us"]
+    dc_bytes = abytes["dispatch"] + abytes["combine"]
+    dc_gbps = dc_bytes / dc_us / 1e3
+    dominant = max(OPS, key=lambda op: kernels[op]["us"])
+    dom_gbps = abytes[dominant] / kernels[dominant]["us"] / 1e3
+
+    line = {
+        "metric": METRIC,
+        "value": round(w.s / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "s": w.s, "m": w.m, "e": w.e, "k": w.k,
+                   "capacity": w.capacity if w.capacity > 0 else "dropless",
+                   "routing": {"uniform": "N(0,1) logits", "zipf": "N(0,1) + 2 ln Zipf(1.2) bias",
+                               "hotspot": "N(0,1), +3 on expert 0 for 10% of tokens"}[w.routing],
+                   "step": "gate+layout+dispatch+combine+replay+combine_bwd+dispatch_bwd+gate_bwd",
+                   "parallelism": "single GPU"},
+        "dispatch_combine": {"tokens_per_s": round(w.s / (dc_us / 1e6), 1), "GBps": round(dc_gbps, 1),
+                             "frac_of_hbm_peak": round(dc_gbps / HBM_PEAK_GBPS, 4), "us": round(dc_us, 2),
+                             "bytes": dc_bytes},
+        "roofline": {"kernel": dominant, "bound": "hbm", "achieved": round(dom_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None},
+        "kernels": kernels,
+        "kept_routes": kept,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = run_cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,280 @@
+"""MI355X-native MoE gate / dispatch / combine: thin Python binding over libmoe_gate.so.
+
+Every step of the path runs in the library's HIP kernels; this module only
+marshals arguments. PyTorch provides device memory and the current stream. The
+function names are those of the C ABI in include/moe_gate.h:
+
+    idx, w  = moe_gate_topk(logits, k)
+    layout  = moe_dispatch_layout(idx, e, capacity)        # capacity <= 0: dropless
+    buf     = moe_dispatch(layout, x)                      # [layout.rows, m]
+    buf     = moe_dispatch_replay(layout, x, idx=None)     # recompute from a saved layout
+    y       = moe_combine(layout, buf_or_expert_out, w)    # [s, m]
+    gE, gw  = moe_combine_backward(layout, grad_y, expert_out, w)
+    gx      = moe_dispatch_backward(layout, grad_out)
+    gl      = moe_gate_topk_backward(idx, w, gw, e)
+    flags, checksum = moe_layout_read(layout)              # synchronises; tests/debug
+
+There is no CPU fallback: without the built library, or without a GPU, every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_gate.so")
+
+MOE_OK = 0
+STATUS_NAMES = {
+    0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE",
+    4: "MOE_ERR_HANDLE_MISMATCH", 5: "MOE_ERR_MISALIGNED", 6: "MOE_ERR_HIP",
+}
+MOE_F32, MOE_BF16, MOE_F16 = 0, 1, 2
+FLAG_EXPERT_OUT_OF_RANGE = 1
+FLAG_DUPLICATE_EXPERT = 2
+FLAG_REPLAY_MISMATCH = 4
+MAX_EXPERTS = 1024
+MAX_TOPK = 16
+
+_DTYPE_CODE = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.float16: MOE_F16}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class LayoutStruct(ctypes.Structure):
+    """Mirror of moe_layout_t."""
+    _fields_ = [
+        ("magic", ctypes.c_uint64),
+        ("s", ctypes.c_int32), ("e", ctypes.c_int32), ("k", ctypes.c_int32),
+        ("capacity", ctypes.c_int32),
+        ("rows", ctypes.c_int64),
+        ("counts", ctypes.c_void_p), ("kept", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
+        ("dst", ctypes.c_void_p), ("src", ctypes.c_void_p), ("route_idx", ctypes.c_void_p),
+        ("checksum", ctypes.c_void_p), ("flags", ctypes.c_void_p), ("scratch", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SIGNATURES = {
+    "moe_abi_version": (ctypes.c_int, []),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_layout_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "moe_gate_topk": (ctypes.c_int, [_P, _I, _I, _I, _P, _P, _P]),
+    "moe_gate_topk_backward": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _P, _P]),
+    "moe_dispatch_layout": (ctypes.c_int, [_P, _I, _I, _I, _I, _P, ctypes.c_size_t,
+                                           ctypes.POINTER(LayoutStruct), _P]),
+    "moe_dispatch": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _I, ctypes.c_int, _P, _P]),
+    "moe_dispatch_replay": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _P, _I, ctypes.c_int,
+                                           _P, _P]),
+    "moe_combine": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _P, _I, ctypes.c_int, _P, _P]),
+    "moe_combine_backward": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _P, _P, _I,
+                                            ctypes.c_int, _P, _P, _P]),
+    "moe_dispatch_backward": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _I, ctypes.c_int,
+                                             _P, _P]),
+    "moe_layout_read": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _P, _P]),
+}
+EXPORTS = tuple(_SIGNATURES)
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe_gate.so (built in-tree); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it first (python -m combine_moe_gate_amd._build)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, lib().moe_last_error().decode())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _require_gpu(*tensors):
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU (no CPU fallback exists)")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def workspace_bytes(s: int, e: int, k: int, capacity: int) -> int:
+    return int(lib().moe_layout_workspace_bytes(s, e, k, capacity))
+
+
+class Layout:
+    """A dispatch layout: the C handle plus the device workspace backing it.
+
+    `rows` is a host int. The array properties are device tensors viewing the
+    workspace (read-only by convention).
+    """
+
+    def __init__(self, struct: LayoutStruct, workspace: torch.Tensor):
+        self.struct = struct
+        self.workspace = workspace
+
+    @property
+    def s(self): return self.struct.s
+    @property
+    def e(self): return self.struct.e
+    @property
+    def k(self): return self.struct.k
+    @property
+    def capacity(self): return self.struct.capacity
+    @property
+    def rows(self): return int(self.struct.rows)
+
+    def _view(self, ptr, n, dtype=torch.int32):
+        off = ptr - self.workspace.data_ptr()
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        return self.workspace[off:off + nbytes].view(dtype)
+
+    @property
+    def counts(self): return self._view(self.struct.counts, self.e)
+    @property
+    def kept(self): return self._view(self.struct.kept, self.e)
+    @property
+    def offsets(self): return self._view(self.struct.offsets, self.e + 1)
+    @property
+    def dst(self): return self._view(self.struct.dst, self.s * self.k).view(self.s, self.k)
+    @property
+    def src(self): return self._view(self.struct.src, self.rows)
+    @property
+    def route_idx(self): return self._view(self.struct.route_idx, self.s * self.k).view(self.s, self.k)
+
+    def byref(self):
+        return ctypes.byref(self.struct)
+
+
+def moe_gate_topk(logits: torch.Tensor, k: int, idx_out=None, w_out=None):
+    _require_gpu(logits)
+    s, e = logits.shape
+    if logits.dtype != torch.float32:
+        raise ValueError("logits must be float32")
+    idx = idx_out if idx_out is not None else torch.empty((s, k), dtype=torch.int32, device=logits.device)
+    w = w_out if w_out is not None else torch.empty((s, k), dtype=torch.float32, device=logits.device)
+    _check(lib().moe_gate_topk(_ptr(logits), s, e, k, _ptr(idx), _ptr(w), _stream(logits)))
+    return idx, w
+
+
+def moe_gate_topk_backward(idx: torch.Tensor, w: torch.Tensor, grad_w: torch.Tensor, e: int, out=None):
+    _require_gpu(idx, w, grad_w)
+    s, k = idx.shape
+    gl = out if out is not None else torch.empty((s, e), dtype=torch.float32, device=idx.device)
+    _check(lib().moe_gate_topk_backward(_ptr(idx), _ptr(w), _ptr(grad_w), s, e, k, _ptr(gl), _stream(idx)))
+    return gl
+
+
+def moe_dispatch_layout(idx: torch.Tensor, e: int, capacity: int = 0, workspace=None) -> Layout:
+    _require_gpu(idx)
+    if idx.dtype != torch.int32:
+        raise ValueError("expert ids must be int32")
+    s, k = idx.shape
+    nbytes = workspace_bytes(s, e, k, capacity)
+    if nbytes == 0:
+        # let the library name the problem
+        _check(lib().moe_dispatch_layout(_ptr(idx), s, e, k, capacity, ctypes.c_void_p(0), 0,
+                                         ctypes.byref(LayoutStruct()), _stream(idx)))
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=idx.device)
+    st = LayoutStruct()
+    _check(lib().moe_dispatch_layout(_ptr(idx), s, e, k, capacity, _ptr(workspace),
+                                     workspace.numel(), ctypes.byref(st), _stream(idx)))
+    return Layout(st, workspace)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPE_CODE[t.dtype]
+    except KeyError:
+        raise ValueError(f"unsupported element type {t.dtype}") from None
+
+
+def moe_dispatch(layout: Layout, x: torch.Tensor, out=None):
+    _require_gpu(x)
+    m = x.shape[1]
+    out = out if out is not None else torch.empty((layout.rows, m), dtype=x.dtype, device=x.device)
+    _check(lib().moe_dispatch(layout.byref(), _ptr(x), m, _dtype_code(x), _ptr(out), _stream(x)))
+    return out
+
+
+def moe_dispatch_replay(layout: Layout, x: torch.Tensor, idx=None, out=None):
+    _require_gpu(x, idx)
+    m = x.shape[1]
+    out = out if out is not None else torch.empty((layout.rows, m), dtype=x.dtype, device=x.device)
+    _check(lib().moe_dispatch_replay(layout.byref(), _ptr(idx), _ptr(x), m, _dtype_code(x),
+                                     _ptr(out), _stream(x)))
+    return out
+
+
+def moe_combine(layout: Layout, expert_out: torch.Tensor, w: torch.Tensor, out=None):
+    _require_gpu(expert_out, w)
+    m = expert_out.shape[1]
+    y = out if out is not None else torch.empty((layout.s, m), dtype=expert_out.dtype, device=expert_out.device)
+    _check(lib().moe_combine(layout.byref(), _ptr(expert_out), _ptr(w), m, _dtype_code(expert_out),
+                             _ptr(y), _stream(expert_out)))
+    return y
+
+
+def moe_combine_backward(layout: Layout, grad_y: torch.Tensor, expert_out: torch.Tensor,
+                         w: torch.Tensor, grad_expert_out=None, grad_w=None):
+    _require_gpu(grad_y, expert_out, w)
+    m = grad_y.shape[1]
+    gE = grad_expert_out if grad_expert_out is not None else torch.empty(
+        (layout.rows, m), dtype=grad_y.dtype, device=grad_y.device)
+    gw = grad_w if grad_w is not None else torch.empty((layout.s, layout.k), dtype=torch.float32,
+                                                      device=grad_y.device)
+    _check(lib().moe_combine_backward(layout.byref(), _ptr(grad_y), _ptr(expert_out), _ptr(w), m,
+                                      _dtype_code(grad_y), _ptr(gE), _ptr(gw), _stream(grad_y)))
+    return gE, gw
+
+
+def moe_dispatch_backward(layout: Layout, grad_out: torch.Tensor, out=None):
+    _require_gpu(grad_out)
+    m = grad_out.shape[1]
+    gx = out if out is not None else torch.empty((layout.s, m), dtype=grad_out.dtype, device=grad_out.device)
+    _check(lib().moe_dispatch_backward(layout.byref(), _ptr(grad_out), m, _dtype_code(grad_out),
+                                       _ptr(gx), _stream(grad_out)))
+    return gx
+
+
+def moe_layout_read(layout: Layout):
+    flags = ctypes.c_int32(0)
+    checksum = ctypes.c_uint64(0)
+    _check(lib().moe_layout_read(layout.byref(), ctypes.byref(flags), ctypes.byref(checksum),
+                                 _stream(layout.workspace)))
+    return int(flags.value), int(checksum.value)
+
+
+__all__ = [
+    "moe_gate_topk", "moe_gate_topk_backward", "moe_dispatch_layout", "moe_dispatch",
+    "moe_dispatch_replay", "moe_combine", "moe_combine_backward", "moe_dispatch_backward",
+    "moe_layout_read", "workspace_bytes", "Layout", "MoeError", "lib", "EXPORTS",
+]

@@ -1,0 +1,146 @@
+// Top-k gate and its backward on gfx950.
+//
+// One wave64 per token. The e logits of a row sit in registers, ceil(e/64) per lane,
+// each as a 64-bit key (order-preserving image of the float32 logit, then 0xffff minus
+// the expert id, so the largest key is the largest logit with ties to the lower id).
+// k rounds of a wave-wide maximum pick the experts in descending order; the owner lane
+// clears the winner. The weights are a softmax over the k selected logits, formed in
+// float64 (equal to the full softmax renormalised over the selection: the full
+// denominator cancels) -- DeepSpeed PR "MoE dispatch: fix silent Tutel + TP corruption,
+// speed up native and Tutel paths", part 1: the gate hands on per-route expert ids and
+// gate values, not a dense mask.
+#include "internal.h"
+#include "moe_device.h"
+
+namespace moe {
+
+// Order-preserving map of a float32 to uint32 (-0.0 folded onto +0.0 first).
+__device__ __forceinline__ uint32_t ordered_key(float v) {
+  uint32_t u = __float_as_uint(v + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_to_float(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+template <int VPL>
+__global__ __launch_bounds__(kBlock) void gate_topk_kernel(const float* __restrict__ logits,
+                                                           int s, int e, int k,
+                                                           int32_t* __restrict__ idx_out,
+                                                           float* __restrict__ w_out) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * kWavesPerBlock + wave_in_block();
+  if (t >= s) return;
+  const float* row = logits + static_cast<size_t>(t) * e;
+
+  uint64_t key[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int i = lane + v * kWave;
+    key[v] = (i < e) ? ((static_cast<uint64_t>(ordered_key(row[i])) << 16) |
+                        static_cast<uint64_t>(0xffff - i))
+                     : 0ull;
+  }
+
+  uint64_t mine = 0;  // lane r keeps the r-th selection
+  for (int r = 0; r < k; ++r) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int v = 1; v < VPL; ++v) best = key[v] > best ? key[v] : best;
+    best = wave_max(best);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+      if (key[v] == best) key[v] = 0ull;
+    if (lane == r) mine = best;
+  }
+
+  const bool active = lane < k;
+  const int expert = 0xffff - static_cast<int>(mine & 0xffffu);
+  const float l = key_to_float(static_cast<uint32_t>(mine >> 16));
+  const float l0 = __shfl(l, 0, kWave);  // the largest selected logit
+  const double ex = active ? exp(static_cast<double>(l) - static_cast<double>(l0)) : 0.0;
+  const double denom = wave_sum(ex);
+  if (active) {
+    const size_t o = static_cast<size_t>(t) * k + lane;
+    idx_out[o] = expert;
+    w_out[o] = static_cast<float>(ex / denom);
+  }
+}
+
+// Gate backward: grad_logits[idx_j] = w_j (grad_w_j - sum_q w_q grad_w_q), float64,
+// zero elsewhere. One wave per token; lanes j < k hold route j.
+template <int VPL>
+__global__ __launch_bounds__(kBlock) void gate_topk_backward_kernel(
+    const int32_t* __restrict__ idx, const float* __restrict__ w, const float* __restrict__ gw,
+    int s, int e, int k, float* __restrict__ gl) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * kWavesPerBlock + wave_in_block();
+  if (t >= s) return;
+  const bool active = lane < k;
+  const size_t o = static_cast<size_t>(t) * k + lane;
+  const int my_idx = active ? idx[o] : -1;
+  const double wj = active ? static_cast<double>(w[o]) : 0.0;
+  const double gj = active ? static_cast<double>(gw[o]) : 0.0;
+  const double dot = wave_sum(wj * gj);
+  const double contrib = active ? wj * (gj - dot) : 0.0;
+
+  int sel[16];
+  double val[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    sel[j] = -1;
+    val[j] = 0.0;
+    if (j < k) {
+      sel[j] = __shfl(my_idx, j, kWave);
+      val[j] = __shfl(contrib, j, kWave);
+    }
+  }
+  float* out = gl + static_cast<size_t>(t) * e;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int i = lane + v * kWave;
+    if (i < e) {
+      double acc = 0.0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j < k && sel[j] == i) acc += val[j];
+      out[i] = static_cast<float>(acc);
+    }
+  }
+}
+
+static int values_per_lane(int e) {
+  const int v = (e + kWave - 1) / kWave;
+  return v <= 1 ? 1 : v <= 2 ? 2 : v <= 4 ? 4 : v <= 8 ? 8 : 16;
+}
+
+hipError_t launch_gate_topk(const float* logits, int s, int e, int k, int32_t* idx, float* w,
+                            hipStream_t stream) {
+  if (s == 0) return hipSuccess;
+  const dim3 grid((s + kWavesPerBlock - 1) / kWavesPerBlock), block(kBlock);
+  switch (values_per_lane(e)) {
+    case 1: gate_topk_kernel<1><<<grid, block, 0, stream>>>(logits, s, e, k, idx, w); break;
+    case 2: gate_topk_kernel<2><<<grid, block, 0, stream>>>(logits, s, e, k, idx, w); break;
+    case 4: gate_topk_kernel<4><<<grid, block, 0, stream>>>(logits, s, e, k, idx, w); break;
+    case 8: gate_topk_kernel<8><<<grid, block, 0, stream>>>(logits, s, e, k, idx, w); break;
+    default: gate_topk_kernel<16><<<grid, block, 0, stream>>>(logits, s, e, k, idx, w); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_topk_backward(const int32_t* idx, const float* w, const float* gw, int s,
+                                     int e, int k, float* gl, hipStream_t stream) {
+  if (s == 0) return hipSuccess;
+  const dim3 grid((s + kWavesPerBlock - 1) / kWavesPerBlock), block(kBlock);
+  switch (values_per_lane(e)) {
+    case 1: gate_topk_backward_kernel<1><<<grid, block, 0, stream>>>(idx, w, gw, s, e, k, gl); break;
+    case 2: gate_topk_backward_kernel<2><<<grid, block, 0, stream>>>(idx, w, gw, s, e, k, gl); break;
+    case 4: gate_topk_backward_kernel<4><<<grid, block, 0, stream>>>(idx, w, gw, s, e, k, gl); break;
+    case 8: gate_topk_backward_kernel<8><<<grid, block, 0, stream>>>(idx, w, gw, s, e, k, gl); break;
+    default: gate_topk_backward_kernel<16><<<grid, block, 0, stream>>>(idx, w, gw, s, e, k, gl); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,124 @@
+// Device helpers shared by the gfx950 kernels of the MoE gate / dispatch / combine path:
+// 16-byte row chunks, element conversions, wave64 reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;           // CDNA wavefront width
+constexpr int kBlock = 256;         // threads per workgroup in the row kernels
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kTileTokens = 256;    // tokens per layout tile (one workgroup)
+
+enum Dtype : int { kF32 = 0, kBF16 = 1, kF16 = 2 };
+
+// One 16-byte row chunk (a native vector, so loads/stores are single dwordx4 ops).
+typedef uint32_t chunk_t __attribute__((ext_vector_type(4)));
+
+// Elements of each type in one 16-byte chunk.
+template <int DT> struct ChunkElems { static constexpr int value = 8; };
+template <> struct ChunkElems<kF32> { static constexpr int value = 4; };
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Wave index inside the workgroup, made provably uniform so that per-wave metadata
+// goes through scalar registers.
+__device__ __forceinline__ int wave_in_block() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
+// ---------------------------------------------------------------------------------
+// element conversions (widening is exact; narrowing rounds to nearest even)
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float a) {
+  uint32_t u = __float_as_uint(a);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;  // NaN
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+
+// The empty asm pins `a` as a materialised float32 register value. Without it the
+// backend folds "float32 product, then narrow to f16" into one mixed-precision
+// multiply that rounds only once, which is not the two-step rounding defined here.
+__device__ __forceinline__ uint32_t f32_to_f16_rne(float a) {
+  asm volatile("" : "+v"(a));
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(a));
+}
+
+// Unpack one 16-byte chunk into float32 values.
+template <int DT>
+__device__ __forceinline__ void unpack(const chunk_t& v, float (&f)[ChunkElems<DT>::value]) {
+  if constexpr (DT == kF32) {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  } else if constexpr (DT == kBF16) {
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+  } else {
+    f[0] = f16_bits_to_f32(v.x & 0xffffu); f[1] = f16_bits_to_f32(v.x >> 16);
+    f[2] = f16_bits_to_f32(v.y & 0xffffu); f[3] = f16_bits_to_f32(v.y >> 16);
+    f[4] = f16_bits_to_f32(v.z & 0xffffu); f[5] = f16_bits_to_f32(v.z >> 16);
+    f[6] = f16_bits_to_f32(v.w & 0xffffu); f[7] = f16_bits_to_f32(v.w >> 16);
+  }
+}
+
+// Pack float32 values into one 16-byte chunk of the element type.
+template <int DT>
+__device__ __forceinline__ chunk_t pack(const float (&f)[ChunkElems<DT>::value]) {
+  chunk_t v;
+  if constexpr (DT == kF32) {
+    v.x = __float_as_uint(f[0]); v.y = __float_as_uint(f[1]);
+    v.z = __float_as_uint(f[2]); v.w = __float_as_uint(f[3]);
+  } else if constexpr (DT == kBF16) {
+    v.x = f32_to_bf16_rne(f[0]) | (f32_to_bf16_rne(f[1]) << 16);
+    v.y = f32_to_bf16_rne(f[2]) | (f32_to_bf16_rne(f[3]) << 16);
+    v.z = f32_to_bf16_rne(f[4]) | (f32_to_bf16_rne(f[5]) << 16);
+    v.w = f32_to_bf16_rne(f[6]) | (f32_to_bf16_rne(f[7]) << 16);
+  } else {
+    v.x = f32_to_f16_rne(f[0]) | (f32_to_f16_rne(f[1]) << 16);
+    v.y = f32_to_f16_rne(f[2]) | (f32_to_f16_rne(f[3]) << 16);
+    v.z = f32_to_f16_rne(f[4]) | (f32_to_f16_rne(f[5]) << 16);
+    v.w = f32_to_f16_rne(f[6]) | (f32_to_f16_rne(f[7]) << 16);
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------------------------
+// wave64 reductions (butterfly over lane xor masks; every lane gets the result)
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_sum(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int wave_or(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint64_t w = __shfl_xor(v, o, kWave);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+}  // namespace moe

@@ -1,0 +1,243 @@
+/*
+ * moe_gate.h -- C ABI of the MI355X (gfx950) MoE gate / dispatch / combine library.
+ *
+ * One data-parallel hot path of a mixture-of-experts layer on one GPU:
+ *   (1) top-k gating over router logits,
+ *   (2) the dispatch layout: per-expert counts, token-order slots, capacity drop,
+ *   (3) the permute of activation rows into an expert-grouped buffer,
+ *   (4) the weighted combine of each token's expert outputs,
+ *   (5) the backward passes, and a replay of (3) from a saved layout.
+ *
+ * Sources, cited by page title and section:
+ *   [DS-8195] DeepSpeed PR "MoE dispatch: fix silent Tutel + TP corruption, speed up
+ *             native and Tutel paths": part 1 (per-route index/location/gate metadata
+ *             as contiguous int32; capacity resolved once on the host), part 2 (the
+ *             [e, c, m] buffer), part 3 (index dispatch/combine, fp32 accumulation in
+ *             combine), the review comment on fast_cumsum_sub_one (slot = cumsum - 1).
+ *   [DS-8213] DeepSpeed PR "Add an opt-in DeepEP transport for the AutoEP expert
+ *             all-to-all": first commit (replicate tokens before top-k expansion, group
+ *             arrivals by expert, reduce the weighted sum in combine, backward = the
+ *             dual operation replayed on the forward handle), review-fix commits
+ *             (weights keep their gradient; rows and weights counted from one source;
+ *             the row count comes from the handle without a device-to-host read), the
+ *             review threads on combine weights, on live handles after a later forward
+ *             and on combine reading only the rows the handle describes.
+ *   [AM-3684] NeMo Automodel PR "perf(moe): reuse the DeepEP dispatch layout on
+ *             activation-checkpoint recompute": section 1 and "How" (a saved handle
+ *             skips the layout on recompute; the replay must reproduce row counts;
+ *             mis-routing must fail loudly, not silently).
+ *
+ * Conventions for every call:
+ *   - All array arguments are DEVICE pointers unless stated otherwise. The caller owns
+ *     every buffer, including the layout workspace; the library allocates nothing and
+ *     keeps no device state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Every call
+ *     that takes a stream only enqueues work on it and returns without waiting, except
+ *     moe_layout_read, which synchronises the stream.
+ *   - Host-side argument checks run before anything is enqueued. On failure nothing is
+ *     enqueued, a status other than MOE_OK is returned and moe_last_error() gives a
+ *     message (thread-local).
+ *   - Routing problems found on the device never fault and never write out of bounds:
+ *     the offending route is treated as dropped and a bit is set in the layout's flags
+ *     word (MOE_FLAG_*), readable with moe_layout_read.
+ *   - Activation rows of m elements must start on 16-byte boundaries and be a multiple
+ *     of 16 bytes long (m * element size % 16 == 0); otherwise MOE_ERR_MISALIGNED.
+ *   - Element types: MOE_F32, MOE_BF16 (bfloat16), MOE_F16 (IEEE half). Narrowing to
+ *     bf16/f16 rounds to nearest even. Weights, weight gradients and logits are float32.
+ *   - Results are deterministic: no floating-point atomics; integer atomics only where
+ *     the result does not depend on their order.
+ */
+#ifndef MOE_GATE_H
+#define MOE_GATE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,     /* null pointer, negative size, k outside [1, e], ... */
+  MOE_ERR_UNSUPPORTED = 2,     /* beyond MOE_MAX_EXPERTS / MOE_MAX_TOPK / 32-bit row ids */
+  MOE_ERR_WORKSPACE = 3,       /* layout workspace smaller than moe_layout_workspace_bytes */
+  MOE_ERR_HANDLE_MISMATCH = 4, /* layout not built by moe_dispatch_layout, or sizes differ */
+  MOE_ERR_MISALIGNED = 5,      /* row pointer or row length not 16-byte aligned */
+  MOE_ERR_HIP = 6              /* the HIP runtime reported an error on enqueue */
+} moe_status_t;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_F16 = 2 } moe_dtype_t;
+
+/* Bits of the layout's device flags word. */
+#define MOE_FLAG_EXPERT_OUT_OF_RANGE 1 /* a route named an expert outside [0, e) */
+#define MOE_FLAG_DUPLICATE_EXPERT 2    /* a route repeated an earlier expert of its token */
+#define MOE_FLAG_REPLAY_MISMATCH 4     /* a replay was handed routing that differs */
+
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 16
+
+/*
+ * Layout handle: a plain host struct whose array members point into the caller's
+ * workspace. It holds routing metadata only (never weights or activations). It is a
+ * value: copy it freely; it stays valid while its workspace lives, and any number of
+ * layouts may be live at once ([DS-8213] review thread on a backward that runs after
+ * a later forward). Fields are filled by moe_dispatch_layout; treat them as read-only.
+ *
+ * Buffer layout ([DS-8195] parts 2-3, [DS-8213] first commit):
+ *   capacity > 0: rows = e * capacity, the [e, capacity, m] buffer; expert x owns rows
+ *                 [x*capacity, (x+1)*capacity); its first kept[x] rows hold its tokens in
+ *                 token order, the rest are zero padding.
+ *   capacity <= 0 (dropless): rows = s * k; expert x owns rows [offsets[x], offsets[x+1])
+ *                 holding its tokens in token order; offsets[e] = number of valid routes
+ *                 (= s*k unless routes were flagged invalid); rows from offsets[e] on are
+ *                 zero padding. For a grouped GEMM, counts[x] = offsets[x+1]-offsets[x].
+ * `rows` is known on the host, so sizing the next buffer needs no device read
+ * ([DS-8213] review-fix commit on the row count taken from the handle).
+ */
+typedef struct moe_layout {
+  uint64_t magic;     /* set by moe_dispatch_layout */
+  int32_t s, e, k;    /* tokens, experts, routes per token */
+  int32_t capacity;   /* > 0: capacity per expert; 0: dropless */
+  int64_t rows;       /* buffer rows (host-known) */
+  int32_t* counts;    /* [e]   valid routes per expert, before the capacity drop */
+  int32_t* kept;      /* [e]   routes placed per expert: min(counts, capacity) */
+  int32_t* offsets;   /* [e+1] first buffer row of each expert's segment */
+  int32_t* dst;       /* [s*k] buffer row of route (t, j) at t*k+j, or -1 if not placed */
+  int32_t* src;       /* [rows] token of each buffer row, or -1 for padding */
+  int32_t* route_idx; /* [s*k] copy of the routing the layout was built from */
+  uint64_t* checksum; /* [1]   sum over routes of (idx+1)*(t*k+j+1), modulo 2^64 */
+  int32_t* flags;     /* [1]   MOE_FLAG_* bits */
+  void* scratch;      /* internal */
+  void* workspace;
+  size_t workspace_bytes;
+} moe_layout_t;
+
+/* ABI version of the loaded library (MOE_ABI_VERSION it was built with). */
+int moe_abi_version(void);
+
+/* Message of the last failed call on this thread ("" if none). Never NULL. */
+const char* moe_last_error(void);
+
+/* Name of a status code. Never NULL. */
+const char* moe_status_string(moe_status_t status);
+
+/*
+ * Bytes of device workspace a layout needs for (s, e, k, capacity); 0 if the sizes are
+ * invalid or unsupported. The workspace must be 256-byte aligned. Host only.
+ */
+size_t moe_layout_workspace_bytes(int32_t s, int32_t e, int32_t k, int32_t capacity);
+
+/*
+ * (1) Top-k gate ([DS-8195] part 1; softmax then top-k renormalised over the k).
+ *   logits     [s, e] float32, row-major.
+ *   topk_idx   [s, k] int32 out: the k experts with the largest logits, largest first,
+ *              ties to the lower expert id (+0.0 and -0.0 are equal).
+ *   topk_w     [s, k] float32 out: softmax over the k selected logits (equal to the full
+ *              softmax renormalised over the selection), formed in float64 and rounded
+ *              once to float32.
+ *   Requires 1 <= k <= e, e <= MOE_MAX_EXPERTS, k <= MOE_MAX_TOPK, s >= 0.
+ *   NaN logits give unspecified (but in-range, distinct) expert ids.
+ */
+moe_status_t moe_gate_topk(const float* logits, int32_t s, int32_t e, int32_t k,
+                           int32_t* topk_idx, float* topk_w, void* stream);
+
+/*
+ * (5) Gate backward ([DS-8213] review-fix commit: the weights' gradient must reach the
+ * router). grad_logits [s, e] float32 out:
+ *   for selected expert idx[t,j]: w[t,j] * (grad_w[t,j] - sum_q w[t,q] * grad_w[t,q]),
+ *   formed in float64 and rounded once; every other entry is 0. Entries of topk_idx
+ *   outside [0, e) are skipped.
+ */
+moe_status_t moe_gate_topk_backward(const int32_t* topk_idx, const float* topk_w,
+                                    const float* grad_w, int32_t s, int32_t e, int32_t k,
+                                    float* grad_logits, void* stream);
+
+/*
+ * (2) Dispatch layout ([DS-8195] review comment on fast_cumsum_sub_one, parts 2-3;
+ * [DS-8213] review thread on the per-expert prefix sum).
+ *   topk_idx   [s, k] int32: expert of route (t, j).
+ *   capacity   > 0: routes whose token-order slot in their expert is >= capacity are
+ *              dropped; <= 0: dropless.
+ *   workspace  device buffer of at least moe_layout_workspace_bytes(s, e, k, capacity)
+ *              bytes, 256-byte aligned; it backs every array of *layout.
+ *   layout     host out: filled on success (also before the device work completes).
+ * The slot of route (t, j) is the number of tokens t' < t whose routes name the same
+ * expert (column cumsum of the token x expert mask, minus one). Routes naming an expert
+ * outside [0, e), or an expert an earlier route of the same token named, are invalid:
+ * not counted, not placed, and flagged. Three kernels, no host synchronisation.
+ */
+moe_status_t moe_dispatch_layout(const int32_t* topk_idx, int32_t s, int32_t e, int32_t k,
+                                 int32_t capacity, void* workspace, size_t workspace_bytes,
+                                 moe_layout_t* layout, void* stream);
+
+/*
+ * (3) Dispatch ([DS-8195] part 3; [DS-8213] first commit): out[dst[t,j]] = x[t] for every
+ * placed route, a bit copy; padding rows are written as zero. Each token row is read
+ * once and written to its k destinations.
+ *   x    [s, m] of dtype;  out  [layout->rows, m] of dtype.
+ */
+moe_status_t moe_dispatch(const moe_layout_t* layout, const void* x, int32_t m,
+                          moe_dtype_t dtype, void* out, void* stream);
+
+/*
+ * (5) Dispatch replayed from a saved layout ([AM-3684] section 1, "How"): the same
+ * buffer as moe_dispatch, without rebuilding the layout. If topk_idx is not NULL it is
+ * compared route by route with the routing the layout was built from, and any
+ * difference sets MOE_FLAG_REPLAY_MISMATCH in the layout's flags (the copy is still
+ * made from the saved layout).
+ */
+moe_status_t moe_dispatch_replay(const moe_layout_t* layout, const int32_t* topk_idx,
+                                 const void* x, int32_t m, moe_dtype_t dtype, void* out,
+                                 void* stream);
+
+/*
+ * (4) Weighted combine ([DS-8195] part 3: fp32 accumulation; [DS-8213] first commit and
+ * the review thread on combine weights: the weights are applied here):
+ *   y[t] = sum over placed routes j = 0..k-1, in that order, of topk_w[t,j] * E[dst[t,j]],
+ *   each product and each sum rounded to float32 (no fused multiply-add), rounded once
+ *   to dtype. Dropped routes add nothing; a token with no placed route gets a zero row.
+ *   Only rows the layout points at are read ([DS-8213] review on combine and rows).
+ *   expert_out [layout->rows, m];  topk_w [s, k] float32;  y [s, m].
+ */
+moe_status_t moe_combine(const moe_layout_t* layout, const void* expert_out,
+                         const float* topk_w, int32_t m, moe_dtype_t dtype, void* y,
+                         void* stream);
+
+/*
+ * (5) Combine backward ([DS-8213] first commit: the gradient of a combine is a dispatch;
+ * review-fix commit: the weights' gradient is returned):
+ *   grad_expert_out[dst[t,j]] = topk_w[t,j] * grad_y[t] (float32 product, rounded to
+ *   dtype); rows no route points at are zero.
+ *   grad_w[t,j] = sum_m grad_y[t,m] * E[dst[t,j],m], accumulated in float64 and rounded
+ *   once to float32; 0 for a dropped route.
+ *   grad_y [s, m];  expert_out [rows, m];  grad_expert_out [rows, m];  grad_w [s, k] f32.
+ */
+moe_status_t moe_combine_backward(const moe_layout_t* layout, const void* grad_y,
+                                  const void* expert_out, const float* topk_w, int32_t m,
+                                  moe_dtype_t dtype, void* grad_expert_out, float* grad_w,
+                                  void* stream);
+
+/*
+ * (5) Dispatch backward ([DS-8213] first commit: the gradient of a dispatch is a combine):
+ *   grad_x[t] = sum over placed routes j, in order, of grad_out[dst[t,j]], float32
+ *   accumulation, rounded once to dtype.
+ *   grad_out [rows, m];  grad_x [s, m].
+ */
+moe_status_t moe_dispatch_backward(const moe_layout_t* layout, const void* grad_out,
+                                   int32_t m, moe_dtype_t dtype, void* grad_x, void* stream);
+
+/*
+ * Read the layout's flags word and routing checksum into HOST memory. Synchronises
+ * `stream` (debugging and tests; not for the hot path). Either output may be NULL.
+ */
+moe_status_t moe_layout_read(const moe_layout_t* layout, int32_t* flags_host,
+                             uint64_t* checksum_host, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_GATE_H */

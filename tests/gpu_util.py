@@ -1,0 +1,69 @@
+"""Helpers for the GPU parity tests: host <-> device conversion and tolerances."""
+import numpy as np
+import torch
+
+import oracle
+
+DEV = "cuda"
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def to_dev(a: np.ndarray, dtype: str | None = None) -> torch.Tensor:
+    """Upload a host array; bf16 arrays are uint16 bit patterns."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    """Download a device tensor; bf16 comes back as uint16 bit patterns."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def bits(a: np.ndarray) -> np.ndarray:
+    """Raw bit patterns, so +0/-0 and NaN payloads compare exactly."""
+    a = np.ascontiguousarray(a)
+    return a.view({1: np.uint8, 2: np.uint16, 4: np.uint32, 8: np.uint64}[a.dtype.itemsize])
+
+
+def assert_bits_equal(got: np.ndarray, want: np.ndarray, what: str):
+    assert got.shape == want.shape, f"{what}: shape {got.shape} != {want.shape}"
+    gb, wb = bits(got), bits(want)
+    if not np.array_equal(gb, wb):
+        bad = np.argwhere(gb != wb)
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} elements differ, first at {i}: got {got[i]!r}, want {want[i]!r}")
+
+
+def f32_ulps(got: np.ndarray, want: np.ndarray) -> np.ndarray:
+    """Distance in float32 units in the last place (monotone integer image)."""
+    def key(a):
+        u = np.ascontiguousarray(a, np.float32).view(np.int32).astype(np.int64)
+        return np.where(u < 0, -(u & 0x7FFFFFFF), u)
+    return np.abs(key(got) - key(want))
+
+
+def sub_layout(L: oracle.Layout, tokens: np.ndarray) -> oracle.Layout:
+    """The oracle layout restricted to some tokens (combine is per token)."""
+    return oracle.Layout(s=len(tokens), e=L.e, k=L.k, capacity=L.capacity, rows=L.rows,
+                         idx=L.idx[tokens], counts=L.counts, kept=L.kept, offsets=L.offsets,
+                         dst=L.dst[tokens], src=L.src, flags=L.flags, checksum=L.checksum)
+
+
+def sample_tokens(s: int, n: int, seed: int = 0) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(s, size=min(n, s), replace=False).tolist())
+    pick.update({0, s - 1, min(255, s - 1), min(256, s - 1)})
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+def weight_grad_bound(gy32: np.ndarray, E32: np.ndarray, dst: np.ndarray) -> np.ndarray:
+    """sum_m |grad_y[t,m] * E[dst[t,j],m]| per route (float64), the scale of grad_w's error."""
+    s, k = dst.shape
+    out = np.zeros((s, k))
+    for j in range(k):
+        sel = dst[:, j] >= 0
+        out[sel, j] = np.abs(gy32[sel].astype(np.float64) * E32[dst[sel, j]].astype(np.float64)).sum(1)
+    return out

@@ -1,0 +1,158 @@
+"""The C-ABI library loads, exports every symbol include/moe_gate.h declares, and
+rejects bad arguments on the host before enqueuing anything (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import combine_moe_gate_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_gate.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(M.LIB_PATH):
+        from combine_moe_gate_amd import _build
+        _build.build()
+    return M.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\*\s]+?\b(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared but not exported"
+    assert set(names) == set(M.EXPORTS)
+
+
+def test_abi_version_and_status_names(lib):
+    assert lib.moe_abi_version() == 1
+    for code, name in M.STATUS_NAMES.items():
+        assert lib.moe_status_string(code).decode() == name
+    assert lib.moe_status_string(99).decode() == "MOE_STATUS_UNKNOWN"
+
+
+def test_layout_struct_matches_header_size():
+    # magic, 4 ints, rows, 10 pointers, size_t
+    assert ctypes.sizeof(M.LayoutStruct) == 8 + 16 + 8 + 10 * 8 + 8
+
+
+def test_workspace_bytes(lib):
+    wb = M.workspace_bytes
+    for args in [(256, 8, 2, 80), (8192, 128, 8, 0), (16384, 64, 4, 1024), (0, 4, 2, 3), (1, 1, 1, 0)]:
+        n = wb(*args)
+        assert n > 0 and n % 256 == 0
+    s, e, k = 8192, 128, 8
+    assert wb(s, e, k, 0) >= 4 * (2 * s * k + s * k)  # dst + route copy + src
+    assert wb(2 * s, e, k, 0) > wb(s, e, k, 0)
+    # invalid or unsupported sizes give 0
+    assert wb(-1, 8, 2, 0) == 0
+    assert wb(10, 8, 9, 0) == 0
+    assert wb(10, 2000, 2, 0) == 0
+    assert wb(10, 64, 17, 0) == 0
+    assert wb(2**30, 128, 8, 0) == 0  # s*k over 2**31
+
+
+# The calls below carry fake device addresses that must be rejected before any
+# kernel is enqueued. On a machine with a GPU they are skipped, so that a bug in the
+# checks could never launch a kernel on a fake address.
+no_gpu_only = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                                 reason="fake-pointer validation tests run only without a GPU")
+
+FAKE = ctypes.c_void_p(1 << 20)
+
+
+@no_gpu_only
+def test_gate_argument_checks(lib):
+    out = ctypes.c_void_p(1 << 21)
+    assert lib.moe_gate_topk(FAKE, 4, 8, 9, out, out, None) == 1  # k > e
+    assert "k must be in" in lib.moe_last_error().decode()
+    assert lib.moe_gate_topk(FAKE, 4, 2048, 2, out, out, None) == 2  # e too large
+    assert lib.moe_gate_topk(FAKE, 4, 64, 17, out, out, None) == 2  # k too large
+    assert lib.moe_gate_topk(None, 4, 8, 2, out, out, None) == 1  # NULL logits
+    assert lib.moe_gate_topk(FAKE, -1, 8, 2, out, out, None) == 1
+    assert lib.moe_gate_topk_backward(FAKE, FAKE, None, 4, 8, 2, out, None) == 1
+
+
+@no_gpu_only
+def test_layout_argument_checks(lib):
+    st = M.LayoutStruct()
+    need = M.workspace_bytes(100, 8, 2, 0)
+    assert lib.moe_dispatch_layout(FAKE, 100, 8, 2, 0, FAKE, need - 1, ctypes.byref(st), None) == 3
+    assert "workspace" in lib.moe_last_error().decode()
+    assert lib.moe_dispatch_layout(FAKE, 100, 8, 2, 0, ctypes.c_void_p((1 << 20) + 8), need,
+                                   ctypes.byref(st), None) == 5
+    assert lib.moe_dispatch_layout(FAKE, 100, 8, 2, 0, None, need, ctypes.byref(st), None) == 1
+    assert lib.moe_dispatch_layout(FAKE, 100, 8, 2, 0, FAKE, need, None, None) == 1
+    assert lib.moe_dispatch_layout(None, 100, 8, 2, 0, FAKE, need, ctypes.byref(st), None) == 1
+    assert st.magic == 0  # nothing was filled
+
+
+@no_gpu_only
+def test_row_calls_reject_foreign_or_bad_handles(lib):
+    st = M.LayoutStruct()  # never filled by moe_dispatch_layout
+    out = ctypes.c_void_p(1 << 21)
+    assert lib.moe_dispatch(ctypes.byref(st), FAKE, 64, 1, out, None) == 4
+    assert lib.moe_combine(ctypes.byref(st), FAKE, FAKE, 64, 1, out, None) == 4
+    assert lib.moe_combine_backward(ctypes.byref(st), FAKE, FAKE, FAKE, 64, 1, out, out, None) == 4
+    assert lib.moe_dispatch_backward(ctypes.byref(st), FAKE, 64, 1, out, None) == 4
+    assert lib.moe_dispatch_replay(ctypes.byref(st), None, FAKE, 64, 1, out, None) == 4
+    assert lib.moe_layout_read(ctypes.byref(st), None, None, None) == 4
+    assert lib.moe_dispatch(None, FAKE, 64, 1, out, None) == 1
+
+
+@no_gpu_only
+def test_row_calls_check_alignment_and_dtype(lib):
+    # a handle that looks valid to the host checks, over a fake workspace
+    s, e, k = 40, 8, 2
+    ws = 1 << 24
+    need = M.workspace_bytes(s, e, k, 0)
+    st = _fake_handle(s, e, k, 0, ws, need)
+    out = ctypes.c_void_p(1 << 22)
+    assert lib.moe_dispatch(ctypes.byref(st), FAKE, 3, 1, out, None) == 5  # 6-byte rows
+    assert lib.moe_dispatch(ctypes.byref(st), ctypes.c_void_p((1 << 20) + 4), 64, 1, out, None) == 5
+    assert lib.moe_dispatch(ctypes.byref(st), FAKE, 64, 7, out, None) == 1  # unknown dtype
+    assert lib.moe_dispatch(ctypes.byref(st), FAKE, 0, 1, out, None) == 1  # m = 0
+    assert lib.moe_combine(ctypes.byref(st), FAKE, None, 64, 1, out, None) == 1  # NULL weights
+    st.rows = st.rows + 1
+    assert lib.moe_dispatch(ctypes.byref(st), FAKE, 64, 1, out, None) == 4
+
+
+def _fake_handle(s, e, k, capacity, ws, need):
+    """Reproduce what moe_dispatch_layout fills in, without running it (256-byte carving)."""
+    def take(cur, n):
+        cur = (cur + 255) // 256 * 256
+        return cur, cur + n
+    rows = e * capacity if capacity > 0 else s * k
+    ntiles = (s + 255) // 256
+    cur = 0
+    offs = {}
+    for name, n in [("counts", 4 * e), ("kept", 4 * e), ("offsets", 4 * (e + 1)), ("dst", 4 * s * k),
+                    ("src", 4 * rows), ("route_idx", 4 * s * k), ("checksum", 8), ("flags", 4),
+                    ("scratch", 4 * ntiles * e)]:
+        at, cur = take(cur, n)
+        offs[name] = at
+    st = M.LayoutStruct()
+    st.magic = 0x4D4F454C41594F54
+    st.s, st.e, st.k, st.capacity, st.rows = s, e, k, capacity, rows
+    for name, at in offs.items():
+        setattr(st, name, ws + at)
+    st.workspace = ws
+    st.workspace_bytes = need
+    return st
+
+
+def test_binding_refuses_cpu_tensors():
+    x = torch.zeros(4, 8)
+    with pytest.raises((ValueError, RuntimeError)):
+        M.moe_gate_topk(x, 2)

@@ -1,0 +1,411 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Bars: expert ids, counts, offsets, slot maps and permuted buffers bit-exact;
+combine, dispatch backward and grad_E bit-exact when both sides are given the
+same weights (both accumulate in float32 in route order, separate multiply and
+add, one rounding); grad_w within 1e-6 of sum_m |grad_y * E| (float64 sums on
+both sides, summed in different orders); gate weights and gate gradients within
+one float32 ulp (float64 on both sides). End to end, where each side uses its
+own gate weights, outputs agree within 1e-6 relative (float32) or one ulp of
+the element type (bf16/f16), the tolerance the weights' last-ulp freedom needs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_moe_gate_amd as M
+import oracle
+import workloads as W
+from tests.gpu_util import (assert_bits_equal, f32_ulps, sample_tokens, sub_layout, to_dev,
+                            to_host, weight_grad_bound)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["tiny_capacity_top2", "dropless_top8_h2816", "gshard_capacity_drop"]
+ALL = list(W.WORKLOADS)
+
+
+def announce(*what):
+    print("CASE", *what, flush=True)
+
+
+def check_layout(Lg: M.Layout, Lo: oracle.Layout, what: str):
+    assert Lg.rows == Lo.rows, what
+    assert_bits_equal(to_host(Lg.counts), Lo.counts, f"{what} counts")
+    assert_bits_equal(to_host(Lg.kept), Lo.kept, f"{what} kept")
+    assert_bits_equal(to_host(Lg.offsets), Lo.offsets, f"{what} offsets")
+    assert_bits_equal(to_host(Lg.dst), Lo.dst, f"{what} dst")
+    assert_bits_equal(to_host(Lg.src), Lo.src, f"{what} src")
+    assert_bits_equal(to_host(Lg.route_idx), Lo.idx, f"{what} route copy")
+    flags, checksum = M.moe_layout_read(Lg)
+    assert flags == Lo.flags, f"{what} flags {flags} != {Lo.flags}"
+    assert checksum == Lo.checksum, f"{what} checksum"
+
+
+def check_buffer_chunked(buf_dev: torch.Tensor, x: np.ndarray, src: np.ndarray, what: str,
+                         chunk_rows: int = 16384):
+    """Every buffer row equals x[src[r]] bit for bit, or zero where src[r] = -1."""
+    rows = buf_dev.shape[0]
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        got = to_host(buf_dev[r0:r1])
+        s = src[r0:r1]
+        want = np.zeros_like(got)
+        have = s >= 0
+        want[have] = x[s[have]]
+        assert_bits_equal(got, want, f"{what} rows {r0}:{r1}")
+
+
+# ----------------------------------------------------------------------------
+# step 1: gate
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_gate_matches_oracle_on_workload(name):
+    announce("gate", name)
+    inp = W.make_inputs(name)
+    w = inp.workload
+    idx, wt = M.moe_gate_topk(to_dev(inp.logits), w.k)
+    idx_o, wt_o = oracle.gate_topk(inp.logits, w.k)
+    assert_bits_equal(to_host(idx), idx_o, f"{name} idx")
+    ulps = f32_ulps(to_host(wt), wt_o)
+    assert ulps.max() <= 1, f"{name} weights differ by {ulps.max()} ulp"
+
+
+@pytest.mark.parametrize("e,k", [(8, 1), (8, 8), (64, 2), (100, 8), (130, 16), (1024, 16), (1024, 1)])
+def test_gate_ties_signed_zeros_and_shapes(e, k):
+    announce("gate ties", e, k)
+    rng = np.random.default_rng(e * 100 + k)
+    s = 300
+    logits = rng.integers(-2, 3, size=(s, e)).astype(np.float32)
+    logits[rng.random((s, e)) < 0.2] = -0.0
+    logits[:5] = 0.0  # all-equal rows
+    idx, wt = M.moe_gate_topk(to_dev(logits), k)
+    idx_o, wt_o = oracle.gate_topk(logits, k)
+    assert_bits_equal(to_host(idx), idx_o, "idx")
+    assert f32_ulps(to_host(wt), wt_o).max() <= 1
+
+
+def test_gate_backward_matches_oracle():
+    announce("gate backward")
+    rng = np.random.default_rng(9)
+    for s, e, k in [(1000, 128, 8), (257, 8, 2), (64, 1024, 16), (33, 5, 5)]:
+        logits = rng.standard_normal((s, e)).astype(np.float32)
+        idx_o, wt_o = oracle.gate_topk(logits, k)
+        gw = rng.standard_normal((s, k)).astype(np.float32)
+        gl = to_host(M.moe_gate_topk_backward(to_dev(idx_o), to_dev(wt_o), to_dev(gw), e))
+        gl_o = oracle.gate_topk_backward(idx_o, wt_o, gw, e)
+        assert np.all(gl[gl_o == 0] == 0)
+        assert f32_ulps(gl, gl_o).max() <= 1, (s, e, k)
+
+
+# ----------------------------------------------------------------------------
+# step 2: layout
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_layout_matches_oracle_on_workload(name):
+    announce("layout", name)
+    inp = W.make_inputs(name)
+    w = inp.workload
+    idx_o, _ = oracle.gate_topk(inp.logits, w.k)
+    Lg = M.moe_dispatch_layout(to_dev(idx_o), w.e, w.capacity)
+    Lo = oracle.dispatch_layout(idx_o, w.e, w.capacity)
+    check_layout(Lg, Lo, name)
+
+
+LAYOUT_CASES = [
+    # s, e, k, capacity, routing
+    (1, 1, 1, 0, "uniform"), (1, 4, 4, 1, "uniform"), (255, 3, 2, 0, "uniform"),
+    (256, 40, 3, 7, "uniform"), (257, 64, 8, 0, "uniform"), (1000, 129, 5, 40, "uniform"),
+    (3000, 1024, 16, 0, "uniform"), (3000, 1024, 16, 50, "uniform"), (2049, 16, 4, 1, "skew"),
+    (5000, 8, 2, 0, "skew"), (5000, 8, 8, 1000, "skew"), (700, 2, 1, 0, "uniform"),
+]
+
+
+@pytest.mark.parametrize("s,e,k,cap,routing", LAYOUT_CASES)
+def test_layout_random_cases(s, e, k, cap, routing):
+    announce("layout case", s, e, k, cap, routing)
+    rng = np.random.default_rng(s * 7 + e * 3 + k + cap)
+    idx = W.skewed_idx(rng, s, e, k) if routing == "skew" else W.random_idx(rng, s, e, k)
+    Lg = M.moe_dispatch_layout(to_dev(idx), e, cap)
+    check_layout(Lg, oracle.dispatch_layout(idx, e, cap), f"s={s} e={e} k={k} c={cap}")
+
+
+@pytest.mark.parametrize("cap", [0, 3])
+def test_layout_invalid_routes_are_flagged_and_skipped(cap):
+    announce("layout invalid", cap)
+    rng = np.random.default_rng(77 + cap)
+    s, e, k = 600, 12, 4
+    idx = W.random_idx(rng, s, e, k)
+    idx[5, 2] = e          # out of range
+    idx[17, 0] = -3        # out of range
+    idx[300, 3] = idx[300, 1]  # duplicate
+    idx[599, 1] = idx[599, 0]
+    Lg = M.moe_dispatch_layout(to_dev(idx), e, cap)
+    Lo = oracle.dispatch_layout(idx, e, cap)
+    assert Lo.flags == 3
+    check_layout(Lg, Lo, "invalid")
+    # the permute leaves the skipped routes' rows as zero padding
+    x = rng.standard_normal((s, 16)).astype(np.float32)
+    buf = M.moe_dispatch(Lg, to_dev(x))
+    assert_bits_equal(to_host(buf), oracle.dispatch(Lo, x), "dispatch with invalid routes")
+
+
+# ----------------------------------------------------------------------------
+# steps 3-5 on small random cases (several tiles, ragged row tails)
+
+ROW_CASES = [
+    # s, m, dtype, e, k, capacity
+    (1000, 264, "bf16", 40, 3, 0),
+    (1000, 264, "bf16", 40, 3, 60),
+    (777, 72, "f16", 16, 4, 200),
+    (513, 36, "f32", 9, 2, 0),
+    (300, 4, "f32", 5, 5, 50),
+    (64, 8, "bf16", 1024, 16, 0),
+    (2000, 1032, "bf16", 128, 8, 0),
+    (129, 520, "f16", 3, 1, 20),
+]
+
+
+@pytest.mark.parametrize("s,m,dtype,e,k,cap", ROW_CASES)
+def test_rows_forward_backward_bit_exact(s, m, dtype, e, k, cap):
+    announce("rows", s, m, dtype, e, k, cap)
+    rng = np.random.default_rng(s + m + e + k + cap)
+    idx = W.random_idx(rng, s, e, k)
+    x = W.cast_input(rng.standard_normal((s, m)).astype(np.float32), dtype)
+    w = W.random_weights(rng, s, k)
+    Lo = oracle.dispatch_layout(idx, e, cap)
+    E = W.cast_input(rng.standard_normal((Lo.rows, m)).astype(np.float32), dtype)
+    gy = W.cast_input(rng.standard_normal((s, m)).astype(np.float32), dtype)
+    G = W.cast_input(rng.standard_normal((Lo.rows, m)).astype(np.float32), dtype)
+
+    Lg = M.moe_dispatch_layout(to_dev(idx), e, cap)
+    buf = M.moe_dispatch(Lg, to_dev(x, dtype))
+    assert_bits_equal(to_host(buf), oracle.dispatch(Lo, x), "dispatch")
+
+    y = M.moe_combine(Lg, to_dev(E, dtype), to_dev(w))
+    assert_bits_equal(to_host(y), oracle.combine(Lo, E, w, dtype), "combine")
+
+    gE, gw = M.moe_combine_backward(Lg, to_dev(gy, dtype), to_dev(E, dtype), to_dev(w))
+    gE_o, gw_o = oracle.combine_backward(Lo, gy, E, w, dtype)
+    assert_bits_equal(to_host(gE), gE_o, "grad_E")
+    bound = weight_grad_bound(oracle.to_f32(gy, dtype), oracle.to_f32(E, dtype), Lo.dst)
+    err = np.abs(to_host(gw).astype(np.float64) - gw_o)
+    assert np.all(err <= 1e-6 * bound), f"grad_w err {err.max()}"
+    assert f32_ulps(to_host(gw), gw_o).max() <= 1
+
+    gx = M.moe_dispatch_backward(Lg, to_dev(G, dtype))
+    assert_bits_equal(to_host(gx), oracle.dispatch_backward(Lo, G, dtype), "dispatch backward")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("cap", [0, 5])
+def test_unit_weight_round_trip_closed_form(dtype, cap):
+    """combine(dispatch(x), 1) equals each row times its kept-route count, exactly."""
+    announce("round trip", dtype, cap)
+    rng = np.random.default_rng(5)
+    s, e, k, m = 1500, 24, 6, 40
+    idx = W.random_idx(rng, s, e, k)
+    x32 = oracle.to_f32(W.cast_input(rng.standard_normal((s, m)).astype(np.float32), "bf16"), "bf16")
+    x = W.cast_input(x32, dtype)
+    Lg = M.moe_dispatch_layout(to_dev(idx), e, cap)
+    buf = M.moe_dispatch(Lg, to_dev(x, dtype))
+    y = to_host(M.moe_combine(Lg, buf, torch.ones((s, k), device="cuda")))
+    kept_t = (to_host(Lg.dst) >= 0).sum(1)
+    exact = kept_t[:, None] * oracle.to_f32(x, dtype).astype(np.float64) + 0.0
+    assert_bits_equal(y, oracle.from_f32(exact.astype(np.float32), dtype), "round trip")
+
+
+# ----------------------------------------------------------------------------
+# whole path on the five workloads, at full size
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_workload_path_matches_oracle(name):
+    announce("workload", name)
+    inp = W.make_inputs(name)
+    w = inp.workload
+    dt = w.dtype
+    idx_o, wt_o = oracle.gate_topk(inp.logits, w.k)
+    Lo = oracle.dispatch_layout(idx_o, w.e, w.capacity)
+
+    # GPU path end to end
+    logits = to_dev(inp.logits)
+    x = to_dev(inp.x, dt)
+    gy = to_dev(inp.grad_y, dt)
+    idx, wt = M.moe_gate_topk(logits, w.k)
+    Lg = M.moe_dispatch_layout(idx, w.e, w.capacity)
+    buf = M.moe_dispatch(Lg, x)
+    y = M.moe_combine(Lg, buf, wt)
+    replay = M.moe_dispatch_replay(Lg, x, idx)
+    gE, gw = M.moe_combine_backward(Lg, gy, replay, wt)
+    gx = M.moe_dispatch_backward(Lg, gE)
+    gl = M.moe_gate_topk_backward(idx, wt, gw, w.e)
+    torch.cuda.synchronize()
+
+    assert_bits_equal(to_host(idx), idx_o, "idx")
+    check_layout(Lg, Lo, name)
+    check_buffer_chunked(buf, inp.x, Lo.src, "dispatch")
+    assert torch.equal(replay.view(torch.uint8), buf.view(torch.uint8)), "replay differs"
+
+    # op level, bit exact: the oracle's weights fed to the GPU combine
+    wt_o_dev = to_dev(wt_o)
+    toks = np.arange(w.s) if name in SMALL else sample_tokens(w.s, 512)
+    S = sub_layout(Lo, toks)
+    E_o = oracle.dispatch(Lo, inp.x) if name in SMALL else None
+    if E_o is None:
+        E_o = np.zeros((Lo.rows, w.m), dtype=inp.x.dtype)
+        rows = S.dst[S.dst >= 0]
+        E_o[rows] = inp.x[Lo.src[rows]]
+    y_same_w = to_host(M.moe_combine(Lg, buf, wt_o_dev))[toks]
+    assert_bits_equal(y_same_w, oracle.combine(S, E_o, wt_o[toks], dt), "combine (same weights)")
+
+    gE_s, gw_s = M.moe_combine_backward(Lg, gy, buf, wt_o_dev)
+    gE_o, gw_o = oracle.combine_backward(S, inp.grad_y[toks], E_o, wt_o[toks], dt)
+    rows = S.dst[S.dst >= 0]
+    assert_bits_equal(to_host(gE_s)[rows] if name in SMALL else to_host(gE_s[torch.from_numpy(rows).cuda()]),
+                      gE_o[rows], "grad_E (same weights)")
+    bound = weight_grad_bound(oracle.to_f32(inp.grad_y[toks], dt), oracle.to_f32(E_o, dt), S.dst)
+    err = np.abs(to_host(gw_s)[toks].astype(np.float64) - gw_o)
+    assert np.all(err <= 1e-6 * bound)
+
+    gx_s = to_host(M.moe_dispatch_backward(Lg, gE_s))[toks]
+    # oracle dispatch backward over the same grad_E rows (the oracle's own grad_E)
+    assert_bits_equal(gx_s, oracle.dispatch_backward(S, gE_o, dt), "dispatch backward (same weights)")
+
+    # end to end with each side's own weights: within the stated tolerance
+    assert f32_ulps(to_host(wt), wt_o).max() <= 1
+    y_o = oracle.combine(S, E_o, wt_o[toks], dt)
+    y_g = to_host(y)[toks]
+    if dt == "f32":
+        mag = np.zeros((len(toks), w.m))
+        for j in range(w.k):
+            sel = S.dst[:, j] >= 0
+            mag[sel] += np.abs(wt_o[toks][sel, j, None].astype(np.float64) * E_o[S.dst[sel, j]])
+        assert np.all(np.abs(y_g.astype(np.float64) - y_o) <= 1e-6 * mag + 1e-30)
+    else:
+        yg, yo = oracle.to_f32(y_g, dt).astype(np.float64), oracle.to_f32(y_o, dt).astype(np.float64)
+        assert np.all(np.abs(yg - yo) <= dtype_ulp(np.maximum(np.abs(yg), np.abs(yo)), dt))
+    # grad_w does not depend on the weights, so the GPU's end-to-end grad_w meets the
+    # oracle's directly; the gate gradient then differs only through last-ulp weights
+    gw_g = to_host(gw)[toks]
+    assert np.all(np.abs(gw_g.astype(np.float64) - gw_o) <= 1e-6 * bound)
+    gl_o = oracle.gate_topk_backward(idx_o[toks], wt_o[toks], gw_o, w.e)
+    gl_g = to_host(gl)[toks]
+    assert np.all(gl_g[gl_o == 0] == 0)
+    w64, g64 = wt_o[toks].astype(np.float64), gw_o.astype(np.float64)
+    scale = np.zeros((len(toks), w.e))
+    dotmag = np.abs(w64 * g64).sum(1, keepdims=True)
+    np.put_along_axis(scale, idx_o[toks].astype(np.int64), np.abs(w64) * (np.abs(g64) + dotmag), axis=1)
+    assert np.all(np.abs(gl_g.astype(np.float64) - gl_o) <= 8 * 2.0 ** -24 * scale + 1e-38)
+
+
+def dtype_ulp(mag: np.ndarray, dt: str) -> np.ndarray:
+    """One unit in the last place of bf16 (8-bit precision) or f16 (11-bit) at |v|."""
+    p, tiny = (8, 2.0 ** -133) if dt == "bf16" else (11, 2.0 ** -24)
+    _, ex = np.frexp(mag)
+    return np.maximum(np.ldexp(1.0, ex - p), tiny)
+
+
+# ----------------------------------------------------------------------------
+# replay, determinism, handles, degenerate sizes
+
+
+def test_replay_reproduces_rows_and_flags_mismatch():
+    announce("replay")
+    w = W.WORKLOADS["checkpoint_replay_h2816"]
+    inp = W.make_inputs(w)
+    idx, wt = M.moe_gate_topk(to_dev(inp.logits), w.k)
+    x = to_dev(inp.x, w.dtype)
+    L1 = M.moe_dispatch_layout(idx, w.e, w.capacity)
+    buf = M.moe_dispatch(L1, x)
+    rep = M.moe_dispatch_replay(L1, x, idx)
+    assert torch.equal(rep.view(torch.uint8), buf.view(torch.uint8))
+    # a second layout from identical routing gives identical row counts and maps
+    L2 = M.moe_dispatch_layout(idx.clone(), w.e, w.capacity)
+    for f in ("counts", "kept", "offsets", "dst", "src"):
+        assert torch.equal(getattr(L1, f), getattr(L2, f)), f
+    assert M.moe_layout_read(L1) == (0, M.moe_layout_read(L2)[1])
+    # replaying with different routing is reported, not hidden
+    other = idx.clone()
+    other[123, 4] = (other[123, 4] + 1) % w.e
+    M.moe_dispatch_replay(L1, x, other)
+    flags, _ = M.moe_layout_read(L1)
+    assert flags & M.FLAG_REPLAY_MISMATCH
+    assert not (M.moe_layout_read(L2)[0] & M.FLAG_REPLAY_MISMATCH)
+
+
+def test_results_are_deterministic():
+    announce("determinism")
+    w = W.WORKLOADS["zipf_skew_h4096"]
+    inp = W.make_inputs(w)
+    outs = []
+    for _ in range(2):
+        idx, wt = M.moe_gate_topk(to_dev(inp.logits), w.k)
+        L = M.moe_dispatch_layout(idx, w.e, w.capacity)
+        buf = M.moe_dispatch(L, to_dev(inp.x, w.dtype))
+        y = M.moe_combine(L, buf, wt)
+        gE, gw = M.moe_combine_backward(L, to_dev(inp.grad_y, w.dtype), buf, wt)
+        gx = M.moe_dispatch_backward(L, gE)
+        outs.append([t.clone() for t in (idx, wt, L.dst, L.src, y, gw, gx)])
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
+
+
+def test_several_live_layouts():
+    """fwd(b1), fwd(b2), bwd(b2), bwd(b1): each layout stays valid."""
+    announce("live handles")
+    rng = np.random.default_rng(3)
+    s, e, k, m = 900, 32, 4, 64
+    cases = []
+    for cap in (0, 50):
+        idx = W.random_idx(rng, s, e, k)
+        x = W.cast_input(rng.standard_normal((s, m)).astype(np.float32), "bf16")
+        cases.append((idx, x, cap, M.moe_dispatch_layout(to_dev(idx), e, cap)))
+    for idx, x, cap, Lg in reversed(cases):
+        Lo = oracle.dispatch_layout(idx, e, cap)
+        check_layout(Lg, Lo, f"live c={cap}")
+        buf = M.moe_dispatch(Lg, to_dev(x, "bf16"))
+        gx = M.moe_dispatch_backward(Lg, buf)
+        assert_bits_equal(to_host(gx), oracle.dispatch_backward(Lo, oracle.dispatch(Lo, x), "bf16"), "gx")
+
+
+@pytest.mark.parametrize("cap", [0, 4])
+def test_empty_batch(cap):
+    announce("empty", cap)
+    e, k, m = 6, 2, 8
+    idx = torch.zeros((0, k), dtype=torch.int32, device="cuda")
+    L = M.moe_dispatch_layout(idx, e, cap)
+    assert L.rows == (e * cap if cap else 0)
+    x = torch.zeros((0, m), dtype=torch.bfloat16, device="cuda")
+    buf = M.moe_dispatch(L, x)
+    if cap:
+        buf_bits = buf.view(torch.int16)
+        assert int(buf_bits.abs().sum()) == 0
+        assert torch.all(L.src == -1)
+    y = M.moe_combine(L, buf, torch.zeros((0, k), device="cuda"))
+    assert y.shape == (0, m)
+    gE, gw = M.moe_combine_backward(L, x, buf, torch.zeros((0, k), device="cuda"))
+    assert gE.shape == (L.rows, m) and gw.shape == (0, k)
+    assert torch.all(L.counts == 0)
+    lg, lw = M.moe_gate_topk(torch.zeros((0, e), device="cuda"), k)
+    assert lg.shape == (0, k)
+    torch.cuda.synchronize()
+
+
+def test_all_routes_dropped_give_zero_rows():
+    announce("all dropped")
+    s, e, k, m = 40, 2, 2, 16
+    idx = np.tile(np.array([[0, 1]], np.int32), (s, 1))
+    Lg = M.moe_dispatch_layout(to_dev(idx), e, 1)  # only token 0 fits
+    x = -np.abs(np.random.default_rng(0).standard_normal((s, m))).astype(np.float32)
+    buf = M.moe_dispatch(Lg, to_dev(x))
+    y = to_host(M.moe_combine(Lg, buf, torch.full((s, k), 0.5, device="cuda")))
+    assert np.all(bits(y[1:]) == 0)  # +0.0, not -0.0
+    assert np.array_equal(y[0], x[0])
+
+
+def bits(a):
+    return np.ascontiguousarray(a).view(np.uint32)

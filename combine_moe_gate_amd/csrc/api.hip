@@ -68,6 +68,8 @@ moe_status_t check_sizes(int32_t s, int32_t e, int32_t k, int32_t capacity) {
     return fail(MOE_ERR_UNSUPPORTED, "e=%d exceeds MOE_MAX_EXPERTS=%d", e, MOE_MAX_EXPERTS);
   if (k > MOE_MAX_TOPK)
     return fail(MOE_ERR_UNSUPPORTED, "k=%d exceeds MOE_MAX_TOPK=%d", k, MOE_MAX_TOPK);
+  if (s > INT32_MAX - 65536)
+    return fail(MOE_ERR_UNSUPPORTED, "s=%d exceeds the supported token count", s);
   if (static_cast<int64_t>(s) * k > INT32_MAX)
     return fail(MOE_ERR_UNSUPPORTED, "s*k=%lld exceeds 32-bit route ids",
                 static_cast<long long>(s) * k);

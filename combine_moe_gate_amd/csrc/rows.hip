@@ -2,45 +2,77 @@
 // backward passes.
 //
 // All four are HBM-bound row gathers/scatters, not contractions, so there is no MFMA
-// here. Every kernel is token-major: one wave64 per token, the token's k route rows
-// named by the layout (dst) and kept in scalar registers. Each lane moves 16-byte
-// chunks (global_load/store_dwordx4), chunk c of a row at lane c mod 64, so a wave
-// touches 1 KiB of a row per step, fully coalesced.
+// here. Work is token-major: workgroup t owns token t (its k destination rows come
+// from the layout's dst and live in scalar registers). A row of rc 16-byte chunks is
+// cut into ng groups of 64*U chunks; the workgroup's waves take the groups in turn,
+// lane l moving chunks l, l+64, ... of a group (global_load/store_dwordx4, fully
+// coalesced). The first group a token visits is rotated by the token id, so that
+// the waves in flight spread over all offsets within rows instead of all reading
+// the same offset of 8 KiB-aligned rows at once (measured: +20-30% on a 512 MiB
+// buffer). Streaming accesses that are not reused use nontemporal hints.
 //
 //   dispatch          x[t] read once, written to its k rows (DeepSpeed PR "Add an
 //                     opt-in DeepEP transport for the AutoEP expert all-to-all", first
 //                     commit: tokens are taken before top-k expansion and replicated).
-//   combine           the k rows of a token loaded together, then summed in route
-//                     order in float32 with separate multiply and add, rounded once
-//                     (DeepSpeed PR "MoE dispatch: fix silent Tutel + TP corruption,
-//                     speed up native and Tutel paths", part 3: fp32 accumulation; PR
-//                     8213's review thread on combine weights: the weights are applied).
-//   dispatch backward the same kernel without weights (the gradient of a dispatch is a
-//                     combine, PR 8213 first commit).
-//   combine backward  grad_y[t] read once; for each route the weighted copy goes to the
-//                     route's row and the dot product with the expert row accumulates
-//                     in float64 (the gradient of a combine is a dispatch, plus the
+//   combine           a token's k rows loaded together, summed in route order in
+//                     float32 with separate multiply and add, rounded once (DeepSpeed
+//                     PR "MoE dispatch: fix silent Tutel + TP corruption, speed up
+//                     native and Tutel paths", part 3: fp32 accumulation; PR 8213's
+//                     review thread on combine weights: the weights are applied).
+//   dispatch backward the same kernel without weights (the gradient of a dispatch is
+//                     a combine, PR 8213 first commit).
+//   combine backward  grad_y[t] read once; each route gets the weighted copy in its row
+//                     and the dot product with its expert row accumulates in float64,
+//                     per wave, then across the workgroup's waves through LDS in a
+//                     fixed order (the gradient of a combine is a dispatch, plus the
 //                     weights' gradient of PR 8213's review-fix commit).
 //
 // Rows that no route points at (capacity padding, or rows past the last valid route)
-// are zero-filled by a grid-stride tail loop in the kernels that write [rows, m]
-// buffers. No floating-point atomics anywhere: results are deterministic.
+// are zero-filled by extra workgroups after the token workgroups, in the kernels that
+// write [rows, m] buffers. No floating-point atomics: results are deterministic.
 #include "internal.h"
 #include "moe_device.h"
 
 namespace moe {
 
-// Grid-stride loop over the buffer rows that no placed route fills; each wave zeroes
-// whole rows.
-__device__ __forceinline__ void zero_unfilled_rows(chunk_t* __restrict__ out, int64_t rc,
+template <bool NT>
+__device__ __forceinline__ chunk_t load_chunk(const chunk_t* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <bool NT>
+__device__ __forceinline__ void store_chunk(chunk_t* p, const chunk_t& v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+// How a row is cut into groups and how many waves share a token.
+struct RowSplit {
+  int64_t rc;   // 16-byte chunks per row
+  int64_t ng;   // groups of 64*U chunks per row
+  int wpb;      // waves per workgroup (one token per workgroup)
+};
+
+// The token owned by this workgroup's wave `wv` visits groups gi = wv, wv+wpb, ...;
+// group gi maps to g = (gi + t) mod ng.
+__device__ __forceinline__ int64_t rotated_group(int64_t gi, int64_t t, int64_t ng) {
+  int64_t g = gi + t % ng;
+  return g >= ng ? g - ng : g;
+}
+
+// Workgroups past the s token workgroups zero the rows that no placed route fills.
+template <bool NTS>
+__device__ __forceinline__ void zero_unfilled_rows(chunk_t* __restrict__ out, int64_t rc, int s,
                                                    int capacity, int e, int32_t rows,
                                                    const int32_t* __restrict__ kept,
                                                    const int32_t* __restrict__ offsets) {
   const int lane = lane_id();
-  const int32_t wave = blockIdx.x * kWavesPerBlock + wave_in_block();
-  const int32_t nwaves = gridDim.x * kWavesPerBlock;
+  const int wpb = blockDim.x >> 6;
+  const int32_t wave = (blockIdx.x - s) * wpb + wave_in_block();
+  const int32_t nwaves = (gridDim.x - s) * wpb;
   const int32_t begin = capacity > 0 ? 0 : offsets[e];
-  const chunk_t z = chunk_t{0u, 0u, 0u, 0u};
+  const chunk_t z = {0u, 0u, 0u, 0u};
   for (int32_t r = begin + wave; r < rows; r += nwaves) {
     bool pad = true;
     if (capacity > 0) {
@@ -49,7 +81,7 @@ __device__ __forceinline__ void zero_unfilled_rows(chunk_t* __restrict__ out, in
     }
     if (pad) {
       chunk_t* o = out + static_cast<size_t>(r) * rc;
-      for (int64_t c = lane; c < rc; c += kWave) o[c] = z;
+      for (int64_t c = lane; c < rc; c += kWave) store_chunk<NTS>(o + c, z);
     }
   }
 }
@@ -62,62 +94,67 @@ __device__ __forceinline__ void load_dst(const int32_t* __restrict__ dst, int t,
 }
 
 // ---------------------------------------------------------------------------------
-// dispatch
+// dispatch: normal loads of x (tokens are small and may be reread by a replay),
+// nontemporal stores of the buffer rows
 
-template <int KMAX>
+template <int KMAX, int U>
 __global__ __launch_bounds__(kBlock) void dispatch_kernel(
     const chunk_t* __restrict__ x, const int32_t* __restrict__ dst,
     const int32_t* __restrict__ verify_idx, const int32_t* __restrict__ route_idx,
-    int32_t* __restrict__ flags, int s, int k, int64_t rc, chunk_t* __restrict__ out,
+    int32_t* __restrict__ flags, int s, int k, RowSplit sp, chunk_t* __restrict__ out,
     int capacity, int e, int32_t rows, const int32_t* __restrict__ kept,
     const int32_t* __restrict__ offsets) {
-  constexpr int U = 4;  // chunks in flight per lane
+  if (static_cast<int>(blockIdx.x) >= s) {
+    zero_unfilled_rows<true>(out, sp.rc, s, capacity, e, rows, kept, offsets);
+    return;
+  }
   const int lane = lane_id();
-  const int t = blockIdx.x * kWavesPerBlock + wave_in_block();
-  if (t < s) {
-    int d[KMAX];
-    load_dst<KMAX>(dst, t, k, d);
-    if (verify_idx != nullptr) {
-      const size_t o = static_cast<size_t>(t) * k + lane;
-      const bool bad = lane < k && verify_idx[o] != route_idx[o];
-      if (__ballot(bad) != 0ull && lane == 0) atomicOr(flags, 4);
+  const int wv = wave_in_block();
+  const int t = blockIdx.x;
+  int d[KMAX];
+  load_dst<KMAX>(dst, t, k, d);
+  if (verify_idx != nullptr && wv == 0) {
+    const size_t o = static_cast<size_t>(t) * k + lane;
+    const bool bad = lane < k && verify_idx[o] != route_idx[o];
+    if (__ballot(bad) != 0ull && lane == 0) atomicOr(flags, 4);
+  }
+  const chunk_t* xr = x + static_cast<size_t>(t) * sp.rc;
+  for (int64_t gi = wv; gi < sp.ng; gi += sp.wpb) {
+    const int64_t c0 = rotated_group(gi, t, sp.ng) * (kWave * U) + lane;
+    chunk_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * kWave;
+      if (c < sp.rc) v[u] = load_chunk<false>(xr + c);
     }
-    const chunk_t* xr = x + static_cast<size_t>(t) * rc;
-    for (int64_t c0 = lane; c0 < rc; c0 += U * kWave) {
-      chunk_t v[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t c = c0 + u * kWave;
-        if (c < rc) v[u] = *(xr + c);
-      }
+    for (int j = 0; j < KMAX; ++j) {
+      if (d[j] >= 0) {
+        chunk_t* o = out + static_cast<size_t>(d[j]) * sp.rc;
 #pragma unroll
-      for (int j = 0; j < KMAX; ++j) {
-        if (d[j] >= 0) {
-          chunk_t* o = out + static_cast<size_t>(d[j]) * rc;
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const int64_t c = c0 + u * kWave;
-            if (c < rc) o[c] = v[u];
-          }
+        for (int u = 0; u < U; ++u) {
+          const int64_t c = c0 + u * kWave;
+          if (c < sp.rc) store_chunk<true>(o + c, v[u]);
         }
       }
     }
   }
-  zero_unfilled_rows(out, rc, capacity, e, rows, kept, offsets);
 }
 
 // ---------------------------------------------------------------------------------
-// combine (weighted) and dispatch backward (unweighted)
+// combine (weighted) and dispatch backward (unweighted): nontemporal loads of the
+// k rows, one store per chunk
 
-template <int DT, int KMAX, bool WEIGHTED>
+template <int DT, int KMAX, bool WEIGHTED, int U>
 __global__ __launch_bounds__(kBlock) void combine_kernel(const chunk_t* __restrict__ rows_in,
                                                          const float* __restrict__ w,
                                                          const int32_t* __restrict__ dst,
-                                                         int s, int k, int64_t rc,
+                                                         int s, int k, RowSplit sp,
                                                          chunk_t* __restrict__ y) {
   constexpr int N = ChunkElems<DT>::value;
   const int lane = lane_id();
-  const int t = blockIdx.x * kWavesPerBlock + wave_in_block();
+  const int wv = wave_in_block();
+  const int t = blockIdx.x;
   if (t >= s) return;
   int d[KMAX];
   load_dst<KMAX>(dst, t, k, d);
@@ -126,186 +163,240 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const chunk_t* __restri
   for (int j = 0; j < KMAX; ++j)
     wt[j] = (WEIGHTED && j < k) ? w[static_cast<size_t>(t) * k + j] : 1.0f;
 
-  chunk_t* yr = y + static_cast<size_t>(t) * rc;
-  for (int64_t c = lane; c < rc; c += kWave) {
-    chunk_t v[KMAX];
+  chunk_t* yr = y + static_cast<size_t>(t) * sp.rc;
+  for (int64_t gi = wv; gi < sp.ng; gi += sp.wpb) {
+    const int64_t c0 = rotated_group(gi, t, sp.ng) * (kWave * U) + lane;
+    chunk_t v[U][KMAX];
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-      if (d[j] >= 0) v[j] = *(rows_in + static_cast<size_t>(d[j]) * rc + c);
-    float acc[N];
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * kWave;
 #pragma unroll
-    for (int n = 0; n < N; ++n) acc[n] = 0.0f;
+      for (int j = 0; j < KMAX; ++j)
+        if (d[j] >= 0 && c < sp.rc)
+          v[u][j] = load_chunk<true>(rows_in + static_cast<size_t>(d[j]) * sp.rc + c);
+    }
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      if (d[j] >= 0) {
-        float f[N];
-        unpack<DT>(v[j], f);
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * kWave;
+      if (c < sp.rc) {
+        float acc[N];
 #pragma unroll
-        for (int n = 0; n < N; ++n)
-          acc[n] = WEIGHTED ? __fadd_rn(acc[n], __fmul_rn(wt[j], f[n])) : __fadd_rn(acc[n], f[n]);
+        for (int n = 0; n < N; ++n) acc[n] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+          if (d[j] >= 0) {
+            float f[N];
+            unpack<DT>(v[u][j], f);
+#pragma unroll
+            for (int n = 0; n < N; ++n)
+              acc[n] = WEIGHTED ? __fadd_rn(acc[n], __fmul_rn(wt[j], f[n])) : __fadd_rn(acc[n], f[n]);
+          }
+        }
+        yr[c] = pack<DT>(acc);
       }
     }
-    yr[c] = pack<DT>(acc);
   }
 }
 
 // ---------------------------------------------------------------------------------
 // combine backward: grad_E rows and grad_w
 
-template <int DT, int KMAX>
+template <int DT, int KMAX, int U>
 __global__ __launch_bounds__(kBlock) void combine_backward_kernel(
     const chunk_t* __restrict__ gy, const chunk_t* __restrict__ E, const float* __restrict__ w,
-    const int32_t* __restrict__ dst, int s, int k, int64_t rc, chunk_t* __restrict__ gE,
+    const int32_t* __restrict__ dst, int s, int k, RowSplit sp, chunk_t* __restrict__ gE,
     float* __restrict__ gw, int capacity, int e, int32_t rows,
     const int32_t* __restrict__ kept, const int32_t* __restrict__ offsets) {
   constexpr int N = ChunkElems<DT>::value;
+  __shared__ double wave_part[kWavesPerBlock][KMAX];
+  if (static_cast<int>(blockIdx.x) >= s) {
+    zero_unfilled_rows<true>(gE, sp.rc, s, capacity, e, rows, kept, offsets);
+    return;
+  }
   const int lane = lane_id();
-  const int t = blockIdx.x * kWavesPerBlock + wave_in_block();
-  if (t < s) {
-    int d[KMAX];
-    load_dst<KMAX>(dst, t, k, d);
-    float wt[KMAX];
-    double part[KMAX];
+  const int wv = wave_in_block();
+  const int t = blockIdx.x;
+  int d[KMAX];
+  load_dst<KMAX>(dst, t, k, d);
+  float wt[KMAX];
+  double part[KMAX];
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      wt[j] = (j < k) ? w[static_cast<size_t>(t) * k + j] : 0.0f;
-      part[j] = 0.0;
-    }
-    const chunk_t* gr = gy + static_cast<size_t>(t) * rc;
-    for (int64_t c = lane; c < rc; c += kWave) {
-      float g[N];
-      unpack<DT>(*(gr + c), g);
-      chunk_t v[KMAX];
+  for (int j = 0; j < KMAX; ++j) {
+    wt[j] = (j < k) ? w[static_cast<size_t>(t) * k + j] : 0.0f;
+    part[j] = 0.0;
+  }
+  const chunk_t* gr = gy + static_cast<size_t>(t) * sp.rc;
+  for (int64_t gi = wv; gi < sp.ng; gi += sp.wpb) {
+    const int64_t c0 = rotated_group(gi, t, sp.ng) * (kWave * U) + lane;
 #pragma unroll
-      for (int j = 0; j < KMAX; ++j)
-        if (d[j] >= 0) v[j] = *(E + static_cast<size_t>(d[j]) * rc + c);
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * kWave;
+      if (c < sp.rc) {
+        float g[N];
+        unpack<DT>(load_chunk<true>(gr + c), g);
+        chunk_t v[KMAX];
 #pragma unroll
-      for (int j = 0; j < KMAX; ++j) {
-        if (d[j] >= 0) {
-          float f[N], o[N];
-          unpack<DT>(v[j], f);
+        for (int j = 0; j < KMAX; ++j)
+          if (d[j] >= 0) v[j] = load_chunk<true>(E + static_cast<size_t>(d[j]) * sp.rc + c);
 #pragma unroll
-          for (int n = 0; n < N; ++n) {
-            // float32 x float32 is exact in float64, so the fma rounds only the sum
-            part[j] = fma(static_cast<double>(g[n]), static_cast<double>(f[n]), part[j]);
-            o[n] = __fmul_rn(wt[j], g[n]);
+        for (int j = 0; j < KMAX; ++j) {
+          if (d[j] >= 0) {
+            float f[N], o[N];
+            unpack<DT>(v[j], f);
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+              // float32 x float32 is exact in float64, so the fma rounds only the sum
+              part[j] = fma(static_cast<double>(g[n]), static_cast<double>(f[n]), part[j]);
+              o[n] = __fmul_rn(wt[j], g[n]);
+            }
+            store_chunk<true>(gE + static_cast<size_t>(d[j]) * sp.rc + c, pack<DT>(o));
           }
-          gE[static_cast<size_t>(d[j]) * rc + c] = pack<DT>(o);
         }
       }
     }
+  }
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      if (j < k) {
-        const double tot = wave_sum(part[j]);
-        if (lane == 0) gw[static_cast<size_t>(t) * k + j] = d[j] >= 0 ? static_cast<float>(tot) : 0.0f;
-      }
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k) {
+      const double tot = wave_sum(part[j]);
+      if (lane == 0) wave_part[wv][j] = tot;
     }
   }
-  zero_unfilled_rows(gE, rc, capacity, e, rows, kept, offsets);
+  __syncthreads();
+  if (wv == 0 && lane < k) {
+    double tot = 0.0;
+    for (int q = 0; q < sp.wpb; ++q) tot += wave_part[q][lane];
+    int dj = -1;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (j == lane) dj = d[j];
+    gw[static_cast<size_t>(t) * k + lane] = dj >= 0 ? static_cast<float>(tot) : 0.0f;
+  }
 }
 
 // ---------------------------------------------------------------------------------
 // launchers
 
-static int row_grid(const LayoutView& L, bool writes_rows) {
-  int64_t g = (static_cast<int64_t>(L.s) + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (writes_rows && L.capacity > 0) {
-    // enough waves for the zero padding even when there are few tokens
-    int64_t pad = (L.rows + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (pad > 2048) pad = 2048;
-    if (g < pad) g = pad;
-  }
-  return static_cast<int>(g);
+// Chunks per lane per group in dispatch: 2 once a row has at least 256 chunks (4 KiB),
+// so a long row still splits over four waves.
+static int chunks_per_lane(int64_t rc) { return rc >= 4 * kWave ? 2 : 1; }
+
+static RowSplit make_split(int64_t rc, int U) {
+  RowSplit sp;
+  sp.rc = rc;
+  sp.ng = (rc + kWave * U - 1) / (kWave * U);
+  sp.wpb = static_cast<int>(sp.ng < kWavesPerBlock ? sp.ng : kWavesPerBlock);
+  return sp;
 }
 
-template <int KMAX>
+// Workgroups that zero unfilled rows: enough for every capacity row; a few in
+// dropless mode, where only flagged-invalid routes leave rows unfilled.
+static int pad_blocks(const LayoutView& L, int wpb) {
+  if (L.capacity > 0) {
+    int64_t b = (L.rows + 8 * wpb - 1) / (8 * wpb);
+    return static_cast<int>(b < 4096 ? (b < 1 ? 1 : b) : 4096);
+  }
+  return L.s > 0 ? 16 : 0;
+}
+
+template <int KMAX, int U>
 static void dispatch_k(const LayoutView& L, const int32_t* verify_idx, const void* x,
-                       int64_t rc, void* out, int grid, hipStream_t stream) {
-  dispatch_kernel<KMAX><<<grid, kBlock, 0, stream>>>(
-      static_cast<const chunk_t*>(x), L.dst, verify_idx, L.route_idx, L.flags, L.s, L.k, rc,
-      static_cast<chunk_t*>(out), L.capacity, L.e, static_cast<int32_t>(L.rows), L.kept, L.offsets);
+                       const RowSplit& sp, void* out, hipStream_t stream) {
+  const int grid = L.s + pad_blocks(L, sp.wpb);
+  if (grid == 0) return;
+  dispatch_kernel<KMAX, U><<<grid, sp.wpb * kWave, 0, stream>>>(
+      static_cast<const chunk_t*>(x), L.dst, verify_idx, L.route_idx, L.flags, L.s, L.k, sp,
+      static_cast<chunk_t*>(out), L.capacity, L.e, static_cast<int32_t>(L.rows), L.kept,
+      L.offsets);
+}
+
+template <int U>
+static void dispatch_u(const LayoutView& L, const int32_t* verify_idx, const void* x,
+                       const RowSplit& sp, void* out, hipStream_t stream) {
+  switch (route_bound(L.k)) {
+    case 1: dispatch_k<1, U>(L, verify_idx, x, sp, out, stream); break;
+    case 2: dispatch_k<2, U>(L, verify_idx, x, sp, out, stream); break;
+    case 4: dispatch_k<4, U>(L, verify_idx, x, sp, out, stream); break;
+    case 8: dispatch_k<8, U>(L, verify_idx, x, sp, out, stream); break;
+    default: dispatch_k<16, U>(L, verify_idx, x, sp, out, stream); break;
+  }
 }
 
 hipError_t launch_dispatch(const LayoutView& L, const int32_t* verify_idx, const void* x,
                            int64_t rc, void* out, hipStream_t stream) {
-  const int grid = row_grid(L, true);
-  if (grid == 0) return hipSuccess;
-  switch (route_bound(L.k)) {
-    case 1: dispatch_k<1>(L, verify_idx, x, rc, out, grid, stream); break;
-    case 2: dispatch_k<2>(L, verify_idx, x, rc, out, grid, stream); break;
-    case 4: dispatch_k<4>(L, verify_idx, x, rc, out, grid, stream); break;
-    case 8: dispatch_k<8>(L, verify_idx, x, rc, out, grid, stream); break;
-    default: dispatch_k<16>(L, verify_idx, x, rc, out, grid, stream); break;
-  }
+  const int U = chunks_per_lane(rc);
+  const RowSplit sp = make_split(rc, U);
+  if (U == 2) dispatch_u<2>(L, verify_idx, x, sp, out, stream);
+  else dispatch_u<1>(L, verify_idx, x, sp, out, stream);
   return hipGetLastError();
 }
 
 template <int DT, int KMAX>
-static void combine_k(const LayoutView& L, const void* in, const float* w, int64_t rc, void* y,
-                      int grid, hipStream_t stream) {
+static void combine_k(const LayoutView& L, const void* in, const float* w, const RowSplit& sp,
+                      void* y, hipStream_t stream) {
   if (w != nullptr)
-    combine_kernel<DT, KMAX, true><<<grid, kBlock, 0, stream>>>(
-        static_cast<const chunk_t*>(in), w, L.dst, L.s, L.k, rc, static_cast<chunk_t*>(y));
+    combine_kernel<DT, KMAX, true, 1><<<L.s, sp.wpb * kWave, 0, stream>>>(
+        static_cast<const chunk_t*>(in), w, L.dst, L.s, L.k, sp, static_cast<chunk_t*>(y));
   else
-    combine_kernel<DT, KMAX, false><<<grid, kBlock, 0, stream>>>(
-        static_cast<const chunk_t*>(in), nullptr, L.dst, L.s, L.k, rc, static_cast<chunk_t*>(y));
+    combine_kernel<DT, KMAX, false, 1><<<L.s, sp.wpb * kWave, 0, stream>>>(
+        static_cast<const chunk_t*>(in), nullptr, L.dst, L.s, L.k, sp, static_cast<chunk_t*>(y));
 }
 
 template <int DT>
-static void combine_dt(const LayoutView& L, const void* in, const float* w, int64_t rc, void* y,
-                       int grid, hipStream_t stream) {
+static void combine_dt(const LayoutView& L, const void* in, const float* w, const RowSplit& sp,
+                       void* y, hipStream_t stream) {
   switch (route_bound(L.k)) {
-    case 1: combine_k<DT, 1>(L, in, w, rc, y, grid, stream); break;
-    case 2: combine_k<DT, 2>(L, in, w, rc, y, grid, stream); break;
-    case 4: combine_k<DT, 4>(L, in, w, rc, y, grid, stream); break;
-    case 8: combine_k<DT, 8>(L, in, w, rc, y, grid, stream); break;
-    default: combine_k<DT, 16>(L, in, w, rc, y, grid, stream); break;
+    case 1: combine_k<DT, 1>(L, in, w, sp, y, stream); break;
+    case 2: combine_k<DT, 2>(L, in, w, sp, y, stream); break;
+    case 4: combine_k<DT, 4>(L, in, w, sp, y, stream); break;
+    case 8: combine_k<DT, 8>(L, in, w, sp, y, stream); break;
+    default: combine_k<DT, 16>(L, in, w, sp, y, stream); break;
   }
 }
 
 hipError_t launch_combine(const LayoutView& L, const void* in, const float* w, int64_t rc,
                           int dtype, void* y, hipStream_t stream) {
-  const int grid = row_grid(L, false);
-  if (grid == 0) return hipSuccess;
+  if (L.s == 0) return hipSuccess;
+  const RowSplit sp = make_split(rc, 1);
   switch (dtype) {
-    case kF32: combine_dt<kF32>(L, in, w, rc, y, grid, stream); break;
-    case kBF16: combine_dt<kBF16>(L, in, w, rc, y, grid, stream); break;
-    default: combine_dt<kF16>(L, in, w, rc, y, grid, stream); break;
+    case kF32: combine_dt<kF32>(L, in, w, sp, y, stream); break;
+    case kBF16: combine_dt<kBF16>(L, in, w, sp, y, stream); break;
+    default: combine_dt<kF16>(L, in, w, sp, y, stream); break;
   }
   return hipGetLastError();
 }
 
 template <int DT, int KMAX>
 static void combine_bwd_k(const LayoutView& L, const void* gy, const void* E, const float* w,
-                          int64_t rc, void* gE, float* gw, int grid, hipStream_t stream) {
-  combine_backward_kernel<DT, KMAX><<<grid, kBlock, 0, stream>>>(
-      static_cast<const chunk_t*>(gy), static_cast<const chunk_t*>(E), w, L.dst, L.s, L.k, rc,
+                          const RowSplit& sp, void* gE, float* gw, hipStream_t stream) {
+  const int grid = L.s + pad_blocks(L, sp.wpb);
+  if (grid == 0) return;
+  combine_backward_kernel<DT, KMAX, 1><<<grid, sp.wpb * kWave, 0, stream>>>(
+      static_cast<const chunk_t*>(gy), static_cast<const chunk_t*>(E), w, L.dst, L.s, L.k, sp,
       static_cast<chunk_t*>(gE), gw, L.capacity, L.e, static_cast<int32_t>(L.rows), L.kept,
       L.offsets);
 }
 
 template <int DT>
 static void combine_bwd_dt(const LayoutView& L, const void* gy, const void* E, const float* w,
-                           int64_t rc, void* gE, float* gw, int grid, hipStream_t stream) {
+                           const RowSplit& sp, void* gE, float* gw, hipStream_t stream) {
   switch (route_bound(L.k)) {
-    case 1: combine_bwd_k<DT, 1>(L, gy, E, w, rc, gE, gw, grid, stream); break;
-    case 2: combine_bwd_k<DT, 2>(L, gy, E, w, rc, gE, gw, grid, stream); break;
-    case 4: combine_bwd_k<DT, 4>(L, gy, E, w, rc, gE, gw, grid, stream); break;
-    case 8: combine_bwd_k<DT, 8>(L, gy, E, w, rc, gE, gw, grid, stream); break;
-    default: combine_bwd_k<DT, 16>(L, gy, E, w, rc, gE, gw, grid, stream); break;
+    case 1: combine_bwd_k<DT, 1>(L, gy, E, w, sp, gE, gw, stream); break;
+    case 2: combine_bwd_k<DT, 2>(L, gy, E, w, sp, gE, gw, stream); break;
+    case 4: combine_bwd_k<DT, 4>(L, gy, E, w, sp, gE, gw, stream); break;
+    case 8: combine_bwd_k<DT, 8>(L, gy, E, w, sp, gE, gw, stream); break;
+    default: combine_bwd_k<DT, 16>(L, gy, E, w, sp, gE, gw, stream); break;
   }
 }
 
 hipError_t launch_combine_backward(const LayoutView& L, const void* gy, const void* E,
                                    const float* w, int64_t rc, int dtype, void* gE, float* gw,
                                    hipStream_t stream) {
-  const int grid = row_grid(L, true);
-  if (grid == 0) return hipSuccess;
+  const RowSplit sp = make_split(rc, 1);
   switch (dtype) {
-    case kF32: combine_bwd_dt<kF32>(L, gy, E, w, rc, gE, gw, grid, stream); break;
-    case kBF16: combine_bwd_dt<kBF16>(L, gy, E, w, rc, gE, gw, grid, stream); break;
-    default: combine_bwd_dt<kF16>(L, gy, E, w, rc, gE, gw, grid, stream); break;
+    case kF32: combine_bwd_dt<kF32>(L, gy, E, w, sp, gE, gw, stream); break;
+    case kBF16: combine_bwd_dt<kBF16>(L, gy, E, w, sp, gE, gw, stream); break;
+    default: combine_bwd_dt<kF16>(L, gy, E, w, sp, gE, gw, stream); break;
   }
   return hipGetLastError();
 }

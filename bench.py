@@ -37,6 +37,34 @@ HBM_PEAK_GBPS = 8000.0
 OPS = ["gate", "layout", "dispatch", "combine", "replay", "combine_bwd", "dispatch_bwd", "gate_bwd"]
 
 
+def kernel_source_digest() -> str:
+    """sha256 over the HIP sources and build flags the library is compiled from."""
+    import hashlib
+    from combine_moe_gate_amd import _build
+    h = hashlib.sha256()
+    for path in sorted(_build.SOURCES + _build.HEADERS):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    h.update(" ".join(_build.FLAGS).encode())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str) -> dict:
+    """Counter-measured HBM bytes per launch from profiles/, if taken on these sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return {}
+    traffic, digest = {}, None
+    with open(path) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) == 3 and parts[0] == "traffic":
+                traffic[parts[1]] = int(parts[2])
+            elif len(parts) == 2 and parts[0] == "source_digest":
+                digest = parts[1]
+    return traffic if digest == kernel_source_digest() else {}
+
+
 def algorithmic_bytes(w: W.Workload, kept_routes: int) -> dict:
     """Bytes each call must move (zero padding counts: it is part of the output).
 
@@ -185,6 +213,9 @@ def main():
     ap.add_argument("--workload", default=W.HEADLINE, choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, run one plain device-to-device copy of MIB MiB "
+                         "(a known-size reference for hardware memory counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -193,6 +224,14 @@ def main():
 
     w = W.WORKLOADS[args.workload]
     elapsed, per_op, kept = run_gpu(w, args.steps, args.warmup)
+    if args.calibrate_copy > 0:
+        import torch
+        src = torch.ones(args.calibrate_copy << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     ms_per_step = elapsed / args.steps * 1e3
     abytes = algorithmic_bytes(w, kept)
     kernels = {}
@@ -230,7 +269,8 @@ def main():
                              "bytes": dc_bytes},
         "roofline": {"kernel": dominant, "bound": "hbm", "achieved": round(dom_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(w.name).get(dominant),
+                     "algorithmic_bytes": abytes[dominant]},
         "kernels": kernels,
         "kept_routes": kept,
     }

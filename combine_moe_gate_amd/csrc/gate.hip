@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kBlock) void gate_topk_kernel(const float* __restri
   const bool active = lane < k;
   const int expert = 0xffff - static_cast<int>(mine & 0xffffu);
   const float l = key_to_float(static_cast<uint32_t>(mine >> 16));
-  const float l0 = __shfl(l, 0, kWave);  // the largest selected logit
+  const float l0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, l)));
   const double ex = active ? exp(static_cast<double>(l) - static_cast<double>(l0)) : 0.0;
   const double denom = wave_sum(ex);
   if (active) {
@@ -91,9 +91,9 @@ __global__ __launch_bounds__(kBlock) void gate_topk_backward_kernel(
   for (int j = 0; j < 16; ++j) {
     sel[j] = -1;
     val[j] = 0.0;
-    if (j < k) {
-      sel[j] = __shfl(my_idx, j, kWave);
-      val[j] = __shfl(contrib, j, kWave);
+    if (j < k) {  // k is uniform: these are scalar reads of lane j
+      sel[j] = __builtin_amdgcn_readlane(my_idx, j);
+      val[j] = readlane_f64(contrib, j);
     }
   }
   float* out = gl + static_cast<size_t>(t) * e;

@@ -19,7 +19,7 @@ struct LayoutView {
   int32_t* route_idx;
   uint64_t* checksum;
   int32_t* flags;
-  int32_t* tile_counts;       // [ntiles, e] per-tile counts, then per-tile bases
+  int32_t* tile_counts;       // [ntiles, e] per-tile valid-route counts
   uint64_t* tile_checksum;    // [ntiles]
   int32_t* tile_flags;        // [ntiles]
 };

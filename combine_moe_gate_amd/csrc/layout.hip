@@ -5,20 +5,21 @@
 // (DeepSpeed PR "MoE dispatch: fix silent Tutel + TP corruption, speed up native and
 // Tutel paths", review comment on fast_cumsum_sub_one), i.e. the number of earlier
 // tokens that chose the same expert. It is computed without sorting and without any
-// order-dependent atomics, in three launches:
+// order-dependent atomics, in two launches over tiles of 256 tokens:
 //
-//   count  one workgroup per tile of 256 tokens: LDS histogram of the tile's valid
-//          routes (integer atomic adds; the totals do not depend on their order), the
-//          tile's share of the routing checksum and its flag bits.
-//   scan   one workgroup: for every expert an exclusive scan over tiles (in place: the
-//          tile counts become tile bases), the totals, kept = min(count, capacity), and
-//          an exclusive scan over experts of the segment sizes (the dropless offsets;
-//          with a capacity the segments are all `capacity` rows long).
-//   place  one workgroup per tile again: each wave builds, per expert, a 64-bit mask
-//          of its lanes (tokens) that chose it (LDS atomic OR: order-independent). The
-//          slot of a route is then tile base + popcounts of the earlier waves' masks +
-//          popcount of its own wave's mask below its lane. Writes dst, src and a copy
-//          of the routing; rows no route fills get src = -1.
+//   count  one workgroup per tile: LDS histogram of the tile's valid routes (integer
+//          atomic adds; the totals do not depend on their order), the tile's share of
+//          the routing checksum and its flag bits.
+//   place  one workgroup per tile again. Each workgroup first derives what it needs
+//          from the small, L2-resident tile tables: for every expert the sum over
+//          earlier tiles (its tile base) and over all tiles (the count), then an
+//          exclusive scan over experts of the segment sizes (the dropless offsets; with
+//          a capacity every segment is `capacity` rows). Workgroup 0 publishes counts,
+//          kept, offsets, checksum and flags. Then each wave builds, per expert, a
+//          64-bit mask of its lanes (tokens) that chose it (LDS atomic OR: order-
+//          independent); a route's slot is tile base + popcounts of the earlier waves'
+//          masks + popcount of its own wave's mask below its lane. It writes dst, src
+//          and a copy of the routing; rows no route fills get src = -1.
 #include "internal.h"
 #include "moe_device.h"
 
@@ -96,97 +97,126 @@ __global__ __launch_bounds__(kTileTokens) void layout_count_kernel(
   }
 }
 
-constexpr int kScanThreads = 1024;
-
-__global__ __launch_bounds__(kScanThreads) void layout_scan_kernel(
-    int e, int capacity, int ntiles, int32_t* __restrict__ tile_counts,
-    const uint64_t* __restrict__ tile_checksum, const int32_t* __restrict__ tile_flags,
-    int32_t* __restrict__ counts, int32_t* __restrict__ kept, int32_t* __restrict__ offsets,
-    uint64_t* __restrict__ checksum, int32_t* __restrict__ flags) {
-  __shared__ int32_t wave_total[kScanThreads / kWave];
-  __shared__ uint64_t wave_cks[kScanThreads / kWave];
-  __shared__ int32_t wave_flags[kScanThreads / kWave];
-  const int x = threadIdx.x;
+// Exclusive scan of one int per expert across the workgroup (e <= 1024 experts, each
+// thread owning up to four consecutive experts). Returns the total.
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t* __restrict__ vals, int e,
+                                                        int32_t* __restrict__ wave_tot) {
+  constexpr int kPer = 4;
   const int lane = lane_id(), wv = threadIdx.x >> 6;
-
-  // per expert: exclusive scan over tiles, in place
-  int32_t total = 0;
-  if (x < e) {
-    int32_t* col = tile_counts + x;
-    int b = 0;
-    for (; b + 4 <= ntiles; b += 4) {
-      const int32_t c0 = col[static_cast<size_t>(b) * e], c1 = col[static_cast<size_t>(b + 1) * e];
-      const int32_t c2 = col[static_cast<size_t>(b + 2) * e], c3 = col[static_cast<size_t>(b + 3) * e];
-      col[static_cast<size_t>(b) * e] = total;
-      col[static_cast<size_t>(b + 1) * e] = total + c0;
-      col[static_cast<size_t>(b + 2) * e] = total + c0 + c1;
-      col[static_cast<size_t>(b + 3) * e] = total + c0 + c1 + c2;
-      total += c0 + c1 + c2 + c3;
-    }
-    for (; b < ntiles; ++b) {
-      const int32_t c = col[static_cast<size_t>(b) * e];
-      col[static_cast<size_t>(b) * e] = total;
-      total += c;
-    }
-    counts[x] = total;
-    kept[x] = capacity > 0 ? (total < capacity ? total : capacity) : total;
+  const int first = threadIdx.x * kPer;
+  int32_t mine[kPer];
+  int32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    mine[i] = (first + i < e) ? vals[first + i] : 0;
+    sum += mine[i];
   }
-
-  // exclusive scan over experts of the segment sizes
-  int32_t seg = (x < e) ? (capacity > 0 ? capacity : total) : 0;
-  int32_t incl = seg;
+  int32_t incl = sum;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
     const int32_t y = __shfl_up(incl, o, kWave);
     if (lane >= o) incl += y;
   }
-  if (lane == kWave - 1) wave_total[wv] = incl;
-
-  // routing checksum and flags over tiles
-  uint64_t c = 0;
-  int f = 0;
-  for (int b = x; b < ntiles; b += kScanThreads) {
-    c += tile_checksum[b];
-    f |= tile_flags[b];
+  if (lane == kWave - 1) wave_tot[wv] = incl;
+  __syncthreads();
+  int32_t before = 0, total = 0;
+  for (int w = 0; w < kTileTokens / kWave; ++w) {
+    if (w < wv) before += wave_tot[w];
+    total += wave_tot[w];
   }
-  c = wave_sum(c);
-  f = wave_or(f);
-  if (lane == 0) {
-    wave_cks[wv] = c;
-    wave_flags[wv] = f;
+  int32_t run = before + incl - sum;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (first + i < e) vals[first + i] = run;
+    run += mine[i];
   }
   __syncthreads();
-
-  int32_t before = 0;
-  for (int w = 0; w < wv; ++w) before += wave_total[w];
-  if (x < e) {
-    offsets[x] = before + incl - seg;
-    if (x == e - 1) offsets[e] = before + incl;
-  }
-  if (x == 0) {
-    uint64_t cc = 0;
-    int ff = 0;
-    for (int w = 0; w < kScanThreads / kWave; ++w) {
-      cc += wave_cks[w];
-      ff |= wave_flags[w];
-    }
-    *checksum = cc;
-    *flags = ff;
-  }
+  return total;
 }
 
 template <int KMAX>
 __global__ __launch_bounds__(kTileTokens) void layout_place_kernel(
-    const int32_t* __restrict__ idx, int s, int e, int k, int capacity, int32_t rows,
-    const int32_t* __restrict__ tile_base, const int32_t* __restrict__ kept,
-    const int32_t* __restrict__ offsets, int32_t* __restrict__ dst, int32_t* __restrict__ src,
+    const int32_t* __restrict__ idx, int s, int e, int k, int capacity, int32_t rows, int ntiles,
+    const int32_t* __restrict__ tile_counts, const uint64_t* __restrict__ tile_checksum,
+    const int32_t* __restrict__ tile_flags, int32_t* __restrict__ counts,
+    int32_t* __restrict__ kept_out, int32_t* __restrict__ offsets_out, uint64_t* __restrict__ checksum,
+    int32_t* __restrict__ flags, int32_t* __restrict__ dst, int32_t* __restrict__ src,
     int32_t* __restrict__ route_idx) {
-  extern __shared__ unsigned long long lane_masks[];  // [waves per tile][e]
+  // LDS: per expert tile base, total and segment offset, then the per-wave lane masks
+  extern __shared__ unsigned long long lds[];
   constexpr int kWaves = kTileTokens / kWave;
+  __shared__ int32_t wave_tot[kWaves];
+  __shared__ uint64_t wave_cks[kWaves];
+  __shared__ int32_t wave_flg[kWaves];
+  unsigned long long* lane_masks = lds;                                   // [kWaves][e]
+  int32_t* base_s = reinterpret_cast<int32_t*>(lds + kWaves * e);          // [e]
+  int32_t* total_s = base_s + e;                                           // [e]
+  int32_t* off_s = total_s + e;                                            // [e + 1]
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   const int tile = blockIdx.x;
+  const int my_tile = tile < ntiles ? tile : ntiles;  // workgroups past the tiles: pad only
 
-  if (tile * kTileTokens < s) {  // uniform per workgroup
+  // per expert: sum over earlier tiles and over all tiles
+  for (int x = threadIdx.x; x < e; x += kTileTokens) {
+    int32_t before = 0, all = 0;
+    int b = 0;
+    for (; b + 4 <= ntiles; b += 4) {
+      const int32_t c0 = tile_counts[static_cast<size_t>(b) * e + x];
+      const int32_t c1 = tile_counts[static_cast<size_t>(b + 1) * e + x];
+      const int32_t c2 = tile_counts[static_cast<size_t>(b + 2) * e + x];
+      const int32_t c3 = tile_counts[static_cast<size_t>(b + 3) * e + x];
+      before += (b < my_tile ? c0 : 0) + (b + 1 < my_tile ? c1 : 0) + (b + 2 < my_tile ? c2 : 0) +
+                (b + 3 < my_tile ? c3 : 0);
+      all += c0 + c1 + c2 + c3;
+    }
+    for (; b < ntiles; ++b) {
+      const int32_t c = tile_counts[static_cast<size_t>(b) * e + x];
+      before += b < my_tile ? c : 0;
+      all += c;
+    }
+    base_s[x] = before;
+    total_s[x] = all;
+    off_s[x] = capacity > 0 ? capacity : all;  // segment sizes, scanned below
+  }
+  __syncthreads();
+  const int32_t seg_total = block_exclusive_scan(off_s, e, wave_tot);
+  if (threadIdx.x == 0) off_s[e] = seg_total;
+  __syncthreads();
+
+  if (tile == 0) {  // publish the layout's per-expert arrays, checksum and flags
+    for (int x = threadIdx.x; x < e; x += kTileTokens) {
+      const int32_t c = total_s[x];
+      counts[x] = c;
+      kept_out[x] = capacity > 0 ? (c < capacity ? c : capacity) : c;
+      offsets_out[x] = off_s[x];
+    }
+    if (threadIdx.x == 0) offsets_out[e] = off_s[e];
+    uint64_t cks = 0;
+    int f = 0;
+    for (int b = threadIdx.x; b < ntiles; b += kTileTokens) {
+      cks += tile_checksum[b];
+      f |= tile_flags[b];
+    }
+    cks = wave_sum(cks);
+    f = wave_or(f);
+    if (lane == 0) {
+      wave_cks[wv] = cks;
+      wave_flg[wv] = f;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint64_t c = 0;
+      int ff = 0;
+      for (int w = 0; w < kWaves; ++w) {
+        c += wave_cks[w];
+        ff |= wave_flg[w];
+      }
+      *checksum = c;
+      *flags = ff;
+    }
+  }
+
+  if (tile < ntiles) {  // uniform per workgroup
     for (int i = threadIdx.x; i < kWaves * e; i += kTileTokens) lane_masks[i] = 0ull;
     __syncthreads();
 
@@ -208,20 +238,19 @@ __global__ __launch_bounds__(kTileTokens) void layout_place_kernel(
 
     if (t < s) {
       const unsigned long long below = (1ull << lane) - 1ull;
-      const int32_t* base = tile_base + static_cast<size_t>(tile) * e;
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) {
         if (j < k) {
           int d = -1;
           if (ok[j]) {
             const int x = ids[j];
-            int r = base[x];
+            int r = base_s[x];
             for (int w = 0; w < wv; ++w) r += __popcll(lane_masks[w * e + x]);
             r += __popcll(lane_masks[wv * e + x] & below);
             if (capacity > 0)
               d = r < capacity ? x * capacity + r : -1;
             else
-              d = offsets[x] + r;
+              d = off_s[x] + r;
           }
           const size_t o = static_cast<size_t>(t) * k + j;
           dst[o] = d;
@@ -234,12 +263,13 @@ __global__ __launch_bounds__(kTileTokens) void layout_place_kernel(
 
   // rows no route fills: the tail of each capacity segment, or the dropless rows past
   // the last valid route
-  const int32_t begin = capacity > 0 ? 0 : offsets[e];
+  const int32_t begin = capacity > 0 ? 0 : off_s[e];
   const int32_t stride = gridDim.x * kTileTokens;
   for (int32_t r = begin + blockIdx.x * kTileTokens + threadIdx.x; r < rows; r += stride) {
     if (capacity > 0) {
       const int32_t x = r / capacity;
-      if (r - x * capacity >= kept[x]) src[r] = -1;
+      const int32_t c = total_s[x];
+      if (r - x * capacity >= (c < capacity ? c : capacity)) src[r] = -1;
     } else {
       src[r] = -1;
     }
@@ -253,9 +283,6 @@ static hipError_t launch_layout_k(const int32_t* idx, const LayoutView& L, hipSt
     layout_count_kernel<KMAX><<<ntiles, kTileTokens, L.e * sizeof(int32_t), stream>>>(
         idx, L.s, L.e, L.k, L.tile_counts, L.tile_checksum, L.tile_flags);
   }
-  layout_scan_kernel<<<1, kScanThreads, 0, stream>>>(L.e, L.capacity, ntiles, L.tile_counts,
-                                                     L.tile_checksum, L.tile_flags, L.counts,
-                                                     L.kept, L.offsets, L.checksum, L.flags);
   int grid = ntiles;
   if (L.capacity > 0) {
     const int64_t pad_blocks = (L.rows + kTileTokens - 1) / kTileTokens;
@@ -263,10 +290,12 @@ static hipError_t launch_layout_k(const int32_t* idx, const LayoutView& L, hipSt
     if (grid < want) grid = static_cast<int>(want);
   }
   if (grid < 1) grid = 1;
-  const size_t lds = static_cast<size_t>(kTileTokens / kWave) * L.e * sizeof(unsigned long long);
+  const size_t lds = static_cast<size_t>(kTileTokens / kWave) * L.e * sizeof(unsigned long long) +
+                     (3 * static_cast<size_t>(L.e) + 1) * sizeof(int32_t);
   layout_place_kernel<KMAX><<<grid, kTileTokens, lds, stream>>>(
-      idx, L.s, L.e, L.k, L.capacity, static_cast<int32_t>(L.rows), L.tile_counts, L.kept,
-      L.offsets, L.dst, L.src, L.route_idx);
+      idx, L.s, L.e, L.k, L.capacity, static_cast<int32_t>(L.rows), ntiles, L.tile_counts,
+      L.tile_checksum, L.tile_flags, L.counts, L.kept, L.offsets, L.checksum, L.flags, L.dst,
+      L.src, L.route_idx);
   return hipGetLastError();
 }
 

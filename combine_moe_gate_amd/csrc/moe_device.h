@@ -35,10 +35,13 @@ __device__ __forceinline__ int wave_in_block() {
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float a) {
-  uint32_t u = __float_as_uint(a);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;  // NaN
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+// Two float32 values to a packed pair of bfloat16, round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950 (low half = a, high half = b).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
@@ -78,10 +81,10 @@ __device__ __forceinline__ chunk_t pack(const float (&f)[ChunkElems<DT>::value])
     v.x = __float_as_uint(f[0]); v.y = __float_as_uint(f[1]);
     v.z = __float_as_uint(f[2]); v.w = __float_as_uint(f[3]);
   } else if constexpr (DT == kBF16) {
-    v.x = f32_to_bf16_rne(f[0]) | (f32_to_bf16_rne(f[1]) << 16);
-    v.y = f32_to_bf16_rne(f[2]) | (f32_to_bf16_rne(f[3]) << 16);
-    v.z = f32_to_bf16_rne(f[4]) | (f32_to_bf16_rne(f[5]) << 16);
-    v.w = f32_to_bf16_rne(f[6]) | (f32_to_bf16_rne(f[7]) << 16);
+    v.x = f32x2_to_bf16x2_rne(f[0], f[1]);
+    v.y = f32x2_to_bf16x2_rne(f[2], f[3]);
+    v.z = f32x2_to_bf16x2_rne(f[4], f[5]);
+    v.w = f32x2_to_bf16x2_rne(f[6], f[7]);
   } else {
     v.x = f32_to_f16_rne(f[0]) | (f32_to_f16_rne(f[1]) << 16);
     v.y = f32_to_f16_rne(f[2]) | (f32_to_f16_rne(f[3]) << 16);
@@ -94,31 +97,63 @@ __device__ __forceinline__ chunk_t pack(const float (&f)[ChunkElems<DT>::value])
 // ---------------------------------------------------------------------------------
 // wave64 reductions (butterfly over lane xor masks; every lane gets the result)
 
+// 64-bit value of the lane that a DPP control names (all lanes must be active).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_move64(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v)), CTRL,
+                                             0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v >> 32)),
+                                             CTRL, 0xf, 0xf, false);
+  return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), lane);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Wave-wide reductions, returned uniformly to every lane. Inside each row of 16 lanes:
+// combine with the neighbour (quad_perm 1,0,3,2), the other pair (quad_perm 2,3,0,1),
+// the mirrored half-row and the mirrored row, after which every lane of a row holds
+// the row's result; the four rows are then combined from readlane values in the
+// fixed order (r0 op r1) op (r2 op r3). All lanes must be active. No LDS traffic.
+template <class T, class Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  static_assert(sizeof(T) == 8, "64-bit values");
+  auto bits = [](T x) { return __builtin_bit_cast(uint64_t, x); };
+  auto val = [](uint64_t u) { return __builtin_bit_cast(T, u); };
+  v = op(v, val(dpp_move64<0xb1>(bits(v))));   // quad_perm [1,0,3,2]
+  v = op(v, val(dpp_move64<0x4e>(bits(v))));   // quad_perm [2,3,0,1]
+  v = op(v, val(dpp_move64<0x141>(bits(v))));  // row_half_mirror
+  v = op(v, val(dpp_move64<0x140>(bits(v))));  // row_mirror
+  const T a = val(readlane64(bits(v), 0)), b = val(readlane64(bits(v), 16));
+  const T c = val(readlane64(bits(v), 32)), d = val(readlane64(bits(v), 48));
+  return op(op(a, b), op(c, d));
+}
+
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_reduce(v, [](double a, double b) { return a + b; });
 }
 
 __device__ __forceinline__ uint64_t wave_sum(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_reduce(v, [](uint64_t a, uint64_t b) { return a + b; });
 }
 
 __device__ __forceinline__ int wave_or(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, kWave);
-  return v;
+  const uint64_t r = wave_reduce(static_cast<uint64_t>(static_cast<uint32_t>(v)),
+                                 [](uint64_t a, uint64_t b) { return a | b; });
+  return static_cast<int>(r);
 }
 
+// Maximum over the 64 lanes, returned uniformly.
 __device__ __forceinline__ uint64_t wave_max(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint64_t w = __shfl_xor(v, o, kWave);
-    v = w > v ? w : v;
-  }
-  return v;
+  return wave_reduce(v, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  return __builtin_bit_cast(double, readlane64(u, lane));
 }
 
 }  // namespace moe

@@ -21,7 +21,8 @@
 //                     review thread on combine weights: the weights are applied).
 //   dispatch backward the same kernel without weights (the gradient of a dispatch is
 //                     a combine, PR 8213 first commit).
-//   combine backward  grad_y[t] read once; each route gets the weighted copy in its row
+//   combine backward  grad_y[t] read once (normal loads, like x in dispatch: measured
+//                     faster than nontemporal ones); each route gets the weighted copy in its row
 //                     and the dot product with its expert row accumulates in float64,
 //                     per wave, then across the workgroup's waves through LDS in a
 //                     fixed order (the gradient of a combine is a dispatch, plus the
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(kBlock) void combine_backward_kernel(
       const int64_t c = c0 + u * kWave;
       if (c < sp.rc) {
         float g[N];
-        unpack<DT>(load_chunk<true>(gr + c), g);
+        unpack<DT>(load_chunk<false>(gr + c), g);  // measured faster than a nontemporal load
         chunk_t v[KMAX];
 #pragma unroll
         for (int j = 0; j < KMAX; ++j)

@@ -409,3 +409,59 @@ def test_all_routes_dropped_give_zero_rows():
 
 def bits(a):
     return np.ascontiguousarray(a).view(np.uint32)
+
+
+def test_whole_step_replays_correctly_from_a_hip_graph():
+    """The path has no memsets, allocations or host syncs: it can be captured. Each
+    replay (with eager work in between) must equal the eager result."""
+    announce("hip graph")
+    s, m, e, k, cap = 2000, 264, 40, 4, 0
+    inp = W.random_case(61, s, m, e, k, cap, "bf16")
+    logits = to_dev(inp.logits)
+    x = to_dev(inp.x, "bf16")
+    gy = to_dev(inp.grad_y, "bf16")
+    ws = torch.empty(M.workspace_bytes(s, e, k, cap), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((s, k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((s, k), dtype=torch.float32, device="cuda")
+    rows = s * k
+    buf = torch.empty((rows, m), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((s, m), dtype=torch.bfloat16, device="cuda")
+    gE = torch.empty_like(buf)
+    gw = torch.empty_like(wt)
+    gx = torch.empty_like(y)
+    gl = torch.empty((s, e), dtype=torch.float32, device="cuda")
+
+    def step():
+        M.moe_gate_topk(logits, k, idx_out=idx, w_out=wt)
+        L = M.moe_dispatch_layout(idx, e, cap, workspace=ws)
+        M.moe_dispatch(L, x, out=buf)
+        M.moe_combine(L, buf, wt, out=y)
+        M.moe_combine_backward(L, gy, buf, wt, grad_expert_out=gE, grad_w=gw)
+        M.moe_dispatch_backward(L, gE, out=gx)
+        M.moe_gate_topk_backward(idx, wt, gw, e, out=gl)
+
+    outs = (idx, wt, buf, y, gE, gw, gx, gl)
+    step()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, eager):
+            assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.uint8) if b.dtype == torch.bfloat16 else b), f"replay {rep}"
+        # eager work between replays
+        M.moe_gate_topk(logits.flip(0), k)
+        torch.cuda.synchronize()

@@ -38,6 +38,10 @@ from .moe import (  # noqa: F401
     dispatch_backward,
     dispatch_layout,
     dispatch_replay,
+    dispatch_weighted,
+    dispatch_weighted_backward,
+    renormalize_kept,
+    renormalize_kept_backward,
     gate_topk,
     gate_topk_backward,
     gate_weights_f64,

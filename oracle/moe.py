@@ -197,7 +197,8 @@ def route_validity(idx: np.ndarray, e: int) -> tuple[np.ndarray, int]:
     return in_range & ~dup, flags
 
 
-def dispatch_layout(idx: np.ndarray, e: int, capacity: int) -> Layout:
+def dispatch_layout(idx: np.ndarray, e: int, capacity: int, route_major: bool = False,
+                    pad_multiple: int = 1) -> Layout:
     """Per-expert counts, token-order slots, capacity drop and the row maps.
 
     [DS-8195] review comment on fast_cumsum_sub_one: a route's slot in its
@@ -208,20 +209,43 @@ def dispatch_layout(idx: np.ndarray, e: int, capacity: int) -> Layout:
     trimming rows by the prefix sum: without a capacity the buffer holds the
     s*k routes grouped by expert, each expert's segment starting at the
     exclusive prefix sum of the per-expert counts.
+
+    route_major: slots are handed to every token's first route, then every
+    token's second route, and so on (the per-route masks mask1, mask2, ... of
+    the same review comment, each cumsum offset by the counts of the earlier
+    routes: first choices win capacity before second choices).
+    pad_multiple (dropless only): each expert's segment is rounded up to a
+    multiple of rows, as a grouped GEMM with fixed row tiles wants; the buffer
+    then has s*k + e*(pad_multiple-1) rows and the unused ones are padding
+    (NeMo Automodel PR on layout reuse, section 1: a pad multiple fixed at
+    construction).
     """
     idx = np.ascontiguousarray(idx, dtype=np.int32)
     s, k = idx.shape
+    if pad_multiple < 1 or (pad_multiple > 1 and capacity > 0):
+        raise ValueError("pad_multiple must be >= 1, and 1 with a capacity")
     valid, flags = route_validity(idx, e)
     tt, jj = np.nonzero(valid)
     xx = idx[tt, jj].astype(np.int64)
 
-    mask = np.zeros((s, e), dtype=np.int64)
-    mask[tt, xx] = 1
-    locations = np.cumsum(mask, axis=0) - 1  # cumsum-minus-one, token order
-    counts = mask.sum(axis=0).astype(np.int64)
-
     slot = np.full((s, k), -1, dtype=np.int64)
-    slot[tt, jj] = locations[tt, xx]
+    if not route_major:
+        mask = np.zeros((s, e), dtype=np.int64)
+        mask[tt, xx] = 1
+        locations = np.cumsum(mask, axis=0) - 1  # cumsum-minus-one, token order
+        slot[tt, jj] = locations[tt, xx]
+        counts = mask.sum(axis=0).astype(np.int64)
+    else:
+        earlier = np.zeros(e, dtype=np.int64)  # routes of earlier columns per expert
+        for j in range(k):
+            sel = valid[:, j]
+            mask_j = np.zeros((s, e), dtype=np.int64)
+            mask_j[np.nonzero(sel)[0], idx[sel, j].astype(np.int64)] = 1
+            loc_j = np.cumsum(mask_j, axis=0) - 1 + earlier[None, :]
+            rows_j = np.nonzero(sel)[0]
+            slot[rows_j, j] = loc_j[rows_j, idx[sel, j].astype(np.int64)]
+            earlier += mask_j.sum(axis=0)
+        counts = earlier
 
     dst = np.full((s, k), -1, dtype=np.int64)
     if capacity > 0:
@@ -231,8 +255,9 @@ def dispatch_layout(idx: np.ndarray, e: int, capacity: int) -> Layout:
         kept = np.minimum(counts, capacity)
         offsets = np.arange(e + 1, dtype=np.int64) * capacity
     else:
-        rows = s * k
-        offsets = np.concatenate([[0], np.cumsum(counts)])
+        rows = s * k + e * (pad_multiple - 1)
+        seg = -(-counts // pad_multiple) * pad_multiple
+        offsets = np.concatenate([[0], np.cumsum(seg)])
         dst[tt, jj] = offsets[xx] + slot[tt, jj]
         kept = counts.copy()
 
@@ -345,3 +370,75 @@ def dispatch_backward(layout: Layout, grad_out: np.ndarray, dtype: str) -> np.nd
     """
     acc = _route_sum(layout, to_f32(grad_out, dtype), None)
     return from_f32(acc, dtype)
+
+
+# ----------------------------------------------------------------------------
+# variants: weights applied at dispatch, renormalisation over kept routes
+
+
+def dispatch_weighted(layout: Layout, x: np.ndarray, w: np.ndarray, dtype: str) -> np.ndarray:
+    """Dispatch with the routing weight applied to each copy (weights before the experts).
+
+    [DS-8213] review thread on combine weights and the commit that applies them:
+    the weights are applied either before or after the expert MLP (score_apply).
+    Before: out[dst[t,j]] = w[t,j] * x[t], a float32 product rounded to the
+    element type; the combine that follows is then unweighted.
+    """
+    out = zeros((layout.rows,) + x.shape[1:], dtype)
+    x32 = to_f32(x, dtype)
+    w32 = np.asarray(w, np.float32)
+    for j in range(layout.k):
+        sel = layout.dst[:, j] >= 0
+        out[layout.dst[sel, j]] = from_f32(w32[sel, j][:, None] * x32[sel], dtype)
+    return out
+
+
+def dispatch_weighted_backward(layout: Layout, grad_out: np.ndarray, x: np.ndarray,
+                               w: np.ndarray, dtype: str) -> tuple[np.ndarray, np.ndarray]:
+    """Gradients of the weighted dispatch: a weighted combine, and the weight gradient.
+
+    grad_x[t] = sum over placed routes j, in order, of w[t,j] * grad_out[dst[t,j]]
+    (float32, separate multiply and add, rounded once); grad_w[t,j] =
+    <grad_out[dst[t,j]], x[t]> in float64, rounded once (0 for a dropped route).
+    """
+    s, k = layout.s, layout.k
+    g32 = to_f32(grad_out, dtype)
+    gx = from_f32(_route_sum(layout, g32, w), dtype)
+    x32 = to_f32(x, dtype)
+    gw = np.zeros((s, k), np.float32)
+    for j in range(k):
+        sel = layout.dst[:, j] >= 0
+        dots = (x32[sel].astype(np.float64) * g32[layout.dst[sel, j]].astype(np.float64)).sum(axis=1)
+        gw[sel, j] = dots.astype(np.float32)
+    return gx, gw
+
+
+def renormalize_kept(layout: Layout, w: np.ndarray) -> np.ndarray:
+    """Weights renormalised over each token's kept routes after the capacity drop.
+
+    w'[t,j] = w[t,j] / S_t for kept routes, S_t = sum of the token's kept weights
+    (float64 in route order); 0 for dropped routes, and 0 everywhere if none is
+    kept. Rounded once to float32. (The alternative reading of where the
+    renormalisation sits relative to the drop.)
+    """
+    w64 = np.asarray(w, np.float32).astype(np.float64)
+    kept = layout.dst >= 0
+    S = np.where(kept, w64, 0.0).sum(axis=1, keepdims=True)
+    safe = np.where(S != 0, S, 1.0)
+    return np.where(kept & (S != 0), w64 / safe, 0.0).astype(np.float32)
+
+
+def renormalize_kept_backward(layout: Layout, w: np.ndarray, grad_out: np.ndarray) -> np.ndarray:
+    """Gradient of renormalize_kept with respect to the original weights.
+
+    With u_j = w_j / S over kept routes: grad_w_i = (g_i - sum_q u_q g_q) / S for
+    kept i, and 0 for dropped i (float64, rounded once).
+    """
+    w64 = np.asarray(w, np.float32).astype(np.float64)
+    g64 = np.asarray(grad_out, np.float32).astype(np.float64)
+    kept = layout.dst >= 0
+    S = np.where(kept, w64, 0.0).sum(axis=1, keepdims=True)
+    safe = np.where(S != 0, S, 1.0)
+    u = np.where(kept, w64 / safe, 0.0)
+    dot = np.where(kept, u * g64, 0.0).sum(axis=1, keepdims=True)
+    return np.where(kept & (S != 0), (g64 - dot) / safe, 0.0).astype(np.float32)

@@ -11,11 +11,12 @@ import pytest
 import oracle
 from oracle import moe
 from tests import test_oracle_pins as pins
+from tests import test_oracle_variants as vpins
 
 
-def _route_major_layout(idx, e, capacity):
+def _route_major_layout(idx, e, capacity, route_major=False, pad_multiple=1):
     # slots handed out to every token's first route, then every second route, ...
-    L = moe.dispatch_layout(idx, e, capacity)
+    L = moe.dispatch_layout(idx, e, capacity, route_major, pad_multiple)
     s, k = idx.shape
     seen = np.zeros(e, np.int64)
     dst = -np.ones((s, k), np.int64)
@@ -34,8 +35,8 @@ def _route_major_layout(idx, e, capacity):
     return L
 
 
-def _slot_off_by_one(idx, e, capacity):
-    L = moe.dispatch_layout(idx, e, capacity)
+def _slot_off_by_one(idx, e, capacity, route_major=False, pad_multiple=1):
+    L = moe.dispatch_layout(idx, e, capacity, route_major, pad_multiple)
     dst = L.dst.copy()
     dst[dst >= 0] += 1
     dst[dst >= L.rows] = -1
@@ -101,7 +102,40 @@ def _bf16_truncates(a32, dtype):
     return (u >> np.uint32(16)).astype(np.uint16)
 
 
+def _layout_ignores_route_major(idx, e, capacity, route_major=False, pad_multiple=1):
+    return moe.dispatch_layout(idx, e, capacity, False, pad_multiple)
+
+
+def _layout_ignores_padding(idx, e, capacity, route_major=False, pad_multiple=1):
+    L = moe.dispatch_layout(idx, e, capacity, route_major, 1)
+    if pad_multiple > 1:
+        L.rows = L.rows + e * (pad_multiple - 1)
+        L.src = np.concatenate([L.src, -np.ones(e * (pad_multiple - 1), np.int32)])
+    return L
+
+
+def _weighted_dispatch_unweighted(layout, x, w, dtype):
+    return moe.dispatch_weighted(layout, x, np.ones_like(np.asarray(w, np.float32)), dtype)
+
+
+def _renorm_over_all_routes(layout, w):
+    w64 = np.asarray(w, np.float32).astype(np.float64)
+    return (w64 / w64.sum(axis=1, keepdims=True)).astype(np.float32) * (layout.dst >= 0)
+
+
+def _renorm_backward_no_centering(layout, w, g):
+    w64 = np.asarray(w, np.float32).astype(np.float64)
+    kept = layout.dst >= 0
+    S = np.where(kept, w64, 0.0).sum(axis=1, keepdims=True)
+    return np.where(kept & (S != 0), np.asarray(g, np.float64) / np.where(S != 0, S, 1), 0).astype(np.float32)
+
+
 MUTATIONS = {
+    "ignores_route_major": ("dispatch_layout", _layout_ignores_route_major),
+    "ignores_padding": ("dispatch_layout", _layout_ignores_padding),
+    "weighted_dispatch_unweighted": ("dispatch_weighted", _weighted_dispatch_unweighted),
+    "renorm_over_all_routes": ("renormalize_kept", _renorm_over_all_routes),
+    "renorm_backward_no_centering": ("renormalize_kept_backward", _renorm_backward_no_centering),
     "route_major_slots": ("dispatch_layout", _route_major_layout),
     "slot_off_by_one": ("dispatch_layout", _slot_off_by_one),
     "combine_drops_last_route": ("combine", _combine_drops_last_route),
@@ -127,6 +161,12 @@ PINS = [
     pins.test_weight_gradient_matches_finite_difference_of_dense_combine,
     pins.test_identity_expert_closed_forms,
     pins.test_bf16_rounding_brute_force,
+    lambda: vpins.test_layout_options_match_brute_force(),
+    vpins.test_route_major_gives_first_choices_priority,
+    lambda: vpins.test_weighted_dispatch_matches_dense_einsum(5),
+    lambda: vpins.test_weighted_dispatch_backward_adjoint_and_finite_difference(4),
+    vpins.test_renormalized_gate_weights_are_softmax_over_kept_logits,
+    vpins.test_renormalize_backward_matches_finite_differences_through_the_gate,
 ]
 
 

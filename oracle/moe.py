@@ -419,13 +419,21 @@ def renormalize_kept(layout: Layout, w: np.ndarray) -> np.ndarray:
     w'[t,j] = w[t,j] / S_t for kept routes, S_t = sum of the token's kept weights
     (float64 in route order); 0 for dropped routes, and 0 everywhere if none is
     kept. Rounded once to float32. (The alternative reading of where the
-    renormalisation sits relative to the drop.)
+    renormalisation sits relative to the drop.) Sums run in route order.
     """
     w64 = np.asarray(w, np.float32).astype(np.float64)
     kept = layout.dst >= 0
-    S = np.where(kept, w64, 0.0).sum(axis=1, keepdims=True)
+    S = _route_order_sum(np.where(kept, w64, 0.0))
     safe = np.where(S != 0, S, 1.0)
     return np.where(kept & (S != 0), w64 / safe, 0.0).astype(np.float32)
+
+
+def _route_order_sum(a64: np.ndarray) -> np.ndarray:
+    """Row sums in float64, adding the k columns in route order j = 0..k-1."""
+    acc = np.zeros((a64.shape[0], 1), np.float64)
+    for j in range(a64.shape[1]):
+        acc[:, 0] = acc[:, 0] + a64[:, j]
+    return acc
 
 
 def renormalize_kept_backward(layout: Layout, w: np.ndarray, grad_out: np.ndarray) -> np.ndarray:
@@ -437,8 +445,8 @@ def renormalize_kept_backward(layout: Layout, w: np.ndarray, grad_out: np.ndarra
     w64 = np.asarray(w, np.float32).astype(np.float64)
     g64 = np.asarray(grad_out, np.float32).astype(np.float64)
     kept = layout.dst >= 0
-    S = np.where(kept, w64, 0.0).sum(axis=1, keepdims=True)
+    S = _route_order_sum(np.where(kept, w64, 0.0))
     safe = np.where(S != 0, S, 1.0)
     u = np.where(kept, w64 / safe, 0.0)
-    dot = np.where(kept, u * g64, 0.0).sum(axis=1, keepdims=True)
+    dot = _route_order_sum(np.where(kept, u * g64, 0.0))
     return np.where(kept & (S != 0), (g64 - dot) / safe, 0.0).astype(np.float32)

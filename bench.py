@@ -34,7 +34,10 @@ import workloads as W  # noqa: E402
 
 METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (s=8192,m=4096,e=128,k=8)"
 HBM_PEAK_GBPS = 8000.0
-OPS = ["gate", "layout", "dispatch", "combine", "replay", "combine_bwd", "dispatch_bwd", "gate_bwd"]
+# The same step with one of the variants: route-major capacity priority, dropless
+# segments padded to 128 rows, weights applied at dispatch (before the experts), or
+# weights renormalised over the kept routes after the capacity drop.
+VARIANTS = ("route_major", "pad128", "weights_before", "renorm_kept")
 
 
 def kernel_source_digest() -> str:
@@ -65,16 +68,17 @@ def measured_traffic(workload: str) -> dict:
     return traffic if digest == kernel_source_digest() else {}
 
 
-def algorithmic_bytes(w: W.Workload, kept_routes: int) -> dict:
+def algorithmic_bytes(w: W.Workload, kept_routes: int, rows: int | None = None,
+                      variant: str | None = None) -> dict:
     """Bytes each call must move (zero padding counts: it is part of the output).
 
     b = element size; K = placed routes. Routing metadata is int32/float32.
     """
     s, m, e, k, b = w.s, w.m, w.e, w.k, W.ELEM_BYTES[w.dtype]
-    rows = w.rows
+    rows = w.rows if rows is None else rows
     K = kept_routes
     row = m * b
-    return {
+    out = {
         "gate": s * e * 4 + s * k * 8,
         # count + place read the ids twice; dst, route copy, src written; tile tables
         "layout": 2 * s * k * 4 + 2 * s * k * 4 + rows * 4,
@@ -85,7 +89,18 @@ def algorithmic_bytes(w: W.Workload, kept_routes: int) -> dict:
         "combine_bwd": s * row + K * row + rows * row + s * k * 12,
         "dispatch_bwd": K * row + s * k * 4 + s * row,
         "gate_bwd": s * k * 12 + s * e * 4,
+        "renorm": s * k * 12,
+        "renorm_bwd": s * k * 16,
     }
+    if variant == "weights_before":
+        # dispatch and replay read the weights; the combine is unweighted; the combine
+        # backward is a plain dispatch of grad_y; the dispatch backward also reads x
+        out["dispatch"] = s * row + rows * row + s * k * 8
+        out["replay"] = out["dispatch"]
+        out["combine"] = K * row + s * k * 4 + s * row
+        out["combine_bwd"] = s * row + rows * row + s * k * 4
+        out["dispatch_bwd"] = K * row + s * row + s * row + s * k * 12
+    return out
 
 
 def to_dev(a, dtype, dev):
@@ -95,7 +110,7 @@ def to_dev(a, dtype, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def run_gpu(w: W.Workload, steps: int, warmup: int):
+def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None):
     import torch
 
     import combine_moe_gate_amd as M
@@ -110,10 +125,13 @@ def run_gpu(w: W.Workload, steps: int, warmup: int):
     x = to_dev(inp.x, w.dtype, dev)
     gy = to_dev(inp.grad_y, w.dtype, dev)
     tdt = x.dtype
-    s, k, e, m, rows = w.s, w.k, w.e, w.m, w.rows
+    s, k, e, m, cap = w.s, w.k, w.e, w.m, w.capacity
+    opts = dict(route_major=variant == "route_major", pad_multiple=128 if variant == "pad128" else 1)
     idx = torch.empty((s, k), dtype=torch.int32, device=dev)
     wt = torch.empty((s, k), dtype=torch.float32, device=dev)
-    ws = torch.empty(M.workspace_bytes(s, e, k, w.capacity), dtype=torch.uint8, device=dev)
+    ws = torch.empty(M.workspace_bytes(s, e, k, cap, **opts), dtype=torch.uint8, device=dev)
+    M.moe_gate_topk(logits, k, idx_out=idx, w_out=wt)
+    rows = M.moe_dispatch_layout(idx, e, cap, workspace=ws, **opts).rows  # host-known
     buf = torch.empty((rows, m), dtype=tdt, device=dev)
     rep = torch.empty((rows, m), dtype=tdt, device=dev)
     y = torch.empty((s, m), dtype=tdt, device=dev)
@@ -121,53 +139,91 @@ def run_gpu(w: W.Workload, steps: int, warmup: int):
     gw = torch.empty((s, k), dtype=torch.float32, device=dev)
     gx = torch.empty((s, m), dtype=tdt, device=dev)
     gl = torch.empty((s, e), dtype=torch.float32, device=dev)
+    wr = torch.empty_like(wt)
+    gwr = torch.empty_like(gw)
+    st = {}
+
+    def gate():
+        M.moe_gate_topk(logits, k, idx_out=idx, w_out=wt)
+
+    def layout():
+        st["L"] = M.moe_dispatch_layout(idx, e, cap, workspace=ws, **opts)
+
+    def gate_bwd():
+        M.moe_gate_topk_backward(idx, wt, gw, e, out=gl)
+
+    if variant == "weights_before":
+        ops = [
+            ("gate", gate), ("layout", layout),
+            ("dispatch", lambda: M.moe_dispatch_weighted(st["L"], x, wt, out=buf)),
+            ("combine", lambda: M.moe_combine(st["L"], buf, None, out=y)),
+            ("replay", lambda: M.moe_dispatch_weighted(st["L"], x, wt, out=rep)),
+            # the gradient of an unweighted combine is a plain dispatch of grad_y
+            ("combine_bwd", lambda: M.moe_dispatch(st["L"], gy, out=gE)),
+            ("dispatch_bwd", lambda: M.moe_dispatch_weighted_backward(st["L"], gE, x, wt, grad_x=gx,
+                                                                      grad_w=gw)),
+            ("gate_bwd", gate_bwd),
+        ]
+    elif variant == "renorm_kept":
+        ops = [
+            ("gate", gate), ("layout", layout),
+            ("renorm", lambda: M.moe_renormalize_kept(st["L"], wt, out=wr)),
+            ("dispatch", lambda: M.moe_dispatch(st["L"], x, out=buf)),
+            ("combine", lambda: M.moe_combine(st["L"], buf, wr, out=y)),
+            ("replay", lambda: M.moe_dispatch_replay(st["L"], x, idx, out=rep)),
+            ("combine_bwd", lambda: M.moe_combine_backward(st["L"], gy, rep, wr, grad_expert_out=gE,
+                                                           grad_w=gwr)),
+            ("renorm_bwd", lambda: M.moe_renormalize_kept_backward(st["L"], wt, gwr, out=gw)),
+            ("dispatch_bwd", lambda: M.moe_dispatch_backward(st["L"], gE, out=gx)),
+            ("gate_bwd", gate_bwd),
+        ]
+    else:
+        ops = [
+            ("gate", gate), ("layout", layout),
+            ("dispatch", lambda: M.moe_dispatch(st["L"], x, out=buf)),
+            ("combine", lambda: M.moe_combine(st["L"], buf, wt, out=y)),
+            # checkpoint recompute: the dispatch replayed from the saved layout
+            ("replay", lambda: M.moe_dispatch_replay(st["L"], x, idx, out=rep)),
+            ("combine_bwd", lambda: M.moe_combine_backward(st["L"], gy, rep, wt, grad_expert_out=gE,
+                                                           grad_w=gw)),
+            ("dispatch_bwd", lambda: M.moe_dispatch_backward(st["L"], gE, out=gx)),
+            ("gate_bwd", gate_bwd),
+        ]
+    names = [n for n, _ in ops]
 
     def step(ev=None):
-        def mark(i):
+        for i, (_, fn) in enumerate(ops):
             if ev is not None:
                 ev[i].record()
-        mark(0)
-        M.moe_gate_topk(logits, k, idx_out=idx, w_out=wt)
-        mark(1)
-        L = M.moe_dispatch_layout(idx, e, w.capacity, workspace=ws)
-        mark(2)
-        M.moe_dispatch(L, x, out=buf)
-        mark(3)
-        M.moe_combine(L, buf, wt, out=y)
-        mark(4)
-        M.moe_dispatch_replay(L, x, idx, out=rep)  # checkpoint recompute from the saved layout
-        mark(5)
-        M.moe_combine_backward(L, gy, rep, wt, grad_expert_out=gE, grad_w=gw)
-        mark(6)
-        M.moe_dispatch_backward(L, gE, out=gx)
-        mark(7)
-        M.moe_gate_topk_backward(idx, wt, gw, e, out=gl)
-        mark(8)
-        return L
+            fn()
+        if ev is not None:
+            ev[len(ops)].record()
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(OPS) + 1)] for _ in range(steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        L = step(events[i])
+        step(events[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    per_op = {op: [] for op in OPS}
+    per_op = {op: [] for op in names}
     for ev in events:
-        for j, op in enumerate(OPS):
+        for j, op in enumerate(names):
             per_op[op].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)  # microseconds
+    L = st["L"]
     kept = int(L.kept.sum().item())
     flags, _ = M.moe_layout_read(L)
     if flags != 0:
         raise RuntimeError(f"layout flags {flags} on a valid workload")
-    return elapsed, per_op, kept
+    return elapsed, per_op, kept, rows
 
 
-def run_cpu_baseline(w: W.Workload, target_s: float = 12.0, sample_tokens: int = 1024):
+def run_cpu_baseline(w: W.Workload, target_s: float = 12.0, sample_tokens: int = 1024,
+                     variant: str | None = None):
     """The oracle, as it stands, over the first `sample_tokens` tokens of the workload."""
     import oracle
 
@@ -181,14 +237,25 @@ def run_cpu_baseline(w: W.Workload, target_s: float = 12.0, sample_tokens: int =
         cap = max(1, -(-cap * n // w.s))
     reps = 0
     t0 = time.perf_counter()
+    opts = dict(route_major=variant == "route_major", pad_multiple=128 if variant == "pad128" else 1)
     while True:
         idx, wt = oracle.gate_topk(logits, w.k)
-        L = oracle.dispatch_layout(idx, w.e, cap)
-        E = oracle.dispatch(L, x)
-        oracle.combine(L, E, wt, w.dtype)
-        E2, _ = oracle.dispatch_replay(L, x, idx)
-        gE, gw = oracle.combine_backward(L, gy, E2, wt, w.dtype)
-        oracle.dispatch_backward(L, gE, w.dtype)
+        L = oracle.dispatch_layout(idx, w.e, cap, **opts)
+        if variant == "weights_before":
+            E = oracle.dispatch_weighted(L, x, wt, w.dtype)
+            oracle.dispatch_backward(L, E, w.dtype)  # the unweighted combine
+            oracle.dispatch_weighted(L, x, wt, w.dtype)  # replay
+            gE = oracle.dispatch(L, gy)
+            _, gw = oracle.dispatch_weighted_backward(L, gE, x, wt, w.dtype)
+        else:
+            wc = oracle.renormalize_kept(L, wt) if variant == "renorm_kept" else wt
+            E = oracle.dispatch(L, x)
+            oracle.combine(L, E, wc, w.dtype)
+            E2, _ = oracle.dispatch_replay(L, x, idx)
+            gE, gw = oracle.combine_backward(L, gy, E2, wc, w.dtype)
+            if variant == "renorm_kept":
+                gw = oracle.renormalize_kept_backward(L, wt, gw)
+            oracle.dispatch_backward(L, gE, w.dtype)
         oracle.gate_topk_backward(idx, wt, gw, w.e)
         reps += 1
         el = time.perf_counter() - t0
@@ -213,6 +280,8 @@ def main():
     ap.add_argument("--workload", default=W.HEADLINE, choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--variant", choices=VARIANTS, default=None,
+                    help="time the step with one of the variants instead of the default path")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run one plain device-to-device copy of MIB MiB "
                          "(a known-size reference for hardware memory counters)")
@@ -223,7 +292,7 @@ def main():
         sys.exit(2)
 
     w = W.WORKLOADS[args.workload]
-    elapsed, per_op, kept = run_gpu(w, args.steps, args.warmup)
+    elapsed, per_op, kept, rows = run_gpu(w, args.steps, args.warmup, args.variant)
     if args.calibrate_copy > 0:
         import torch
         src = torch.ones(args.calibrate_copy << 20, dtype=torch.uint8, device="cuda:0")
@@ -233,16 +302,17 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     ms_per_step = elapsed / args.steps * 1e3
-    abytes = algorithmic_bytes(w, kept)
+    abytes = algorithmic_bytes(w, kept, rows, args.variant)
+    ops = list(per_op)
     kernels = {}
-    for op in OPS:
+    for op in ops:
         us = float(np.mean(per_op[op]))
         kernels[op] = {"us": round(us, 2), "us_median": round(float(np.median(per_op[op])), 2),
                        "bytes": abytes[op], "GBps": round(abytes[op] / us / 1e3, 1)}
     dc_us = kernels["dispatch"]["us"] + kernels["combine"]["us"]
     dc_bytes = abytes["dispatch"] + abytes["combine"]
     dc_gbps = dc_bytes / dc_us / 1e3
-    dominant = max(OPS, key=lambda op: kernels[op]["us"])
+    dominant = max(ops, key=lambda op: kernels[op]["us"])
     dom_gbps = abytes[dominant] / kernels[dominant]["us"] / 1e3
 
     line = {
@@ -262,20 +332,20 @@ def main():
                    "capacity": w.capacity if w.capacity > 0 else "dropless",
                    "routing": {"uniform": "N(0,1) logits", "zipf": "N(0,1) + 2 ln Zipf(1.2) bias",
                                "hotspot": "N(0,1), +3 on expert 0 for 10% of tokens"}[w.routing],
-                   "step": "gate+layout+dispatch+combine+replay+combine_bwd+dispatch_bwd+gate_bwd",
+                   "step": "+".join(ops), "variant": args.variant or "default",
                    "parallelism": "single GPU"},
         "dispatch_combine": {"tokens_per_s": round(w.s / (dc_us / 1e6), 1), "GBps": round(dc_gbps, 1),
                              "frac_of_hbm_peak": round(dc_gbps / HBM_PEAK_GBPS, 4), "us": round(dc_us, 2),
                              "bytes": dc_bytes},
         "roofline": {"kernel": dominant, "bound": "hbm", "achieved": round(dom_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(w.name).get(dominant),
+                     "traffic": None if args.variant else measured_traffic(w.name).get(dominant),
                      "algorithmic_bytes": abytes[dominant]},
         "kernels": kernels,
         "kept_routes": kept,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = run_cpu_baseline(w, args.cpu_seconds)
+        line["cpu_baseline"] = run_cpu_baseline(w, args.cpu_seconds, variant=args.variant)
     print(json.dumps(line), flush=True)
 
 

@@ -54,12 +54,18 @@ class LayoutStruct(ctypes.Structure):
         ("magic", ctypes.c_uint64),
         ("s", ctypes.c_int32), ("e", ctypes.c_int32), ("k", ctypes.c_int32),
         ("capacity", ctypes.c_int32),
+        ("route_major", ctypes.c_int32), ("pad_multiple", ctypes.c_int32),
         ("rows", ctypes.c_int64),
         ("counts", ctypes.c_void_p), ("kept", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
         ("dst", ctypes.c_void_p), ("src", ctypes.c_void_p), ("route_idx", ctypes.c_void_p),
         ("checksum", ctypes.c_void_p), ("flags", ctypes.c_void_p), ("scratch", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
     ]
+
+
+class LayoutOptions(ctypes.Structure):
+    """Mirror of moe_layout_options_t."""
+    _fields_ = [("route_major", ctypes.c_int32), ("pad_multiple", ctypes.c_int32)]
 
 
 _lib = None
@@ -71,6 +77,14 @@ _SIGNATURES = {
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_layout_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "moe_layout_workspace_bytes_ex": (ctypes.c_size_t, [_I, _I, _I, _I, ctypes.POINTER(LayoutOptions)]),
+    "moe_dispatch_layout_ex": (ctypes.c_int, [_P, _I, _I, _I, _I, ctypes.POINTER(LayoutOptions), _P,
+                                              ctypes.c_size_t, ctypes.POINTER(LayoutStruct), _P]),
+    "moe_dispatch_weighted": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _P, _I, ctypes.c_int, _P, _P]),
+    "moe_dispatch_weighted_backward": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _P, _P, _I,
+                                                      ctypes.c_int, _P, _P, _P]),
+    "moe_renormalize_kept": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _P, _P]),
+    "moe_renormalize_kept_backward": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _P, _P, _P]),
     "moe_gate_topk": (ctypes.c_int, [_P, _I, _I, _I, _P, _P, _P]),
     "moe_gate_topk_backward": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _P, _P]),
     "moe_dispatch_layout": (ctypes.c_int, [_P, _I, _I, _I, _I, _P, ctypes.c_size_t,
@@ -125,8 +139,10 @@ def _require_gpu(*tensors):
             raise ValueError("all tensors must be contiguous")
 
 
-def workspace_bytes(s: int, e: int, k: int, capacity: int) -> int:
-    return int(lib().moe_layout_workspace_bytes(s, e, k, capacity))
+def workspace_bytes(s: int, e: int, k: int, capacity: int, route_major: bool = False,
+                    pad_multiple: int = 1) -> int:
+    opts = LayoutOptions(int(route_major), pad_multiple)
+    return int(lib().moe_layout_workspace_bytes_ex(s, e, k, capacity, ctypes.byref(opts)))
 
 
 class Layout:
@@ -150,6 +166,10 @@ class Layout:
     def capacity(self): return self.struct.capacity
     @property
     def rows(self): return int(self.struct.rows)
+    @property
+    def route_major(self): return bool(self.struct.route_major)
+    @property
+    def pad_multiple(self): return int(self.struct.pad_multiple)
 
     def _view(self, ptr, n, dtype=torch.int32):
         off = ptr - self.workspace.data_ptr()
@@ -192,21 +212,25 @@ def moe_gate_topk_backward(idx: torch.Tensor, w: torch.Tensor, grad_w: torch.Ten
     return gl
 
 
-def moe_dispatch_layout(idx: torch.Tensor, e: int, capacity: int = 0, workspace=None) -> Layout:
+def moe_dispatch_layout(idx: torch.Tensor, e: int, capacity: int = 0, workspace=None,
+                        route_major: bool = False, pad_multiple: int = 1) -> Layout:
     _require_gpu(idx)
     if idx.dtype != torch.int32:
         raise ValueError("expert ids must be int32")
     s, k = idx.shape
-    nbytes = workspace_bytes(s, e, k, capacity)
+    opts = LayoutOptions(int(route_major), pad_multiple)
+    nbytes = workspace_bytes(s, e, k, capacity, route_major, pad_multiple)
     if nbytes == 0:
         # let the library name the problem
-        _check(lib().moe_dispatch_layout(_ptr(idx), s, e, k, capacity, ctypes.c_void_p(0), 0,
-                                         ctypes.byref(LayoutStruct()), _stream(idx)))
+        _check(lib().moe_dispatch_layout_ex(_ptr(idx), s, e, k, capacity, ctypes.byref(opts),
+                                            ctypes.c_void_p(0), 0, ctypes.byref(LayoutStruct()),
+                                            _stream(idx)))
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=idx.device)
     st = LayoutStruct()
-    _check(lib().moe_dispatch_layout(_ptr(idx), s, e, k, capacity, _ptr(workspace),
-                                     workspace.numel(), ctypes.byref(st), _stream(idx)))
+    _check(lib().moe_dispatch_layout_ex(_ptr(idx), s, e, k, capacity, ctypes.byref(opts),
+                                        _ptr(workspace), workspace.numel(), ctypes.byref(st),
+                                        _stream(idx)))
     return Layout(st, workspace)
 
 
@@ -234,7 +258,8 @@ def moe_dispatch_replay(layout: Layout, x: torch.Tensor, idx=None, out=None):
     return out
 
 
-def moe_combine(layout: Layout, expert_out: torch.Tensor, w: torch.Tensor, out=None):
+def moe_combine(layout: Layout, expert_out: torch.Tensor, w, out=None):
+    """Weighted combine; w=None gives the unweighted sum (after moe_dispatch_weighted)."""
     _require_gpu(expert_out, w)
     m = expert_out.shape[1]
     y = out if out is not None else torch.empty((layout.s, m), dtype=expert_out.dtype, device=expert_out.device)
@@ -265,6 +290,42 @@ def moe_dispatch_backward(layout: Layout, grad_out: torch.Tensor, out=None):
     return gx
 
 
+def moe_dispatch_weighted(layout: Layout, x: torch.Tensor, w: torch.Tensor, out=None):
+    _require_gpu(x, w)
+    m = x.shape[1]
+    out = out if out is not None else torch.empty((layout.rows, m), dtype=x.dtype, device=x.device)
+    _check(lib().moe_dispatch_weighted(layout.byref(), _ptr(x), _ptr(w), m, _dtype_code(x), _ptr(out),
+                                       _stream(x)))
+    return out
+
+
+def moe_dispatch_weighted_backward(layout: Layout, grad_out: torch.Tensor, x: torch.Tensor,
+                                   w: torch.Tensor, grad_x=None, grad_w=None):
+    _require_gpu(grad_out, x, w)
+    m = x.shape[1]
+    gx = grad_x if grad_x is not None else torch.empty_like(x)
+    gw = grad_w if grad_w is not None else torch.empty((layout.s, layout.k), dtype=torch.float32,
+                                                      device=x.device)
+    _check(lib().moe_dispatch_weighted_backward(layout.byref(), _ptr(grad_out), _ptr(x), _ptr(w), m,
+                                                _dtype_code(x), _ptr(gx), _ptr(gw), _stream(x)))
+    return gx, gw
+
+
+def moe_renormalize_kept(layout: Layout, w: torch.Tensor, out=None):
+    _require_gpu(w)
+    w_out = out if out is not None else torch.empty_like(w)
+    _check(lib().moe_renormalize_kept(layout.byref(), _ptr(w), _ptr(w_out), _stream(w)))
+    return w_out
+
+
+def moe_renormalize_kept_backward(layout: Layout, w: torch.Tensor, grad_out: torch.Tensor, out=None):
+    _require_gpu(w, grad_out)
+    gw = out if out is not None else torch.empty_like(w)
+    _check(lib().moe_renormalize_kept_backward(layout.byref(), _ptr(w), _ptr(grad_out), _ptr(gw),
+                                               _stream(w)))
+    return gw
+
+
 def moe_layout_read(layout: Layout):
     flags = ctypes.c_int32(0)
     checksum = ctypes.c_uint64(0)
@@ -276,5 +337,7 @@ def moe_layout_read(layout: Layout):
 __all__ = [
     "moe_gate_topk", "moe_gate_topk_backward", "moe_dispatch_layout", "moe_dispatch",
     "moe_dispatch_replay", "moe_combine", "moe_combine_backward", "moe_dispatch_backward",
-    "moe_layout_read", "workspace_bytes", "Layout", "MoeError", "lib", "EXPORTS",
+    "moe_layout_read", "moe_dispatch_weighted", "moe_dispatch_weighted_backward",
+    "moe_renormalize_kept", "moe_renormalize_kept_backward", "workspace_bytes", "Layout",
+    "LayoutOptions", "MoeError", "lib", "EXPORTS",
 ]

@@ -31,8 +31,10 @@ import torch
 import torch.utils.checkpoint
 
 from . import (FLAG_REPLAY_MISMATCH, Layout, moe_combine, moe_combine_backward, moe_dispatch,
-               moe_dispatch_backward, moe_dispatch_layout, moe_dispatch_replay, moe_gate_topk,
-               moe_gate_topk_backward, moe_layout_read)
+               moe_dispatch_backward, moe_dispatch_layout, moe_dispatch_replay,
+               moe_dispatch_weighted, moe_dispatch_weighted_backward, moe_gate_topk,
+               moe_gate_topk_backward, moe_layout_read, moe_renormalize_kept,
+               moe_renormalize_kept_backward)
 
 
 class _Gate(torch.autograd.Function):
@@ -65,6 +67,24 @@ class _Dispatch(torch.autograd.Function):
         return moe_dispatch_backward(ctx.layout, g_buf.contiguous()), None, None
 
 
+class _DispatchWeighted(torch.autograd.Function):
+    """Weights applied before the experts: out[dst] = w * x."""
+
+    @staticmethod
+    def forward(ctx, x, w, layout):
+        x = x.contiguous()
+        w = w.contiguous()
+        ctx.layout = layout
+        ctx.save_for_backward(x, w)
+        return moe_dispatch_weighted(layout, x, w)
+
+    @staticmethod
+    def backward(ctx, g_buf):
+        x, w = ctx.saved_tensors
+        g_x, g_w = moe_dispatch_weighted_backward(ctx.layout, g_buf.contiguous(), x, w)
+        return g_x, g_w, None
+
+
 class _Combine(torch.autograd.Function):
     @staticmethod
     def forward(ctx, expert_out, w, layout):
@@ -79,6 +99,33 @@ class _Combine(torch.autograd.Function):
         expert_out, w = ctx.saved_tensors
         g_e, g_w = moe_combine_backward(ctx.layout, g_y.contiguous(), expert_out, w)
         return g_e, g_w, None
+
+
+class _Sum(torch.autograd.Function):
+    """Unweighted combine (after a weighted dispatch); its gradient is a plain dispatch."""
+
+    @staticmethod
+    def forward(ctx, expert_out, layout):
+        ctx.layout = layout
+        return moe_combine(layout, expert_out.contiguous(), None)
+
+    @staticmethod
+    def backward(ctx, g_y):
+        return moe_dispatch(ctx.layout, g_y.contiguous()), None
+
+
+class _Renormalize(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, w, layout):
+        w = w.contiguous()
+        ctx.layout = layout
+        ctx.save_for_backward(w)
+        return moe_renormalize_kept(layout, w)
+
+    @staticmethod
+    def backward(ctx, g):
+        (w,) = ctx.saved_tensors
+        return moe_renormalize_kept_backward(ctx.layout, w, g.float().contiguous()), None
 
 
 class LayoutRecorder:
@@ -108,11 +155,11 @@ class LayoutRecorder:
         self.passes += 1
         return False
 
-    def layout_for(self, idx: torch.Tensor, e: int, capacity: int):
+    def layout_for(self, idx: torch.Tensor, e: int, capacity: int, **options):
         """The layout to dispatch with, and the routing to verify a replay against."""
-        key = (tuple(idx.shape), e, capacity)
+        key = (tuple(idx.shape), e, capacity, tuple(sorted(options.items())))
         if self._recording:
-            layout = moe_dispatch_layout(idx, e, capacity)
+            layout = moe_dispatch_layout(idx, e, capacity, **options)
             self.layouts_built += 1
             self.log.append((layout, key))
             return layout, None
@@ -125,7 +172,7 @@ class LayoutRecorder:
             self._replayed.append(layout)
             return layout, (idx.contiguous() if self.verify else None)
         self.fallbacks += 1  # the recompute outran its log: build the layout afresh
-        layout = moe_dispatch_layout(idx, e, capacity)
+        layout = moe_dispatch_layout(idx, e, capacity, **options)
         self.layouts_built += 1
         return layout, None
 
@@ -142,19 +189,47 @@ def route(logits: torch.Tensor, k: int):
     return _Gate.apply(logits, k)
 
 
-def dispatch(x: torch.Tensor, idx: torch.Tensor, e: int, capacity: int = 0,
-             recorder: LayoutRecorder | None = None):
-    """Permute token rows into the expert-grouped buffer. Returns (buffer, layout)."""
+def layout(idx: torch.Tensor, e: int, capacity: int = 0, recorder: LayoutRecorder | None = None,
+           route_major: bool = False, pad_multiple: int = 1):
+    """The dispatch layout (recorded or replayed through `recorder` if given)."""
+    options = dict(route_major=route_major, pad_multiple=pad_multiple)
     if recorder is not None:
-        layout, verify_idx = recorder.layout_for(idx, e, capacity)
-    else:
-        layout, verify_idx = moe_dispatch_layout(idx, e, capacity), None
-    return _Dispatch.apply(x, layout, verify_idx), layout
+        return recorder.layout_for(idx, e, capacity, **options)
+    return moe_dispatch_layout(idx, e, capacity, **options), None
 
 
-def combine(expert_out: torch.Tensor, w: torch.Tensor, layout: Layout):
-    """Weighted, route-ordered float32 sum of each token's expert rows."""
+def dispatch(x: torch.Tensor, idx: torch.Tensor, e: int, capacity: int = 0,
+             recorder: LayoutRecorder | None = None, w: torch.Tensor | None = None,
+             route_major: bool = False, pad_multiple: int = 1):
+    """Permute token rows into the expert-grouped buffer. Returns (buffer, layout).
+
+    With w given, the weights are applied here, before the experts (the combine is
+    then combine(expert_out, None, layout)); a recorder's routing verification
+    covers the plain dispatch only.
+    """
+    L, verify_idx = layout(idx, e, capacity, recorder, route_major, pad_multiple)
+    if w is not None:
+        return _DispatchWeighted.apply(x, w, L), L
+    return _Dispatch.apply(x, L, verify_idx), L
+
+
+def dispatch_on(x: torch.Tensor, layout: Layout, w: torch.Tensor | None = None):
+    """Dispatch on a layout built earlier (e.g. one whose weights were renormalised)."""
+    if w is not None:
+        return _DispatchWeighted.apply(x, w, layout)
+    return _Dispatch.apply(x, layout, None)
+
+
+def combine(expert_out: torch.Tensor, w: torch.Tensor | None, layout: Layout):
+    """Route-ordered float32 sum of each token's expert rows, weighted unless w is None."""
+    if w is None:
+        return _Sum.apply(expert_out, layout)
     return _Combine.apply(expert_out, w, layout)
+
+
+def renormalize(w: torch.Tensor, layout: Layout):
+    """Weights renormalised over each token's kept routes (after the capacity drop)."""
+    return _Renormalize.apply(w, layout)
 
 
 def checkpoint(fn, *args, verify: bool = False, **kwargs):
@@ -169,4 +244,4 @@ def checkpoint(fn, *args, verify: bool = False, **kwargs):
     return out, rec
 
 
-__all__ = ["route", "dispatch", "combine", "checkpoint", "LayoutRecorder"]
+__all__ = ["route", "layout", "dispatch", "dispatch_on", "combine", "renormalize", "checkpoint", "LayoutRecorder"]

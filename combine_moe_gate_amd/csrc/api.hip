@@ -79,10 +79,36 @@ moe_status_t check_sizes(int32_t s, int32_t e, int32_t k, int32_t capacity) {
   return MOE_OK;
 }
 
-Plan make_plan(int32_t s, int32_t e, int32_t k, int32_t capacity) {
+struct Options {
+  int32_t route_major = 0;
+  int32_t pad_multiple = 1;
+};
+
+moe_status_t read_options(const moe_layout_options_t* o, int32_t s, int32_t e, int32_t k,
+                          int32_t capacity, Options* out) {
+  Options opt;
+  if (o != nullptr) {
+    opt.route_major = o->route_major;
+    opt.pad_multiple = o->pad_multiple;
+  }
+  if (opt.route_major != 0 && opt.route_major != 1)
+    return fail(MOE_ERR_INVALID_ARG, "route_major must be 0 or 1 (got %d)", opt.route_major);
+  if (opt.pad_multiple < 1)
+    return fail(MOE_ERR_INVALID_ARG, "pad_multiple must be >= 1 (got %d)", opt.pad_multiple);
+  if (opt.pad_multiple > 1 && capacity > 0)
+    return fail(MOE_ERR_INVALID_ARG, "pad_multiple applies to dropless layouts only");
+  if (static_cast<int64_t>(s) * k + static_cast<int64_t>(e) * (opt.pad_multiple - 1) > INT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "padded row count exceeds 32-bit row ids");
+  *out = opt;
+  return MOE_OK;
+}
+
+Plan make_plan(int32_t s, int32_t e, int32_t k, int32_t capacity, const Options& opt) {
   Plan p;
-  p.rows = capacity > 0 ? static_cast<int64_t>(e) * capacity : static_cast<int64_t>(s) * k;
-  p.ntiles = (s + moe::kTileTokens - 1) / moe::kTileTokens;
+  p.rows = capacity > 0 ? static_cast<int64_t>(e) * capacity
+                        : static_cast<int64_t>(s) * k + static_cast<int64_t>(e) * (opt.pad_multiple - 1);
+  const int64_t items = opt.route_major ? static_cast<int64_t>(s) * k : s;
+  p.ntiles = static_cast<int32_t>((items + moe::kTileTokens - 1) / moe::kTileTokens);
   const size_t routes = static_cast<size_t>(s) * k;
   size_t cur = 0;
   p.off_counts = take(cur, sizeof(int32_t) * e);
@@ -107,7 +133,11 @@ moe_status_t view_of(const moe_layout_t* h, moe::LayoutView* v) {
     return fail(MOE_ERR_HANDLE_MISMATCH, "layout was not filled by moe_dispatch_layout");
   moe_status_t st = check_sizes(h->s, h->e, h->k, h->capacity);
   if (st != MOE_OK) return fail(MOE_ERR_HANDLE_MISMATCH, "layout sizes invalid: %s", g_last_error.c_str());
-  const Plan p = make_plan(h->s, h->e, h->k, h->capacity);
+  moe_layout_options_t o{h->route_major, h->pad_multiple};
+  Options opt;
+  st = read_options(&o, h->s, h->e, h->k, h->capacity, &opt);
+  if (st != MOE_OK) return fail(MOE_ERR_HANDLE_MISMATCH, "layout options invalid: %s", g_last_error.c_str());
+  const Plan p = make_plan(h->s, h->e, h->k, h->capacity, opt);
   if (h->rows != p.rows || h->workspace == nullptr || h->workspace_bytes < p.bytes)
     return fail(MOE_ERR_HANDLE_MISMATCH, "layout fields are inconsistent with its sizes");
   char* ws = static_cast<char*>(h->workspace);
@@ -119,6 +149,8 @@ moe_status_t view_of(const moe_layout_t* h, moe::LayoutView* v) {
   v->e = h->e;
   v->k = h->k;
   v->capacity = h->capacity > 0 ? h->capacity : 0;
+  v->route_major = opt.route_major;
+  v->pad_multiple = opt.pad_multiple;
   v->rows = p.rows;
   v->ntiles = p.ntiles;
   v->counts = reinterpret_cast<int32_t*>(ws + p.off_counts);
@@ -183,13 +215,21 @@ const char* moe_status_string(moe_status_t status) {
   }
 }
 
-size_t moe_layout_workspace_bytes(int32_t s, int32_t e, int32_t k, int32_t capacity) {
+size_t moe_layout_workspace_bytes_ex(int32_t s, int32_t e, int32_t k, int32_t capacity,
+                                     const moe_layout_options_t* options) {
   const std::string saved = g_last_error;
-  if (check_sizes(s, e, k, capacity) != MOE_OK) {
+  if (capacity < 0) capacity = 0;
+  Options opt;
+  if (check_sizes(s, e, k, capacity) != MOE_OK ||
+      read_options(options, s, e, k, capacity, &opt) != MOE_OK) {
     g_last_error = saved;
     return 0;
   }
-  return make_plan(s, e, k, capacity).bytes;
+  return make_plan(s, e, k, capacity, opt).bytes;
+}
+
+size_t moe_layout_workspace_bytes(int32_t s, int32_t e, int32_t k, int32_t capacity) {
+  return moe_layout_workspace_bytes_ex(s, e, k, capacity, nullptr);
 }
 
 moe_status_t moe_gate_topk(const float* logits, int32_t s, int32_t e, int32_t k,
@@ -219,14 +259,24 @@ moe_status_t moe_gate_topk_backward(const int32_t* topk_idx, const float* topk_w
 moe_status_t moe_dispatch_layout(const int32_t* topk_idx, int32_t s, int32_t e, int32_t k,
                                  int32_t capacity, void* workspace, size_t workspace_bytes,
                                  moe_layout_t* layout, void* stream) {
+  return moe_dispatch_layout_ex(topk_idx, s, e, k, capacity, nullptr, workspace, workspace_bytes,
+                                layout, stream);
+}
+
+moe_status_t moe_dispatch_layout_ex(const int32_t* topk_idx, int32_t s, int32_t e, int32_t k,
+                                    int32_t capacity, const moe_layout_options_t* options,
+                                    void* workspace, size_t workspace_bytes,
+                                    moe_layout_t* layout, void* stream) {
   if (capacity < 0) capacity = 0;
   MOE_TRY(check_sizes(s, e, k, capacity));
+  Options opt;
+  MOE_TRY(read_options(options, s, e, k, capacity, &opt));
   if (layout == nullptr) return fail(MOE_ERR_INVALID_ARG, "layout is NULL");
   MOE_TRY(check_array(topk_idx, s, "topk_idx", false));
   if (workspace == nullptr) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
     return fail(MOE_ERR_MISALIGNED, "workspace is not %zu-byte aligned", kAlign);
-  const Plan p = make_plan(s, e, k, capacity);
+  const Plan p = make_plan(s, e, k, capacity, opt);
   if (workspace_bytes < p.bytes)
     return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, the layout needs %zu",
                 workspace_bytes, p.bytes);
@@ -239,6 +289,8 @@ moe_status_t moe_dispatch_layout(const int32_t* topk_idx, int32_t s, int32_t e, 
   h.e = e;
   h.k = k;
   h.capacity = capacity;
+  h.route_major = opt.route_major;
+  h.pad_multiple = opt.pad_multiple;
   h.rows = p.rows;
   h.counts = reinterpret_cast<int32_t*>(ws + p.off_counts);
   h.kept = reinterpret_cast<int32_t*>(ws + p.off_kept);
@@ -292,11 +344,67 @@ moe_status_t moe_combine(const moe_layout_t* layout, const void* expert_out,
   int64_t rc = 0;
   MOE_TRY(check_rows(m, dtype, &rc));
   MOE_TRY(check_array(expert_out, v.s > 0 ? v.rows : 0, "expert_out", true));
-  MOE_TRY(check_array(topk_w, v.s, "topk_w", false));
   MOE_TRY(check_array(y, v.s, "y", true));
   return hip_status(moe::launch_combine(v, expert_out, topk_w, rc, static_cast<int>(dtype), y,
                                         static_cast<hipStream_t>(stream)),
                     "moe_combine");
+}
+
+moe_status_t moe_dispatch_weighted(const moe_layout_t* layout, const void* x,
+                                   const float* topk_w, int32_t m, moe_dtype_t dtype, void* out,
+                                   void* stream) {
+  moe::LayoutView v;
+  MOE_TRY(view_of(layout, &v));
+  int64_t rc = 0;
+  MOE_TRY(check_rows(m, dtype, &rc));
+  MOE_TRY(check_array(x, v.s, "x", true));
+  MOE_TRY(check_array(topk_w, v.s, "topk_w", false));
+  MOE_TRY(check_array(out, v.rows, "out", true));
+  return hip_status(moe::launch_dispatch_weighted(v, x, topk_w, rc, static_cast<int>(dtype), out,
+                                                  static_cast<hipStream_t>(stream)),
+                    "moe_dispatch_weighted");
+}
+
+moe_status_t moe_dispatch_weighted_backward(const moe_layout_t* layout, const void* grad_out,
+                                            const void* x, const float* topk_w, int32_t m,
+                                            moe_dtype_t dtype, void* grad_x, float* grad_w,
+                                            void* stream) {
+  moe::LayoutView v;
+  MOE_TRY(view_of(layout, &v));
+  int64_t rc = 0;
+  MOE_TRY(check_rows(m, dtype, &rc));
+  MOE_TRY(check_array(grad_out, v.s > 0 ? v.rows : 0, "grad_out", true));
+  MOE_TRY(check_array(x, v.s, "x", true));
+  MOE_TRY(check_array(topk_w, v.s, "topk_w", false));
+  MOE_TRY(check_array(grad_x, v.s, "grad_x", true));
+  MOE_TRY(check_array(grad_w, v.s, "grad_w", false));
+  return hip_status(moe::launch_dispatch_weighted_backward(v, grad_out, x, topk_w, rc,
+                                                           static_cast<int>(dtype), grad_x, grad_w,
+                                                           static_cast<hipStream_t>(stream)),
+                    "moe_dispatch_weighted_backward");
+}
+
+moe_status_t moe_renormalize_kept(const moe_layout_t* layout, const float* topk_w, float* w_out,
+                                  void* stream) {
+  moe::LayoutView v;
+  MOE_TRY(view_of(layout, &v));
+  MOE_TRY(check_array(topk_w, v.s, "topk_w", false));
+  MOE_TRY(check_array(w_out, v.s, "w_out", false));
+  if (v.s > 0 && topk_w == w_out) return fail(MOE_ERR_INVALID_ARG, "topk_w and w_out may not overlap");
+  return hip_status(moe::launch_renormalize_kept(v, topk_w, w_out, static_cast<hipStream_t>(stream)),
+                    "moe_renormalize_kept");
+}
+
+moe_status_t moe_renormalize_kept_backward(const moe_layout_t* layout, const float* topk_w,
+                                           const float* grad_out, float* grad_w, void* stream) {
+  moe::LayoutView v;
+  MOE_TRY(view_of(layout, &v));
+  MOE_TRY(check_array(topk_w, v.s, "topk_w", false));
+  MOE_TRY(check_array(grad_out, v.s, "grad_out", false));
+  MOE_TRY(check_array(grad_w, v.s, "grad_w", false));
+  return hip_status(moe::launch_renormalize_kept_backward(v, topk_w, grad_out, grad_w,
+                                                          static_cast<hipStream_t>(stream)),
+                    "moe_renormalize_kept_backward");
 }
 
 moe_status_t moe_combine_backward(const moe_layout_t* layout, const void* grad_y,

@@ -110,6 +110,62 @@ __global__ __launch_bounds__(kBlock) void gate_topk_backward_kernel(
   }
 }
 
+// Weights renormalised over each token's kept routes (dst >= 0): w' = w / S with S the
+// float64 sum of the kept weights in route order; 0 for dropped routes, and for every
+// route when nothing is kept. One thread per token.
+__global__ __launch_bounds__(kBlock) void renormalize_kept_kernel(const int32_t* __restrict__ dst,
+                                                                  const float* __restrict__ w,
+                                                                  int s, int k,
+                                                                  float* __restrict__ w_out) {
+  const int t = blockIdx.x * kBlock + threadIdx.x;
+  if (t >= s) return;
+  const size_t o = static_cast<size_t>(t) * k;
+  double S = 0.0;
+  for (int j = 0; j < k; ++j)
+    if (dst[o + j] >= 0) S += static_cast<double>(w[o + j]);
+  for (int j = 0; j < k; ++j) {
+    const bool keep = dst[o + j] >= 0 && S != 0.0;
+    w_out[o + j] = keep ? static_cast<float>(static_cast<double>(w[o + j]) / S) : 0.0f;
+  }
+}
+
+// Its backward: with u_j = w_j / S over kept routes, grad_w_i = (g_i - sum_q u_q g_q) / S
+// for kept i and 0 otherwise, in float64 (sums in route order).
+__global__ __launch_bounds__(kBlock) void renormalize_kept_backward_kernel(
+    const int32_t* __restrict__ dst, const float* __restrict__ w, const float* __restrict__ g,
+    int s, int k, float* __restrict__ gw) {
+  const int t = blockIdx.x * kBlock + threadIdx.x;
+  if (t >= s) return;
+  const size_t o = static_cast<size_t>(t) * k;
+  double S = 0.0;
+  for (int j = 0; j < k; ++j)
+    if (dst[o + j] >= 0) S += static_cast<double>(w[o + j]);
+  double dot = 0.0;
+  if (S != 0.0)
+    for (int j = 0; j < k; ++j)
+      if (dst[o + j] >= 0) dot += (static_cast<double>(w[o + j]) / S) * static_cast<double>(g[o + j]);
+  for (int j = 0; j < k; ++j) {
+    const bool keep = dst[o + j] >= 0 && S != 0.0;
+    gw[o + j] = keep ? static_cast<float>((static_cast<double>(g[o + j]) - dot) / S) : 0.0f;
+  }
+}
+
+hipError_t launch_renormalize_kept(const LayoutView& L, const float* w, float* w_out,
+                                   hipStream_t stream) {
+  if (L.s == 0) return hipSuccess;
+  renormalize_kept_kernel<<<(L.s + kBlock - 1) / kBlock, kBlock, 0, stream>>>(L.dst, w, L.s, L.k, w_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_renormalize_kept_backward(const LayoutView& L, const float* w,
+                                            const float* grad_out, float* grad_w,
+                                            hipStream_t stream) {
+  if (L.s == 0) return hipSuccess;
+  renormalize_kept_backward_kernel<<<(L.s + kBlock - 1) / kBlock, kBlock, 0, stream>>>(
+      L.dst, w, grad_out, L.s, L.k, grad_w);
+  return hipGetLastError();
+}
+
 static int values_per_lane(int e) {
   const int v = (e + kWave - 1) / kWave;
   return v <= 1 ? 1 : v <= 2 ? 2 : v <= 4 ? 4 : v <= 8 ? 8 : 16;

@@ -9,8 +9,10 @@ namespace moe {
 // Device view of a layout: the handle's arrays plus the internal tile scratch.
 struct LayoutView {
   int32_t s, e, k, capacity;  // capacity 0 = dropless
+  int32_t route_major;        // 1: slots walk every token's first route, then second, ...
+  int32_t pad_multiple;       // dropless segments rounded up to this many rows (>= 1)
   int64_t rows;
-  int32_t ntiles;             // ceil(s / kTileTokens)
+  int32_t ntiles;             // ceil(items / kTileTokens); items = s, or s*k route-major
   int32_t* counts;
   int32_t* kept;
   int32_t* offsets;
@@ -43,5 +45,18 @@ hipError_t launch_combine(const LayoutView& L, const void* rows_in, const float*
 hipError_t launch_combine_backward(const LayoutView& L, const void* gy, const void* E,
                                    const float* w, int64_t row_chunks, int dtype, void* gE,
                                    float* gw, hipStream_t stream);
+// Weights applied at dispatch: out[dst] = w * x (and its backward: a weighted combine of
+// grad_out plus grad_w = <grad_out[dst], x>).
+hipError_t launch_dispatch_weighted(const LayoutView& L, const void* x, const float* w,
+                                    int64_t row_chunks, int dtype, void* out, hipStream_t stream);
+hipError_t launch_dispatch_weighted_backward(const LayoutView& L, const void* grad_out,
+                                             const void* x, const float* w, int64_t row_chunks,
+                                             int dtype, void* gx, float* gw, hipStream_t stream);
+// Weights renormalised over each token's kept routes, and the backward.
+hipError_t launch_renormalize_kept(const LayoutView& L, const float* w, float* w_out,
+                                   hipStream_t stream);
+hipError_t launch_renormalize_kept_backward(const LayoutView& L, const float* w,
+                                            const float* grad_out, float* grad_w,
+                                            hipStream_t stream);
 
 }  // namespace moe

@@ -1,11 +1,19 @@
-// Dispatch layout on gfx950: per-expert counts, token-order slots, capacity drop, and
-// the route -> row (dst) and row -> token (src) maps.
+// Dispatch layout on gfx950: per-expert counts, slots, capacity drop, and the
+// route -> row (dst) and row -> token (src) maps.
 //
 // The slot of a route is the column cumsum of the token x expert mask minus one
 // (DeepSpeed PR "MoE dispatch: fix silent Tutel + TP corruption, speed up native and
-// Tutel paths", review comment on fast_cumsum_sub_one), i.e. the number of earlier
-// tokens that chose the same expert. It is computed without sorting and without any
-// order-dependent atomics, in two launches over tiles of 256 tokens:
+// Tutel paths", review comment on fast_cumsum_sub_one): the number of routes to the
+// same expert that come earlier. "Earlier" walks the routes as items:
+//
+//   token order  (default) item t = token t with its k routes; a token's routes never
+//                share an expert, so the slot counts earlier tokens.
+//   route major  item v = j*s + t holds the single route (t, j): every token's first
+//                route comes before every second route (the per-route masks mask1,
+//                mask2, ... of the same review comment, later columns offset by the
+//                counts of earlier ones), so first choices win capacity.
+//
+// No sorting and no order-dependent atomics; two launches over tiles of 256 items:
 //
 //   count  one workgroup per tile: LDS histogram of the tile's valid routes (integer
 //          atomic adds; the totals do not depend on their order), the tile's share of
@@ -13,64 +21,88 @@
 //   place  one workgroup per tile again. Each workgroup first derives what it needs
 //          from the small, L2-resident tile tables: for every expert the sum over
 //          earlier tiles (its tile base) and over all tiles (the count), then an
-//          exclusive scan over experts of the segment sizes (the dropless offsets; with
-//          a capacity every segment is `capacity` rows). Workgroup 0 publishes counts,
-//          kept, offsets, checksum and flags. Then each wave builds, per expert, a
-//          64-bit mask of its lanes (tokens) that chose it (LDS atomic OR: order-
-//          independent); a route's slot is tile base + popcounts of the earlier waves'
-//          masks + popcount of its own wave's mask below its lane. It writes dst, src
-//          and a copy of the routing; rows no route fills get src = -1.
+//          exclusive scan over experts of the segment sizes (dropless: the count,
+//          rounded up to the pad multiple; with a capacity: the capacity). Workgroup 0
+//          publishes counts, kept, offsets, checksum and flags. Then each wave builds,
+//          per expert, a 64-bit mask of its lanes (items) that chose it (LDS atomic OR:
+//          order-independent); a route's slot is tile base + popcounts of the earlier
+//          waves' masks + popcount of its own wave's mask below its lane. It writes
+//          dst, src and a copy of the routing. Rows no route fills get src = -1.
 #include "internal.h"
 #include "moe_device.h"
 
 namespace moe {
 
-// Load a token's k expert ids and decide which routes are valid: in [0, e) and not a
-// repeat of an earlier route of the same token. Returns the flag bits raised.
-template <int KMAX>
-__device__ __forceinline__ int load_routes(const int32_t* __restrict__ idx, int t, int k, int e,
-                                           int (&ids)[KMAX], bool (&ok)[KMAX]) {
+// The routes of one item. Token order: item t holds routes (t, 0..k-1); route major:
+// item v holds the single route (v mod s, v div s). A route is valid if its expert is
+// in [0, e) and no earlier route of the same token named it. Returns the flag bits.
+template <int KMAX, bool RM>
+__device__ __forceinline__ int load_item(const int32_t* __restrict__ idx, int item, int s, int k,
+                                         int e, int& tok, int (&ids)[KMAX], bool (&ok)[KMAX],
+                                         int64_t (&pos)[KMAX]) {
   int flags = 0;
+  if constexpr (RM) {
+    static_assert(KMAX == 1, "one route per item in route-major order");
+    const int j = item / s;
+    const int t = item - j * s;
+    tok = t;
+    const int64_t base = static_cast<int64_t>(t) * k;
+    pos[0] = base + j;
+    ids[0] = idx[pos[0]];
+    const bool in_range = static_cast<unsigned>(ids[0]) < static_cast<unsigned>(e);
+    bool dup = false;
+    for (int q = 0; q < j; ++q) dup |= (idx[base + q] == ids[0]);
+    if (!in_range) flags |= 1;
+    else if (dup) flags |= 2;
+    ok[0] = in_range && !dup;
+  } else {
+    tok = item;
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) ids[j] = (j < k) ? idx[static_cast<size_t>(t) * k + j] : -1;
+    for (int j = 0; j < KMAX; ++j) {
+      pos[j] = static_cast<int64_t>(item) * k + j;
+      ids[j] = (j < k) ? idx[pos[j]] : -1;
+    }
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    ok[j] = false;
-    if (j < k) {
-      const bool in_range = static_cast<unsigned>(ids[j]) < static_cast<unsigned>(e);
-      bool dup = false;
+    for (int j = 0; j < KMAX; ++j) {
+      ok[j] = false;
+      if (j < k) {
+        const bool in_range = static_cast<unsigned>(ids[j]) < static_cast<unsigned>(e);
+        bool dup = false;
 #pragma unroll
-      for (int q = 0; q < j; ++q) dup |= (ids[q] == ids[j]);
-      if (!in_range) flags |= 1;
-      else if (dup) flags |= 2;
-      ok[j] = in_range && !dup;
+        for (int q = 0; q < j; ++q) dup |= (ids[q] == ids[j]);
+        if (!in_range) flags |= 1;
+        else if (dup) flags |= 2;
+        ok[j] = in_range && !dup;
+      }
     }
   }
   return flags;
 }
 
-template <int KMAX>
+template <int KMAX, bool RM>
 __global__ __launch_bounds__(kTileTokens) void layout_count_kernel(
-    const int32_t* __restrict__ idx, int s, int e, int k, int32_t* __restrict__ tile_counts,
-    uint64_t* __restrict__ tile_checksum, int32_t* __restrict__ tile_flags) {
+    const int32_t* __restrict__ idx, int s, int e, int k, int items,
+    int32_t* __restrict__ tile_counts, uint64_t* __restrict__ tile_checksum,
+    int32_t* __restrict__ tile_flags) {
   extern __shared__ int32_t hist[];  // [e]
   __shared__ uint64_t part_sum[kTileTokens / kWave];
   __shared__ int32_t part_flags[kTileTokens / kWave];
   for (int i = threadIdx.x; i < e; i += kTileTokens) hist[i] = 0;
   __syncthreads();
 
-  const int t = blockIdx.x * kTileTokens + threadIdx.x;
+  const int item = blockIdx.x * kTileTokens + threadIdx.x;
   uint64_t cks = 0;
   int flags = 0;
-  if (t < s) {
-    int ids[KMAX];
+  if (item < items) {
+    int tok, ids[KMAX];
     bool ok[KMAX];
-    flags = load_routes<KMAX>(idx, t, k, e, ids, ok);
+    int64_t pos[KMAX];
+    flags = load_item<KMAX, RM>(idx, item, s, k, e, tok, ids, ok, pos);
+    const int nr = RM ? 1 : k;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
-      if (j < k) {
-        const uint64_t pos = static_cast<uint64_t>(t) * k + j + 1;
-        cks += static_cast<uint64_t>(static_cast<int64_t>(ids[j]) + 1) * pos;
+      if (j < nr) {
+        cks += static_cast<uint64_t>(static_cast<int64_t>(ids[j]) + 1) * static_cast<uint64_t>(pos[j] + 1);
         if (ok[j]) atomicAdd(&hist[ids[j]], 1);
       }
     }
@@ -134,15 +166,15 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t* __restrict__ va
   return total;
 }
 
-template <int KMAX>
+template <int KMAX, bool RM>
 __global__ __launch_bounds__(kTileTokens) void layout_place_kernel(
-    const int32_t* __restrict__ idx, int s, int e, int k, int capacity, int32_t rows, int ntiles,
-    const int32_t* __restrict__ tile_counts, const uint64_t* __restrict__ tile_checksum,
-    const int32_t* __restrict__ tile_flags, int32_t* __restrict__ counts,
-    int32_t* __restrict__ kept_out, int32_t* __restrict__ offsets_out, uint64_t* __restrict__ checksum,
-    int32_t* __restrict__ flags, int32_t* __restrict__ dst, int32_t* __restrict__ src,
-    int32_t* __restrict__ route_idx) {
-  // LDS: per expert tile base, total and segment offset, then the per-wave lane masks
+    const int32_t* __restrict__ idx, int s, int e, int k, int items, int capacity, int pad,
+    int32_t rows, int ntiles, const int32_t* __restrict__ tile_counts,
+    const uint64_t* __restrict__ tile_checksum, const int32_t* __restrict__ tile_flags,
+    int32_t* __restrict__ counts, int32_t* __restrict__ kept_out, int32_t* __restrict__ offsets_out,
+    uint64_t* __restrict__ checksum, int32_t* __restrict__ flags, int32_t* __restrict__ dst,
+    int32_t* __restrict__ src, int32_t* __restrict__ route_idx) {
+  // LDS: the per-wave lane masks, then per expert tile base, total and segment offset
   extern __shared__ unsigned long long lds[];
   constexpr int kWaves = kTileTokens / kWave;
   __shared__ int32_t wave_tot[kWaves];
@@ -154,7 +186,7 @@ __global__ __launch_bounds__(kTileTokens) void layout_place_kernel(
   int32_t* off_s = total_s + e;                                            // [e + 1]
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   const int tile = blockIdx.x;
-  const int my_tile = tile < ntiles ? tile : ntiles;  // workgroups past the tiles: pad only
+  const int my_tile = tile < ntiles ? tile : ntiles;  // workgroups past the tiles: padding only
 
   // per expert: sum over earlier tiles and over all tiles
   for (int x = threadIdx.x; x < e; x += kTileTokens) {
@@ -176,7 +208,7 @@ __global__ __launch_bounds__(kTileTokens) void layout_place_kernel(
     }
     base_s[x] = before;
     total_s[x] = all;
-    off_s[x] = capacity > 0 ? capacity : all;  // segment sizes, scanned below
+    off_s[x] = capacity > 0 ? capacity : (all + pad - 1) / pad * pad;  // segment sizes
   }
   __syncthreads();
   const int32_t seg_total = block_exclusive_scan(off_s, e, wave_tot);
@@ -220,27 +252,30 @@ __global__ __launch_bounds__(kTileTokens) void layout_place_kernel(
     for (int i = threadIdx.x; i < kWaves * e; i += kTileTokens) lane_masks[i] = 0ull;
     __syncthreads();
 
-    const int t = tile * kTileTokens + threadIdx.x;
-    int ids[KMAX];
+    const int item = tile * kTileTokens + threadIdx.x;
+    const int nr = RM ? 1 : k;
+    int tok = 0, ids[KMAX];
     bool ok[KMAX];
+    int64_t pos[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       ids[j] = -1;
       ok[j] = false;
+      pos[j] = 0;
     }
-    if (t < s) {
-      load_routes<KMAX>(idx, t, k, e, ids, ok);
+    if (item < items) {
+      load_item<KMAX, RM>(idx, item, s, k, e, tok, ids, ok, pos);
 #pragma unroll
       for (int j = 0; j < KMAX; ++j)
         if (ok[j]) atomicOr(&lane_masks[wv * e + ids[j]], 1ull << lane);
     }
     __syncthreads();
 
-    if (t < s) {
+    if (item < items) {
       const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) {
-        if (j < k) {
+        if (j < nr) {
           int d = -1;
           if (ok[j]) {
             const int x = ids[j];
@@ -252,60 +287,59 @@ __global__ __launch_bounds__(kTileTokens) void layout_place_kernel(
             else
               d = off_s[x] + r;
           }
-          const size_t o = static_cast<size_t>(t) * k + j;
-          dst[o] = d;
-          route_idx[o] = ids[j];
-          if (d >= 0) src[d] = t;
+          dst[pos[j]] = d;
+          route_idx[pos[j]] = ids[j];
+          if (d >= 0) src[d] = tok;
         }
       }
     }
   }
 
-  // rows no route fills: the tail of each capacity segment, or the dropless rows past
-  // the last valid route
-  const int32_t begin = capacity > 0 ? 0 : off_s[e];
-  const int32_t stride = gridDim.x * kTileTokens;
-  for (int32_t r = begin + blockIdx.x * kTileTokens + threadIdx.x; r < rows; r += stride) {
-    if (capacity > 0) {
-      const int32_t x = r / capacity;
+  // rows no route fills: the tail of each expert segment (capacity or pad rows), and
+  // the rows past the last segment. Workgroup g takes segments x = g, g + grid, ...
+  // (segment e is the tail), its threads striding over the segment's rows.
+  for (int x = blockIdx.x; x <= e; x += gridDim.x) {
+    int32_t r0, r1;
+    if (x < e) {
       const int32_t c = total_s[x];
-      if (r - x * capacity >= (c < capacity ? c : capacity)) src[r] = -1;
+      r0 = off_s[x] + (capacity > 0 ? (c < capacity ? c : capacity) : c);
+      r1 = capacity > 0 ? off_s[x] + capacity : off_s[x + 1];
     } else {
-      src[r] = -1;
+      r0 = off_s[e];
+      r1 = rows;
     }
+    for (int32_t r = r0 + threadIdx.x; r < r1; r += kTileTokens) src[r] = -1;
   }
 }
 
-template <int KMAX>
+template <int KMAX, bool RM>
 static hipError_t launch_layout_k(const int32_t* idx, const LayoutView& L, hipStream_t stream) {
   const int ntiles = L.ntiles;
+  const int items = RM ? L.s * L.k : L.s;
   if (ntiles > 0) {
-    layout_count_kernel<KMAX><<<ntiles, kTileTokens, L.e * sizeof(int32_t), stream>>>(
-        idx, L.s, L.e, L.k, L.tile_counts, L.tile_checksum, L.tile_flags);
+    layout_count_kernel<KMAX, RM><<<ntiles, kTileTokens, L.e * sizeof(int32_t), stream>>>(
+        idx, L.s, L.e, L.k, items, L.tile_counts, L.tile_checksum, L.tile_flags);
   }
-  int grid = ntiles;
-  if (L.capacity > 0) {
-    const int64_t pad_blocks = (L.rows + kTileTokens - 1) / kTileTokens;
-    const int64_t want = pad_blocks < 1024 ? pad_blocks : 1024;
-    if (grid < want) grid = static_cast<int>(want);
-  }
-  if (grid < 1) grid = 1;
+  int grid = ntiles < 1 ? 1 : ntiles;
+  if ((L.capacity > 0 || L.pad_multiple > 1) && grid < L.e + 1)
+    grid = L.e + 1 < 1024 ? L.e + 1 : 1024;  // one workgroup per padded segment
   const size_t lds = static_cast<size_t>(kTileTokens / kWave) * L.e * sizeof(unsigned long long) +
                      (3 * static_cast<size_t>(L.e) + 1) * sizeof(int32_t);
-  layout_place_kernel<KMAX><<<grid, kTileTokens, lds, stream>>>(
-      idx, L.s, L.e, L.k, L.capacity, static_cast<int32_t>(L.rows), ntiles, L.tile_counts,
-      L.tile_checksum, L.tile_flags, L.counts, L.kept, L.offsets, L.checksum, L.flags, L.dst,
-      L.src, L.route_idx);
+  layout_place_kernel<KMAX, RM><<<grid, kTileTokens, lds, stream>>>(
+      idx, L.s, L.e, L.k, items, L.capacity, L.pad_multiple, static_cast<int32_t>(L.rows), ntiles,
+      L.tile_counts, L.tile_checksum, L.tile_flags, L.counts, L.kept, L.offsets, L.checksum,
+      L.flags, L.dst, L.src, L.route_idx);
   return hipGetLastError();
 }
 
 hipError_t launch_layout(const int32_t* idx, const LayoutView& L, hipStream_t stream) {
+  if (L.route_major) return launch_layout_k<1, true>(idx, L, stream);
   switch (route_bound(L.k)) {
-    case 1: return launch_layout_k<1>(idx, L, stream);
-    case 2: return launch_layout_k<2>(idx, L, stream);
-    case 4: return launch_layout_k<4>(idx, L, stream);
-    case 8: return launch_layout_k<8>(idx, L, stream);
-    default: return launch_layout_k<16>(idx, L, stream);
+    case 1: return launch_layout_k<1, false>(idx, L, stream);
+    case 2: return launch_layout_k<2, false>(idx, L, stream);
+    case 4: return launch_layout_k<4, false>(idx, L, stream);
+    case 8: return launch_layout_k<8, false>(idx, L, stream);
+    default: return launch_layout_k<16, false>(idx, L, stream);
   }
 }
 

@@ -28,9 +28,15 @@
 //                     fixed order (the gradient of a combine is a dispatch, plus the
 //                     weights' gradient of PR 8213's review-fix commit).
 //
-// Rows that no route points at (capacity padding, or rows past the last valid route)
-// are zero-filled by extra workgroups after the token workgroups, in the kernels that
-// write [rows, m] buffers. No floating-point atomics: results are deterministic.
+//   weighted dispatch the combine backward's scatter without the dot: out[dst] = w * x
+//                     (the weights applied before the experts; PR 8213's score_apply).
+//   its backward      the weighted combine of grad_out, plus grad_w = <grad_out[dst], x>
+//                     accumulated like the combine backward's dot.
+//
+// Rows that no route points at (the tail of each expert segment: capacity or pad rows,
+// and rows past the last segment) are zero-filled by extra workgroups after the token
+// workgroups, in the kernels that write [rows, m] buffers. No floating-point atomics:
+// results are deterministic.
 #include "internal.h"
 #include "moe_device.h"
 
@@ -62,25 +68,27 @@ __device__ __forceinline__ int64_t rotated_group(int64_t gi, int64_t t, int64_t 
   return g >= ng ? g - ng : g;
 }
 
-// Workgroups past the s token workgroups zero the rows that no placed route fills.
+// Workgroups past the s token workgroups zero the rows that no placed route fills:
+// segment x in [0, e) has rows [offsets[x] + kept[x], offsets[x+1]) unfilled, and
+// "segment" e is the tail [offsets[e], rows). Each (segment, sub-stride) pair is one
+// work item, so a few long segments still spread over many waves.
 template <bool NTS>
 __device__ __forceinline__ void zero_unfilled_rows(chunk_t* __restrict__ out, int64_t rc, int s,
-                                                   int capacity, int e, int32_t rows,
+                                                   int e, int32_t rows,
                                                    const int32_t* __restrict__ kept,
                                                    const int32_t* __restrict__ offsets) {
   const int lane = lane_id();
   const int wpb = blockDim.x >> 6;
   const int32_t wave = (blockIdx.x - s) * wpb + wave_in_block();
   const int32_t nwaves = (gridDim.x - s) * wpb;
-  const int32_t begin = capacity > 0 ? 0 : offsets[e];
+  const int32_t nseg = e + 1;
+  const int32_t R = nwaves > nseg ? nwaves / nseg : 1;
   const chunk_t z = {0u, 0u, 0u, 0u};
-  for (int32_t r = begin + wave; r < rows; r += nwaves) {
-    bool pad = true;
-    if (capacity > 0) {
-      const int32_t x = r / capacity;
-      pad = (r - x * capacity) >= kept[x];
-    }
-    if (pad) {
+  for (int32_t item = wave; item < nseg * R; item += nwaves) {
+    const int32_t x = item % nseg, sub = item / nseg;
+    const int32_t r0 = x < e ? offsets[x] + kept[x] : offsets[e];
+    const int32_t r1 = x < e ? offsets[x + 1] : rows;
+    for (int32_t r = r0 + sub; r < r1; r += R) {
       chunk_t* o = out + static_cast<size_t>(r) * rc;
       for (int64_t c = lane; c < rc; c += kWave) store_chunk<NTS>(o + c, z);
     }
@@ -106,7 +114,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_kernel(
     int capacity, int e, int32_t rows, const int32_t* __restrict__ kept,
     const int32_t* __restrict__ offsets) {
   if (static_cast<int>(blockIdx.x) >= s) {
-    zero_unfilled_rows<true>(out, sp.rc, s, capacity, e, rows, kept, offsets);
+    zero_unfilled_rows<true>(out, sp.rc, s, e, rows, kept, offsets);
     return;
   }
   const int lane = lane_id();
@@ -143,16 +151,47 @@ __global__ __launch_bounds__(kBlock) void dispatch_kernel(
 }
 
 // ---------------------------------------------------------------------------------
-// combine (weighted) and dispatch backward (unweighted): nontemporal loads of the
-// k rows, one store per chunk
+// combine (weighted), dispatch backward (unweighted) and the weighted dispatch's
+// backward (weighted, plus the dot of each row with the token's own row): nontemporal
+// loads of the k rows, one store per chunk
 
-template <int DT, int KMAX, bool WEIGHTED, int U>
+// Per-route float64 partials of one wave, summed across the workgroup's waves through
+// LDS in wave order; lane j < k of wave 0 writes grad_w[t, j] (0 for a dropped route).
+template <int KMAX>
+__device__ __forceinline__ void reduce_route_dots(double (&part)[KMAX], const int (&d)[KMAX],
+                                                  int t, int k, int wpb, float* __restrict__ gw,
+                                                  double (*wave_part)[KMAX]) {
+  const int lane = lane_id();
+  const int wv = wave_in_block();
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k) {
+      const double tot = wave_sum(part[j]);
+      if (lane == 0) wave_part[wv][j] = tot;
+    }
+  }
+  __syncthreads();
+  if (wv == 0 && lane < k) {
+    double tot = 0.0;
+    for (int q = 0; q < wpb; ++q) tot += wave_part[q][lane];
+    int dj = -1;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (j == lane) dj = d[j];
+    gw[static_cast<size_t>(t) * k + lane] = dj >= 0 ? static_cast<float>(tot) : 0.0f;
+  }
+}
+
+template <int DT, int KMAX, bool WEIGHTED, bool WITH_DOT, int U>
 __global__ __launch_bounds__(kBlock) void combine_kernel(const chunk_t* __restrict__ rows_in,
                                                          const float* __restrict__ w,
                                                          const int32_t* __restrict__ dst,
                                                          int s, int k, RowSplit sp,
-                                                         chunk_t* __restrict__ y) {
+                                                         chunk_t* __restrict__ y,
+                                                         const chunk_t* __restrict__ xdot,
+                                                         float* __restrict__ gw) {
   constexpr int N = ChunkElems<DT>::value;
+  __shared__ double wave_part[kWavesPerBlock][KMAX];
   const int lane = lane_id();
   const int wv = wave_in_block();
   const int t = blockIdx.x;
@@ -160,11 +199,15 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const chunk_t* __restri
   int d[KMAX];
   load_dst<KMAX>(dst, t, k, d);
   float wt[KMAX];
+  double part[KMAX];
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j)
+  for (int j = 0; j < KMAX; ++j) {
     wt[j] = (WEIGHTED && j < k) ? w[static_cast<size_t>(t) * k + j] : 1.0f;
+    part[j] = 0.0;
+  }
 
   chunk_t* yr = y + static_cast<size_t>(t) * sp.rc;
+  const chunk_t* xr = WITH_DOT ? xdot + static_cast<size_t>(t) * sp.rc : nullptr;
   for (int64_t gi = wv; gi < sp.ng; gi += sp.wpb) {
     const int64_t c0 = rotated_group(gi, t, sp.ng) * (kWave * U) + lane;
     chunk_t v[U][KMAX];
@@ -180,6 +223,8 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const chunk_t* __restri
     for (int u = 0; u < U; ++u) {
       const int64_t c = c0 + u * kWave;
       if (c < sp.rc) {
+        float xs[N];
+        if constexpr (WITH_DOT) unpack<DT>(load_chunk<false>(xr + c), xs);
         float acc[N];
 #pragma unroll
         for (int n = 0; n < N; ++n) acc[n] = 0.0f;
@@ -189,29 +234,36 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const chunk_t* __restri
             float f[N];
             unpack<DT>(v[u][j], f);
 #pragma unroll
-            for (int n = 0; n < N; ++n)
+            for (int n = 0; n < N; ++n) {
               acc[n] = WEIGHTED ? __fadd_rn(acc[n], __fmul_rn(wt[j], f[n])) : __fadd_rn(acc[n], f[n]);
+              if constexpr (WITH_DOT)
+                part[j] = fma(static_cast<double>(xs[n]), static_cast<double>(f[n]), part[j]);
+            }
           }
         }
         yr[c] = pack<DT>(acc);
       }
     }
   }
+  if constexpr (WITH_DOT) reduce_route_dots<KMAX>(part, d, t, k, sp.wpb, gw, wave_part);
 }
 
 // ---------------------------------------------------------------------------------
-// combine backward: grad_E rows and grad_w
+// weighted scatter: out[dst[t,j]] = w[t,j] * in[t] for every placed route, and with
+// WITH_DOT also grad_w[t,j] = <in[t], E[dst[t,j]]>. The combine backward is the scatter
+// of grad_y with the dot against the expert rows; the weighted dispatch is the scatter
+// of x without it.
 
-template <int DT, int KMAX, int U>
-__global__ __launch_bounds__(kBlock) void combine_backward_kernel(
-    const chunk_t* __restrict__ gy, const chunk_t* __restrict__ E, const float* __restrict__ w,
-    const int32_t* __restrict__ dst, int s, int k, RowSplit sp, chunk_t* __restrict__ gE,
-    float* __restrict__ gw, int capacity, int e, int32_t rows,
-    const int32_t* __restrict__ kept, const int32_t* __restrict__ offsets) {
+template <int DT, int KMAX, bool WITH_DOT, int U>
+__global__ __launch_bounds__(kBlock) void weighted_scatter_kernel(
+    const chunk_t* __restrict__ in, const chunk_t* __restrict__ E, const float* __restrict__ w,
+    const int32_t* __restrict__ dst, int s, int k, RowSplit sp, chunk_t* __restrict__ out,
+    float* __restrict__ gw, int e, int32_t rows, const int32_t* __restrict__ kept,
+    const int32_t* __restrict__ offsets) {
   constexpr int N = ChunkElems<DT>::value;
   __shared__ double wave_part[kWavesPerBlock][KMAX];
   if (static_cast<int>(blockIdx.x) >= s) {
-    zero_unfilled_rows<true>(gE, sp.rc, s, capacity, e, rows, kept, offsets);
+    zero_unfilled_rows<true>(out, sp.rc, s, e, rows, kept, offsets);
     return;
   }
   const int lane = lane_id();
@@ -226,7 +278,7 @@ __global__ __launch_bounds__(kBlock) void combine_backward_kernel(
     wt[j] = (j < k) ? w[static_cast<size_t>(t) * k + j] : 0.0f;
     part[j] = 0.0;
   }
-  const chunk_t* gr = gy + static_cast<size_t>(t) * sp.rc;
+  const chunk_t* ir = in + static_cast<size_t>(t) * sp.rc;
   for (int64_t gi = wv; gi < sp.ng; gi += sp.wpb) {
     const int64_t c0 = rotated_group(gi, t, sp.ng) * (kWave * U) + lane;
 #pragma unroll
@@ -234,45 +286,35 @@ __global__ __launch_bounds__(kBlock) void combine_backward_kernel(
       const int64_t c = c0 + u * kWave;
       if (c < sp.rc) {
         float g[N];
-        unpack<DT>(load_chunk<false>(gr + c), g);  // measured faster than a nontemporal load
+        // the token's own row: normal loads (measured faster than nontemporal ones)
+        unpack<DT>(load_chunk<false>(ir + c), g);
         chunk_t v[KMAX];
+        if constexpr (WITH_DOT) {
 #pragma unroll
-        for (int j = 0; j < KMAX; ++j)
-          if (d[j] >= 0) v[j] = load_chunk<true>(E + static_cast<size_t>(d[j]) * sp.rc + c);
+          for (int j = 0; j < KMAX; ++j)
+            if (d[j] >= 0) v[j] = load_chunk<true>(E + static_cast<size_t>(d[j]) * sp.rc + c);
+        }
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
           if (d[j] >= 0) {
-            float f[N], o[N];
-            unpack<DT>(v[j], f);
+            float o[N];
+            if constexpr (WITH_DOT) {
+              float f[N];
+              unpack<DT>(v[j], f);
 #pragma unroll
-            for (int n = 0; n < N; ++n) {
-              // float32 x float32 is exact in float64, so the fma rounds only the sum
-              part[j] = fma(static_cast<double>(g[n]), static_cast<double>(f[n]), part[j]);
-              o[n] = __fmul_rn(wt[j], g[n]);
+              for (int n = 0; n < N; ++n)
+                // float32 x float32 is exact in float64, so the fma rounds only the sum
+                part[j] = fma(static_cast<double>(g[n]), static_cast<double>(f[n]), part[j]);
             }
-            store_chunk<true>(gE + static_cast<size_t>(d[j]) * sp.rc + c, pack<DT>(o));
+#pragma unroll
+            for (int n = 0; n < N; ++n) o[n] = __fmul_rn(wt[j], g[n]);
+            store_chunk<true>(out + static_cast<size_t>(d[j]) * sp.rc + c, pack<DT>(o));
           }
         }
       }
     }
   }
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    if (j < k) {
-      const double tot = wave_sum(part[j]);
-      if (lane == 0) wave_part[wv][j] = tot;
-    }
-  }
-  __syncthreads();
-  if (wv == 0 && lane < k) {
-    double tot = 0.0;
-    for (int q = 0; q < sp.wpb; ++q) tot += wave_part[q][lane];
-    int dj = -1;
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-      if (j == lane) dj = d[j];
-    gw[static_cast<size_t>(t) * k + lane] = dj >= 0 ? static_cast<float>(tot) : 0.0f;
-  }
+  if constexpr (WITH_DOT) reduce_route_dots<KMAX>(part, d, t, k, sp.wpb, gw, wave_part);
 }
 
 // ---------------------------------------------------------------------------------
@@ -290,14 +332,15 @@ static RowSplit make_split(int64_t rc, int U) {
   return sp;
 }
 
-// Workgroups that zero unfilled rows: enough for every capacity row; a few in
-// dropless mode, where only flagged-invalid routes leave rows unfilled.
+// Workgroups that zero unfilled rows: enough for every capacity row or pad row; a few
+// otherwise, where only flagged-invalid routes leave rows unfilled.
 static int pad_blocks(const LayoutView& L, int wpb) {
-  if (L.capacity > 0) {
-    int64_t b = (L.rows + 8 * wpb - 1) / (8 * wpb);
-    return static_cast<int>(b < 4096 ? (b < 1 ? 1 : b) : 4096);
-  }
-  return L.s > 0 ? 16 : 0;
+  int64_t want = 16;
+  if (L.capacity > 0) want = (L.rows + 8 * wpb - 1) / (8 * wpb);
+  else if (L.pad_multiple > 1) want = (static_cast<int64_t>(L.e) * (L.pad_multiple - 1) + 8 * wpb - 1) / (8 * wpb);
+  if (want < 16) want = 16;
+  if (want > 4096) want = 4096;
+  return L.s > 0 || L.rows > 0 ? static_cast<int>(want) : 0;
 }
 
 template <int KMAX, int U>
@@ -332,74 +375,100 @@ hipError_t launch_dispatch(const LayoutView& L, const int32_t* verify_idx, const
   return hipGetLastError();
 }
 
+// mode: 0 weighted combine, 1 unweighted sum, 2 weighted combine plus dots with xdot
 template <int DT, int KMAX>
 static void combine_k(const LayoutView& L, const void* in, const float* w, const RowSplit& sp,
-                      void* y, hipStream_t stream) {
-  if (w != nullptr)
-    combine_kernel<DT, KMAX, true, 1><<<L.s, sp.wpb * kWave, 0, stream>>>(
-        static_cast<const chunk_t*>(in), w, L.dst, L.s, L.k, sp, static_cast<chunk_t*>(y));
+                      void* y, const void* xdot, float* gw, int mode, hipStream_t stream) {
+  const chunk_t* src = static_cast<const chunk_t*>(in);
+  chunk_t* dsty = static_cast<chunk_t*>(y);
+  const chunk_t* xd = static_cast<const chunk_t*>(xdot);
+  if (mode == 0)
+    combine_kernel<DT, KMAX, true, false, 1><<<L.s, sp.wpb * kWave, 0, stream>>>(src, w, L.dst, L.s, L.k, sp, dsty, nullptr, nullptr);
+  else if (mode == 1)
+    combine_kernel<DT, KMAX, false, false, 1><<<L.s, sp.wpb * kWave, 0, stream>>>(src, nullptr, L.dst, L.s, L.k, sp, dsty, nullptr, nullptr);
   else
-    combine_kernel<DT, KMAX, false, 1><<<L.s, sp.wpb * kWave, 0, stream>>>(
-        static_cast<const chunk_t*>(in), nullptr, L.dst, L.s, L.k, sp, static_cast<chunk_t*>(y));
+    combine_kernel<DT, KMAX, true, true, 1><<<L.s, sp.wpb * kWave, 0, stream>>>(src, w, L.dst, L.s, L.k, sp, dsty, xd, gw);
 }
 
 template <int DT>
 static void combine_dt(const LayoutView& L, const void* in, const float* w, const RowSplit& sp,
-                       void* y, hipStream_t stream) {
+                       void* y, const void* xdot, float* gw, int mode, hipStream_t stream) {
   switch (route_bound(L.k)) {
-    case 1: combine_k<DT, 1>(L, in, w, sp, y, stream); break;
-    case 2: combine_k<DT, 2>(L, in, w, sp, y, stream); break;
-    case 4: combine_k<DT, 4>(L, in, w, sp, y, stream); break;
-    case 8: combine_k<DT, 8>(L, in, w, sp, y, stream); break;
-    default: combine_k<DT, 16>(L, in, w, sp, y, stream); break;
+    case 1: combine_k<DT, 1>(L, in, w, sp, y, xdot, gw, mode, stream); break;
+    case 2: combine_k<DT, 2>(L, in, w, sp, y, xdot, gw, mode, stream); break;
+    case 4: combine_k<DT, 4>(L, in, w, sp, y, xdot, gw, mode, stream); break;
+    case 8: combine_k<DT, 8>(L, in, w, sp, y, xdot, gw, mode, stream); break;
+    default: combine_k<DT, 16>(L, in, w, sp, y, xdot, gw, mode, stream); break;
   }
 }
 
-hipError_t launch_combine(const LayoutView& L, const void* in, const float* w, int64_t rc,
-                          int dtype, void* y, hipStream_t stream) {
+static hipError_t combine_any(const LayoutView& L, const void* in, const float* w, int64_t rc,
+                              int dtype, void* y, const void* xdot, float* gw, int mode,
+                              hipStream_t stream) {
   if (L.s == 0) return hipSuccess;
   const RowSplit sp = make_split(rc, 1);
   switch (dtype) {
-    case kF32: combine_dt<kF32>(L, in, w, sp, y, stream); break;
-    case kBF16: combine_dt<kBF16>(L, in, w, sp, y, stream); break;
-    default: combine_dt<kF16>(L, in, w, sp, y, stream); break;
+    case kF32: combine_dt<kF32>(L, in, w, sp, y, xdot, gw, mode, stream); break;
+    case kBF16: combine_dt<kBF16>(L, in, w, sp, y, xdot, gw, mode, stream); break;
+    default: combine_dt<kF16>(L, in, w, sp, y, xdot, gw, mode, stream); break;
   }
   return hipGetLastError();
 }
 
-template <int DT, int KMAX>
-static void combine_bwd_k(const LayoutView& L, const void* gy, const void* E, const float* w,
-                          const RowSplit& sp, void* gE, float* gw, hipStream_t stream) {
-  const int grid = L.s + pad_blocks(L, sp.wpb);
-  if (grid == 0) return;
-  combine_backward_kernel<DT, KMAX, 1><<<grid, sp.wpb * kWave, 0, stream>>>(
-      static_cast<const chunk_t*>(gy), static_cast<const chunk_t*>(E), w, L.dst, L.s, L.k, sp,
-      static_cast<chunk_t*>(gE), gw, L.capacity, L.e, static_cast<int32_t>(L.rows), L.kept,
-      L.offsets);
+hipError_t launch_combine(const LayoutView& L, const void* in, const float* w, int64_t rc,
+                          int dtype, void* y, hipStream_t stream) {
+  return combine_any(L, in, w, rc, dtype, y, nullptr, nullptr, w != nullptr ? 0 : 1, stream);
 }
 
-template <int DT>
-static void combine_bwd_dt(const LayoutView& L, const void* gy, const void* E, const float* w,
-                           const RowSplit& sp, void* gE, float* gw, hipStream_t stream) {
+hipError_t launch_dispatch_weighted_backward(const LayoutView& L, const void* grad_out,
+                                             const void* x, const float* w, int64_t rc,
+                                             int dtype, void* gx, float* gw, hipStream_t stream) {
+  return combine_any(L, grad_out, w, rc, dtype, gx, x, gw, 2, stream);
+}
+
+template <int DT, int KMAX, bool WITH_DOT>
+static void scatter_k(const LayoutView& L, const void* in, const void* E, const float* w,
+                      const RowSplit& sp, void* out, float* gw, hipStream_t stream) {
+  const int grid = L.s + pad_blocks(L, sp.wpb);
+  if (grid == 0) return;
+  weighted_scatter_kernel<DT, KMAX, WITH_DOT, 1><<<grid, sp.wpb * kWave, 0, stream>>>(
+      static_cast<const chunk_t*>(in), static_cast<const chunk_t*>(E), w, L.dst, L.s, L.k, sp,
+      static_cast<chunk_t*>(out), gw, L.e, static_cast<int32_t>(L.rows), L.kept, L.offsets);
+}
+
+template <int DT, bool WITH_DOT>
+static void scatter_dt(const LayoutView& L, const void* in, const void* E, const float* w,
+                       const RowSplit& sp, void* out, float* gw, hipStream_t stream) {
   switch (route_bound(L.k)) {
-    case 1: combine_bwd_k<DT, 1>(L, gy, E, w, sp, gE, gw, stream); break;
-    case 2: combine_bwd_k<DT, 2>(L, gy, E, w, sp, gE, gw, stream); break;
-    case 4: combine_bwd_k<DT, 4>(L, gy, E, w, sp, gE, gw, stream); break;
-    case 8: combine_bwd_k<DT, 8>(L, gy, E, w, sp, gE, gw, stream); break;
-    default: combine_bwd_k<DT, 16>(L, gy, E, w, sp, gE, gw, stream); break;
+    case 1: scatter_k<DT, 1, WITH_DOT>(L, in, E, w, sp, out, gw, stream); break;
+    case 2: scatter_k<DT, 2, WITH_DOT>(L, in, E, w, sp, out, gw, stream); break;
+    case 4: scatter_k<DT, 4, WITH_DOT>(L, in, E, w, sp, out, gw, stream); break;
+    case 8: scatter_k<DT, 8, WITH_DOT>(L, in, E, w, sp, out, gw, stream); break;
+    default: scatter_k<DT, 16, WITH_DOT>(L, in, E, w, sp, out, gw, stream); break;
   }
+}
+
+template <bool WITH_DOT>
+static hipError_t scatter_any(const LayoutView& L, const void* in, const void* E, const float* w,
+                              int64_t rc, int dtype, void* out, float* gw, hipStream_t stream) {
+  const RowSplit sp = make_split(rc, 1);
+  switch (dtype) {
+    case kF32: scatter_dt<kF32, WITH_DOT>(L, in, E, w, sp, out, gw, stream); break;
+    case kBF16: scatter_dt<kBF16, WITH_DOT>(L, in, E, w, sp, out, gw, stream); break;
+    default: scatter_dt<kF16, WITH_DOT>(L, in, E, w, sp, out, gw, stream); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_combine_backward(const LayoutView& L, const void* gy, const void* E,
                                    const float* w, int64_t rc, int dtype, void* gE, float* gw,
                                    hipStream_t stream) {
-  const RowSplit sp = make_split(rc, 1);
-  switch (dtype) {
-    case kF32: combine_bwd_dt<kF32>(L, gy, E, w, sp, gE, gw, stream); break;
-    case kBF16: combine_bwd_dt<kBF16>(L, gy, E, w, sp, gE, gw, stream); break;
-    default: combine_bwd_dt<kF16>(L, gy, E, w, sp, gE, gw, stream); break;
-  }
-  return hipGetLastError();
+  return scatter_any<true>(L, gy, E, w, rc, dtype, gE, gw, stream);
+}
+
+hipError_t launch_dispatch_weighted(const LayoutView& L, const void* x, const float* w,
+                                    int64_t rc, int dtype, void* out, hipStream_t stream) {
+  return scatter_any<false>(L, x, nullptr, w, rc, dtype, out, nullptr, stream);
 }
 
 }  // namespace moe

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -94,6 +94,9 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_F16 = 2 } moe_dtype_t;
  *                 holding its tokens in token order; offsets[e] = number of valid routes
  *                 (= s*k unless routes were flagged invalid); rows from offsets[e] on are
  *                 zero padding. For a grouped GEMM, counts[x] = offsets[x+1]-offsets[x].
+ * With a pad multiple P > 1 (dropless only), each segment [offsets[x], offsets[x+1]) is
+ * counts[x] rounded up to a multiple of P rows, the rows after counts[x] being zero
+ * padding, and rows = s*k + e*(P-1) (an upper bound: offsets[e] is the rows used).
  * `rows` is known on the host, so sizing the next buffer needs no device read
  * ([DS-8213] review-fix commit on the row count taken from the handle).
  */
@@ -101,6 +104,8 @@ typedef struct moe_layout {
   uint64_t magic;     /* set by moe_dispatch_layout */
   int32_t s, e, k;    /* tokens, experts, routes per token */
   int32_t capacity;   /* > 0: capacity per expert; 0: dropless */
+  int32_t route_major;  /* slot order (moe_layout_options_t) */
+  int32_t pad_multiple; /* dropless segment rounding (moe_layout_options_t) */
   int64_t rows;       /* buffer rows (host-known) */
   int32_t* counts;    /* [e]   valid routes per expert, before the capacity drop */
   int32_t* kept;      /* [e]   routes placed per expert: min(counts, capacity) */
@@ -114,6 +119,26 @@ typedef struct moe_layout {
   void* workspace;
   size_t workspace_bytes;
 } moe_layout_t;
+
+/*
+ * Layout options (moe_dispatch_layout_ex). A NULL options pointer means the defaults
+ * {route_major = 0, pad_multiple = 1}, which is what moe_dispatch_layout uses.
+ *   route_major   0: a route's slot counts the earlier tokens that chose its expert
+ *                    (token order over each token's routes).
+ *                 1: slots are handed to every token's first route, then every token's
+ *                    second route, ... so first choices win capacity before second ones
+ *                    ([DS-8195] review comment on fast_cumsum_sub_one: per-route masks
+ *                    mask1, mask2, ..., later routes offset by the earlier routes'
+ *                    counts).
+ *   pad_multiple  >= 1; dropless only (must be 1 with a capacity): each expert segment is
+ *                 rounded up to a multiple of this many rows, for grouped GEMMs with
+ *                 fixed row tiles ([AM-3684] section 1: a pad multiple fixed at
+ *                 construction).
+ */
+typedef struct moe_layout_options {
+  int32_t route_major;
+  int32_t pad_multiple;
+} moe_layout_options_t;
 
 /* ABI version of the loaded library (MOE_ABI_VERSION it was built with). */
 int moe_abi_version(void);
@@ -129,6 +154,10 @@ const char* moe_status_string(moe_status_t status);
  * invalid or unsupported. The workspace must be 256-byte aligned. Host only.
  */
 size_t moe_layout_workspace_bytes(int32_t s, int32_t e, int32_t k, int32_t capacity);
+
+/* Workspace bytes for a layout built with options (NULL = defaults); 0 if invalid. */
+size_t moe_layout_workspace_bytes_ex(int32_t s, int32_t e, int32_t k, int32_t capacity,
+                                     const moe_layout_options_t* options);
 
 /*
  * (1) Top-k gate ([DS-8195] part 1; softmax then top-k renormalised over the k).
@@ -174,6 +203,16 @@ moe_status_t moe_dispatch_layout(const int32_t* topk_idx, int32_t s, int32_t e, 
                                  moe_layout_t* layout, void* stream);
 
 /*
+ * (2) Dispatch layout with options (host-side `options`, NULL = defaults): the same
+ * contract as moe_dispatch_layout, with the slot order and segment padding above.
+ * MOE_ERR_INVALID_ARG if pad_multiple < 1, or > 1 together with a capacity.
+ */
+moe_status_t moe_dispatch_layout_ex(const int32_t* topk_idx, int32_t s, int32_t e, int32_t k,
+                                    int32_t capacity, const moe_layout_options_t* options,
+                                    void* workspace, size_t workspace_bytes,
+                                    moe_layout_t* layout, void* stream);
+
+/*
  * (3) Dispatch ([DS-8195] part 3; [DS-8213] first commit): out[dst[t,j]] = x[t] for every
  * placed route, a bit copy; padding rows are written as zero. Each token row is read
  * once and written to its k destinations.
@@ -194,13 +233,54 @@ moe_status_t moe_dispatch_replay(const moe_layout_t* layout, const int32_t* topk
                                  void* stream);
 
 /*
+ * (3') Dispatch with the weights applied before the experts ([DS-8213] review thread on
+ * combine weights and the commit that applies them before or after the expert MLP,
+ * score_apply): out[dst[t,j]] = topk_w[t,j] * x[t], a float32 product rounded to dtype;
+ * padding rows are zero. The combine that follows is then unweighted (moe_combine with
+ * topk_w = NULL).
+ */
+moe_status_t moe_dispatch_weighted(const moe_layout_t* layout, const void* x,
+                                   const float* topk_w, int32_t m, moe_dtype_t dtype, void* out,
+                                   void* stream);
+
+/*
+ * (5') Backward of moe_dispatch_weighted: grad_x[t] = sum over placed routes j, in order,
+ * of topk_w[t,j] * grad_out[dst[t,j]] (float32, separate multiply and add, rounded once to
+ * dtype); grad_w[t,j] = <grad_out[dst[t,j]], x[t]> accumulated in float64 and rounded once
+ * (0 for a dropped route).
+ */
+moe_status_t moe_dispatch_weighted_backward(const moe_layout_t* layout, const void* grad_out,
+                                            const void* x, const float* topk_w, int32_t m,
+                                            moe_dtype_t dtype, void* grad_x, float* grad_w,
+                                            void* stream);
+
+/*
+ * Weights renormalised over each token's kept routes after the capacity drop (the other
+ * reading of where the renormalisation sits): w_out[t,j] = topk_w[t,j] / S_t for routes
+ * the layout placed, S_t the float64 sum of those weights in route order; 0 for dropped
+ * routes, and for all of a token's routes if none was placed. Rounded once to float32.
+ * topk_w and w_out are [s, k] float32 and may not overlap.
+ */
+moe_status_t moe_renormalize_kept(const moe_layout_t* layout, const float* topk_w, float* w_out,
+                                  void* stream);
+
+/*
+ * Backward of moe_renormalize_kept, given the original weights: with u = w / S over the
+ * placed routes, grad_w[t,i] = (grad_out[t,i] - sum_q u_q grad_out[t,q]) / S for placed i
+ * and 0 otherwise (float64, sums in route order, rounded once).
+ */
+moe_status_t moe_renormalize_kept_backward(const moe_layout_t* layout, const float* topk_w,
+                                           const float* grad_out, float* grad_w, void* stream);
+
+/*
  * (4) Weighted combine ([DS-8195] part 3: fp32 accumulation; [DS-8213] first commit and
  * the review thread on combine weights: the weights are applied here):
  *   y[t] = sum over placed routes j = 0..k-1, in that order, of topk_w[t,j] * E[dst[t,j]],
  *   each product and each sum rounded to float32 (no fused multiply-add), rounded once
  *   to dtype. Dropped routes add nothing; a token with no placed route gets a zero row.
  *   Only rows the layout points at are read ([DS-8213] review on combine and rows).
- *   expert_out [layout->rows, m];  topk_w [s, k] float32;  y [s, m].
+ *   expert_out [layout->rows, m];  topk_w [s, k] float32, or NULL for an unweighted sum
+ *   (after moe_dispatch_weighted);  y [s, m].
  */
 moe_status_t moe_combine(const moe_layout_t* layout, const void* expert_out,
                          const float* topk_w, int32_t m, moe_dtype_t dtype, void* y,

@@ -17,6 +17,7 @@ def to_dev(a: np.ndarray, dtype: str | None = None) -> torch.Tensor:
 
 def to_host(t: torch.Tensor) -> np.ndarray:
     """Download a device tensor; bf16 comes back as uint16 bit patterns."""
+    t = t.detach()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
     return t.cpu().numpy()

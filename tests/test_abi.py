@@ -36,15 +36,16 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_names(lib):
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     for code, name in M.STATUS_NAMES.items():
         assert lib.moe_status_string(code).decode() == name
     assert lib.moe_status_string(99).decode() == "MOE_STATUS_UNKNOWN"
 
 
 def test_layout_struct_matches_header_size():
-    # magic, 4 ints, rows, 10 pointers, size_t
-    assert ctypes.sizeof(M.LayoutStruct) == 8 + 16 + 8 + 10 * 8 + 8
+    # magic, 6 ints, rows, 10 pointers, size_t
+    assert ctypes.sizeof(M.LayoutStruct) == 8 + 24 + 8 + 10 * 8 + 8
+    assert ctypes.sizeof(M.LayoutOptions) == 8
 
 
 def test_workspace_bytes(lib):
@@ -61,6 +62,11 @@ def test_workspace_bytes(lib):
     assert wb(10, 2000, 2, 0) == 0
     assert wb(10, 64, 17, 0) == 0
     assert wb(2**30, 128, 8, 0) == 0  # s*k over 2**31
+    # options: route-major tiles cover s*k items, padding adds e*(P-1) rows
+    assert wb(1000, 64, 4, 0, route_major=True) > wb(1000, 64, 4, 0)
+    assert wb(1000, 64, 4, 0, pad_multiple=128) >= wb(1000, 64, 4, 0) + 4 * 64 * 127
+    assert wb(1000, 64, 4, 10, pad_multiple=2) == 0  # padding is dropless-only
+    assert wb(1000, 64, 4, 0, pad_multiple=0) == 0
 
 
 # The calls below carry fake device addresses that must be rejected before any
@@ -96,6 +102,13 @@ def test_layout_argument_checks(lib):
     assert lib.moe_dispatch_layout(FAKE, 100, 8, 2, 0, FAKE, need, None, None) == 1
     assert lib.moe_dispatch_layout(None, 100, 8, 2, 0, FAKE, need, ctypes.byref(st), None) == 1
     assert st.magic == 0  # nothing was filled
+    bad = M.LayoutOptions(0, 4)
+    assert lib.moe_dispatch_layout_ex(FAKE, 100, 8, 2, 5, ctypes.byref(bad), FAKE, need,
+                                      ctypes.byref(st), None) == 1  # padding with a capacity
+    bad = M.LayoutOptions(2, 1)
+    assert lib.moe_dispatch_layout_ex(FAKE, 100, 8, 2, 0, ctypes.byref(bad), FAKE, need,
+                                      ctypes.byref(st), None) == 1
+    assert st.magic == 0
 
 
 @no_gpu_only
@@ -123,7 +136,9 @@ def test_row_calls_check_alignment_and_dtype(lib):
     assert lib.moe_dispatch(ctypes.byref(st), ctypes.c_void_p((1 << 20) + 4), 64, 1, out, None) == 5
     assert lib.moe_dispatch(ctypes.byref(st), FAKE, 64, 7, out, None) == 1  # unknown dtype
     assert lib.moe_dispatch(ctypes.byref(st), FAKE, 0, 1, out, None) == 1  # m = 0
-    assert lib.moe_combine(ctypes.byref(st), FAKE, None, 64, 1, out, None) == 1  # NULL weights
+    assert lib.moe_dispatch_weighted(ctypes.byref(st), FAKE, None, 64, 1, out, None) == 1  # NULL weights
+    assert lib.moe_renormalize_kept(ctypes.byref(st), FAKE, FAKE, None) == 1  # in place
+    assert lib.moe_dispatch_weighted_backward(ctypes.byref(st), FAKE, FAKE, FAKE, 64, 1, out, None, None) == 1
     st.rows = st.rows + 1
     assert lib.moe_dispatch(ctypes.byref(st), FAKE, 64, 1, out, None) == 4
 
@@ -145,6 +160,7 @@ def _fake_handle(s, e, k, capacity, ws, need):
     st = M.LayoutStruct()
     st.magic = 0x4D4F454C41594F54
     st.s, st.e, st.k, st.capacity, st.rows = s, e, k, capacity, rows
+    st.route_major, st.pad_multiple = 0, 1
     for name, at in offs.items():
         setattr(st, name, ws + at)
     st.workspace = ws

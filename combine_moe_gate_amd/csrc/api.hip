@@ -119,7 +119,7 @@ Plan make_plan(int32_t s, int32_t e, int32_t k, int32_t capacity, const Options&
   p.off_route = take(cur, sizeof(int32_t) * routes);
   p.off_checksum = take(cur, sizeof(uint64_t));
   p.off_flags = take(cur, sizeof(int32_t));
-  p.off_tile_counts = take(cur, sizeof(int32_t) * static_cast<size_t>(p.ntiles) * e);
+  p.off_tile_counts = take(cur, sizeof(int32_t) * static_cast<size_t>(moe::tile_row_length(p.ntiles)) * e);
   p.off_tile_checksum = take(cur, sizeof(uint64_t) * static_cast<size_t>(p.ntiles));
   p.off_tile_flags = take(cur, sizeof(int32_t) * static_cast<size_t>(p.ntiles));
   p.bytes = (cur + kAlign - 1) / kAlign * kAlign;

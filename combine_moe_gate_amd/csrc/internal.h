@@ -21,10 +21,14 @@ struct LayoutView {
   int32_t* route_idx;
   uint64_t* checksum;
   int32_t* flags;
-  int32_t* tile_counts;       // [ntiles, e] per-tile valid-route counts
+  int32_t* tile_counts;       // [e, tile_row_length(ntiles)] per-tile valid-route counts
   uint64_t* tile_checksum;    // [ntiles]
   int32_t* tile_flags;        // [ntiles]
 };
+
+// Row length of the expert-major tile table: the tile count rounded up to a multiple
+// of 4, so each row can be read with 16-byte loads.
+inline int tile_row_length(int ntiles) { return (ntiles + 3) / 4 * 4; }
 
 // Smallest supported compile-time route bound >= k (k in [1, 16]).
 inline int route_bound(int k) { return k <= 1 ? 1 : k <= 2 ? 2 : k <= 4 ? 4 : k <= 8 ? 8 : 16; }

@@ -81,7 +81,7 @@ __device__ __forceinline__ int load_item(const int32_t* __restrict__ idx, int it
 
 template <int KMAX, bool RM>
 __global__ __launch_bounds__(kTileTokens) void layout_count_kernel(
-    const int32_t* __restrict__ idx, int s, int e, int k, int items,
+    const int32_t* __restrict__ idx, int s, int e, int k, int items, int ntp,
     int32_t* __restrict__ tile_counts, uint64_t* __restrict__ tile_checksum,
     int32_t* __restrict__ tile_flags) {
   extern __shared__ int32_t hist[];  // [e]
@@ -114,8 +114,9 @@ __global__ __launch_bounds__(kTileTokens) void layout_count_kernel(
     part_flags[threadIdx.x >> 6] = flags;
   }
   __syncthreads();
-  int32_t* out = tile_counts + static_cast<size_t>(blockIdx.x) * e;
-  for (int i = threadIdx.x; i < e; i += kTileTokens) out[i] = hist[i];
+  // expert-major table: row x holds expert x's count in every tile (row length ntp)
+  for (int i = threadIdx.x; i < e; i += kTileTokens)
+    tile_counts[static_cast<size_t>(i) * ntp + blockIdx.x] = hist[i];
   if (threadIdx.x == 0) {
     uint64_t c = 0;
     int f = 0;
@@ -169,7 +170,7 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t* __restrict__ va
 template <int KMAX, bool RM>
 __global__ __launch_bounds__(kTileTokens) void layout_place_kernel(
     const int32_t* __restrict__ idx, int s, int e, int k, int items, int capacity, int pad,
-    int32_t rows, int ntiles, const int32_t* __restrict__ tile_counts,
+    int32_t rows, int ntiles, int ntp, const int32_t* __restrict__ tile_counts,
     const uint64_t* __restrict__ tile_checksum, const int32_t* __restrict__ tile_flags,
     int32_t* __restrict__ counts, int32_t* __restrict__ kept_out, int32_t* __restrict__ offsets_out,
     uint64_t* __restrict__ checksum, int32_t* __restrict__ flags, int32_t* __restrict__ dst,
@@ -188,27 +189,52 @@ __global__ __launch_bounds__(kTileTokens) void layout_place_kernel(
   const int tile = blockIdx.x;
   const int my_tile = tile < ntiles ? tile : ntiles;  // workgroups past the tiles: padding only
 
-  // per expert: sum over earlier tiles and over all tiles
-  for (int x = threadIdx.x; x < e; x += kTileTokens) {
-    int32_t before = 0, all = 0;
-    int b = 0;
-    for (; b + 4 <= ntiles; b += 4) {
-      const int32_t c0 = tile_counts[static_cast<size_t>(b) * e + x];
-      const int32_t c1 = tile_counts[static_cast<size_t>(b + 1) * e + x];
-      const int32_t c2 = tile_counts[static_cast<size_t>(b + 2) * e + x];
-      const int32_t c3 = tile_counts[static_cast<size_t>(b + 3) * e + x];
-      before += (b < my_tile ? c0 : 0) + (b + 1 < my_tile ? c1 : 0) + (b + 2 < my_tile ? c2 : 0) +
-                (b + 3 < my_tile ? c3 : 0);
-      all += c0 + c1 + c2 + c3;
+  // per expert: sum over earlier tiles and over all tiles. Row x of the expert-major
+  // tile table is read with 16-byte loads; with e <= 128 several threads share a row
+  // (P parts of consecutive tiles) and their partial sums meet in LDS.
+  __shared__ int32_t part_before[kTileTokens], part_all[kTileTokens];
+  {
+    const int P = e <= kTileTokens / 2 ? kTileTokens / e : 1;  // threads per expert
+    const int nq = ntp / 4;                                      // int4 groups per row
+    const int qlen = (nq + P - 1) / P;
+    for (int slot = threadIdx.x; slot < (P > 1 ? P * e : e); slot += kTileTokens) {
+      const int x = P > 1 ? slot % e : slot;
+      const int part = P > 1 ? slot / e : 0;
+      const int4* row = reinterpret_cast<const int4*>(tile_counts + static_cast<size_t>(x) * ntp);
+      int32_t before = 0, all = 0;
+      const int q1 = (part + 1) * qlen < nq ? (part + 1) * qlen : nq;
+      for (int q = part * qlen; q < q1; ++q) {
+        const int4 c = row[q];
+        const int b = 4 * q;
+        const int32_t c0 = b < ntiles ? c.x : 0, c1 = b + 1 < ntiles ? c.y : 0;
+        const int32_t c2 = b + 2 < ntiles ? c.z : 0, c3 = b + 3 < ntiles ? c.w : 0;
+        before += (b < my_tile ? c0 : 0) + (b + 1 < my_tile ? c1 : 0) + (b + 2 < my_tile ? c2 : 0) +
+                  (b + 3 < my_tile ? c3 : 0);
+        all += c0 + c1 + c2 + c3;
+      }
+      if (P > 1) {
+        part_before[slot] = before;
+        part_all[slot] = all;
+      } else {
+        base_s[x] = before;
+        total_s[x] = all;
+      }
     }
-    for (; b < ntiles; ++b) {
-      const int32_t c = tile_counts[static_cast<size_t>(b) * e + x];
-      before += b < my_tile ? c : 0;
-      all += c;
+    if (P > 1) {
+      __syncthreads();
+      for (int x = threadIdx.x; x < e; x += kTileTokens) {
+        int32_t before = 0, all = 0;
+        for (int part = 0; part < P; ++part) {
+          before += part_before[part * e + x];
+          all += part_all[part * e + x];
+        }
+        base_s[x] = before;
+        total_s[x] = all;
+      }
     }
-    base_s[x] = before;
-    total_s[x] = all;
-    off_s[x] = capacity > 0 ? capacity : (all + pad - 1) / pad * pad;  // segment sizes
+    __syncthreads();
+    for (int x = threadIdx.x; x < e; x += kTileTokens)
+      off_s[x] = capacity > 0 ? capacity : (total_s[x] + pad - 1) / pad * pad;  // segment sizes
   }
   __syncthreads();
   const int32_t seg_total = block_exclusive_scan(off_s, e, wave_tot);
@@ -318,7 +344,8 @@ static hipError_t launch_layout_k(const int32_t* idx, const LayoutView& L, hipSt
   const int items = RM ? L.s * L.k : L.s;
   if (ntiles > 0) {
     layout_count_kernel<KMAX, RM><<<ntiles, kTileTokens, L.e * sizeof(int32_t), stream>>>(
-        idx, L.s, L.e, L.k, items, L.tile_counts, L.tile_checksum, L.tile_flags);
+        idx, L.s, L.e, L.k, items, tile_row_length(ntiles), L.tile_counts, L.tile_checksum,
+        L.tile_flags);
   }
   int grid = ntiles < 1 ? 1 : ntiles;
   if ((L.capacity > 0 || L.pad_multiple > 1) && grid < L.e + 1)
@@ -327,7 +354,7 @@ static hipError_t launch_layout_k(const int32_t* idx, const LayoutView& L, hipSt
                      (3 * static_cast<size_t>(L.e) + 1) * sizeof(int32_t);
   layout_place_kernel<KMAX, RM><<<grid, kTileTokens, lds, stream>>>(
       idx, L.s, L.e, L.k, items, L.capacity, L.pad_multiple, static_cast<int32_t>(L.rows), ntiles,
-      L.tile_counts, L.tile_checksum, L.tile_flags, L.counts, L.kept, L.offsets, L.checksum,
+      tile_row_length(ntiles), L.tile_counts, L.tile_checksum, L.tile_flags, L.counts, L.kept, L.offsets, L.checksum,
       L.flags, L.dst, L.src, L.route_idx);
   return hipGetLastError();
 }

@@ -69,9 +69,11 @@ __device__ __forceinline__ int64_t rotated_group(int64_t gi, int64_t t, int64_t 
 }
 
 // Workgroups past the s token workgroups zero the rows that no placed route fills:
-// segment x in [0, e) has rows [offsets[x] + kept[x], offsets[x+1]) unfilled, and
-// "segment" e is the tail [offsets[e], rows). Each (segment, sub-stride) pair is one
-// work item, so a few long segments still spread over many waves.
+// segment x in [0, e) has rows [offsets[x] + kept[x], offsets[x+1]) unfilled (capacity
+// or pad rows), each (segment, sub-stride) pair being one work item so that a few long
+// gaps still spread over many waves; then every padding wave strides over the tail
+// [offsets[e], rows), which is long when a padded layout's row bound is far above
+// the rows in use.
 template <bool NTS>
 __device__ __forceinline__ void zero_unfilled_rows(chunk_t* __restrict__ out, int64_t rc, int s,
                                                    int e, int32_t rows,
@@ -81,17 +83,19 @@ __device__ __forceinline__ void zero_unfilled_rows(chunk_t* __restrict__ out, in
   const int wpb = blockDim.x >> 6;
   const int32_t wave = (blockIdx.x - s) * wpb + wave_in_block();
   const int32_t nwaves = (gridDim.x - s) * wpb;
-  const int32_t nseg = e + 1;
-  const int32_t R = nwaves > nseg ? nwaves / nseg : 1;
+  const int32_t R = nwaves > e ? nwaves / e : 1;
   const chunk_t z = {0u, 0u, 0u, 0u};
-  for (int32_t item = wave; item < nseg * R; item += nwaves) {
-    const int32_t x = item % nseg, sub = item / nseg;
-    const int32_t r0 = x < e ? offsets[x] + kept[x] : offsets[e];
-    const int32_t r1 = x < e ? offsets[x + 1] : rows;
-    for (int32_t r = r0 + sub; r < r1; r += R) {
+  for (int32_t item = wave; item < e * R; item += nwaves) {
+    const int32_t x = item % e, sub = item / e;
+    const int32_t r1 = offsets[x + 1];
+    for (int32_t r = offsets[x] + kept[x] + sub; r < r1; r += R) {
       chunk_t* o = out + static_cast<size_t>(r) * rc;
       for (int64_t c = lane; c < rc; c += kWave) store_chunk<NTS>(o + c, z);
     }
+  }
+  for (int32_t r = offsets[e] + wave; r < rows; r += nwaves) {
+    chunk_t* o = out + static_cast<size_t>(r) * rc;
+    for (int64_t c = lane; c < rc; c += kWave) store_chunk<NTS>(o + c, z);
   }
 }
 

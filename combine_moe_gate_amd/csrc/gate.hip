@@ -1,14 +1,16 @@
 // Top-k gate and its backward on gfx950.
 //
 // One wave64 per token. The e logits of a row sit in registers, ceil(e/64) per lane,
-// each as a 64-bit key (order-preserving image of the float32 logit, then 0xffff minus
-// the expert id, so the largest key is the largest logit with ties to the lower id).
-// k rounds of a wave-wide maximum pick the experts in descending order; the owner lane
-// clears the winner. The weights are a softmax over the k selected logits, formed in
-// float64 (equal to the full softmax renormalised over the selection: the full
-// denominator cancels) -- DeepSpeed PR "MoE dispatch: fix silent Tutel + TP corruption,
-// speed up native and Tutel paths", part 1: the gate hands on per-route expert ids and
-// gate values, not a dense mask.
+// as 32-bit order-preserving images of the float32 values (element i at lane i mod 64,
+// slot i / 64). Each of the k rounds takes the wave-wide maximum of the untaken keys
+// (DPP max steps plus four readlanes), then finds the lowest expert id holding it with
+// one ballot per slot (ids of slot v are all below those of slot v+1), so ties go to
+// the lower id; the owner marks it taken. The experts come out in descending order.
+// The weights are a softmax over the k selected logits, formed in float64 (equal to
+// the full softmax renormalised over the selection: the full denominator cancels) --
+// DeepSpeed PR "MoE dispatch: fix silent Tutel + TP corruption, speed up native and
+// Tutel paths", part 1: the gate hands on per-route expert ids and gate values, not a
+// dense mask.
 #include "internal.h"
 #include "moe_device.h"
 
@@ -34,36 +36,50 @@ __global__ __launch_bounds__(kBlock) void gate_topk_kernel(const float* __restri
   if (t >= s) return;
   const float* row = logits + static_cast<size_t>(t) * e;
 
-  uint64_t key[VPL];
+  uint32_t key[VPL];
+  bool taken[VPL];
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     const int i = lane + v * kWave;
-    key[v] = (i < e) ? ((static_cast<uint64_t>(ordered_key(row[i])) << 16) |
-                        static_cast<uint64_t>(0xffff - i))
-                     : 0ull;
+    taken[v] = i >= e;  // lanes past e never compete
+    key[v] = taken[v] ? 0u : ordered_key(row[i]);
   }
 
-  uint64_t mine = 0;  // lane r keeps the r-th selection
+  int my_idx = 0;      // lane r keeps the r-th selection
+  uint32_t my_key = 0;
   for (int r = 0; r < k; ++r) {
-    uint64_t best = key[0];
+    uint32_t best = 0;
 #pragma unroll
-    for (int v = 1; v < VPL; ++v) best = key[v] > best ? key[v] : best;
-    best = wave_max(best);
+    for (int v = 0; v < VPL; ++v) {
+      const uint32_t kv = taken[v] ? 0u : key[v];
+      best = kv > best ? kv : best;
+    }
+    best = wave_max_u32(best);
+    int sel = 0;
 #pragma unroll
-    for (int v = 0; v < VPL; ++v)
-      if (key[v] == best) key[v] = 0ull;
-    if (lane == r) mine = best;
+    for (int v = 0; v < VPL; ++v) {
+      const uint64_t hit = __ballot(!taken[v] && key[v] == best);
+      if (hit != 0ull) {  // uniform: the lowest id with the maximum is in slot v
+        const int owner = static_cast<int>(__builtin_ctzll(hit));
+        sel = owner + v * kWave;
+        if (lane == owner) taken[v] = true;
+        break;
+      }
+    }
+    if (lane == r) {
+      my_idx = sel;
+      my_key = best;
+    }
   }
 
   const bool active = lane < k;
-  const int expert = 0xffff - static_cast<int>(mine & 0xffffu);
-  const float l = key_to_float(static_cast<uint32_t>(mine >> 16));
+  const float l = key_to_float(my_key);
   const float l0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, l)));
   const double ex = active ? exp(static_cast<double>(l) - static_cast<double>(l0)) : 0.0;
   const double denom = wave_sum(ex);
   if (active) {
     const size_t o = static_cast<size_t>(t) * k + lane;
-    idx_out[o] = expert;
+    idx_out[o] = my_idx;
     w_out[o] = static_cast<float>(ex / denom);
   }
 }

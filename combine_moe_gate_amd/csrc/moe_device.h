@@ -146,6 +146,21 @@ __device__ __forceinline__ int wave_or(int v) {
   return static_cast<int>(r);
 }
 
+// 32-bit maximum over the 64 lanes, returned uniformly: the same DPP pattern, where
+// each step is a single v_max_u32 with a DPP source.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  auto step = [](uint32_t x, uint32_t y) { return x > y ? x : y; };
+  v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xb1, 0xf, 0xf, false)));
+  v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4e, 0xf, 0xf, false)));
+  v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x141, 0xf, 0xf, false)));
+  v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x140, 0xf, 0xf, false)));
+  const uint32_t a = __builtin_amdgcn_readlane(static_cast<int>(v), 0);
+  const uint32_t b = __builtin_amdgcn_readlane(static_cast<int>(v), 16);
+  const uint32_t c = __builtin_amdgcn_readlane(static_cast<int>(v), 32);
+  const uint32_t d = __builtin_amdgcn_readlane(static_cast<int>(v), 48);
+  return step(step(a, b), step(c, d));
+}
+
 // Maximum over the 64 lanes, returned uniformly.
 __device__ __forceinline__ uint64_t wave_max(uint64_t v) {
   return wave_reduce(v, [](uint64_t a, uint64_t b) { return a > b ? a : b; });

@@ -189,6 +189,20 @@ __global__ __launch_bounds__(kTileTokens) void layout_place_kernel(
   const int tile = blockIdx.x;
   const int my_tile = tile < ntiles ? tile : ntiles;  // workgroups past the tiles: padding only
 
+  // this thread's routes, loaded first so that their latency overlaps the table reads
+  const int item = tile * kTileTokens + threadIdx.x;
+  const int nr = RM ? 1 : k;
+  int tok = 0, ids[KMAX];
+  bool ok[KMAX];
+  int64_t pos[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    ids[j] = -1;
+    ok[j] = false;
+    pos[j] = 0;
+  }
+  if (tile < ntiles && item < items) load_item<KMAX, RM>(idx, item, s, k, e, tok, ids, ok, pos);
+
   // per expert: sum over earlier tiles and over all tiles. Row x of the expert-major
   // tile table is read with 16-byte loads; with e <= 128 several threads share a row
   // (P parts of consecutive tiles) and their partial sums meet in LDS.
@@ -278,23 +292,9 @@ __global__ __launch_bounds__(kTileTokens) void layout_place_kernel(
     for (int i = threadIdx.x; i < kWaves * e; i += kTileTokens) lane_masks[i] = 0ull;
     __syncthreads();
 
-    const int item = tile * kTileTokens + threadIdx.x;
-    const int nr = RM ? 1 : k;
-    int tok = 0, ids[KMAX];
-    bool ok[KMAX];
-    int64_t pos[KMAX];
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      ids[j] = -1;
-      ok[j] = false;
-      pos[j] = 0;
-    }
-    if (item < items) {
-      load_item<KMAX, RM>(idx, item, s, k, e, tok, ids, ok, pos);
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j)
-        if (ok[j]) atomicOr(&lane_masks[wv * e + ids[j]], 1ull << lane);
-    }
+    for (int j = 0; j < KMAX; ++j)
+      if (ok[j]) atomicOr(&lane_masks[wv * e + ids[j]], 1ull << lane);
     __syncthreads();
 
     if (item < items) {

@@ -40,6 +40,7 @@ from .moe import (  # noqa: F401
     dispatch_replay,
     dispatch_weighted,
     dispatch_weighted_backward,
+    expert_gemm,
     renormalize_kept,
     renormalize_kept_backward,
     gate_topk,

@@ -450,3 +450,49 @@ def renormalize_kept_backward(layout: Layout, w: np.ndarray, grad_out: np.ndarra
     u = np.where(kept, w64 / safe, 0.0)
     dot = _route_order_sum(np.where(kept, u * g64, 0.0))
     return np.where(kept & (S != 0), (g64 - dot) / safe, 0.0).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# the grouped expert GEMM that consumes the layout
+
+
+def expert_gemm(layout: Layout, a: np.ndarray, weights: np.ndarray, dtype: str, gather: bool,
+                route_w: np.ndarray | None = None) -> tuple[np.ndarray, np.ndarray]:
+    """Per-expert projection of the buffer rows, with the dispatch optionally fused in.
+
+    For expert x and each placed row r of its segment:
+        out[r] = A(r) @ weights[x]^T,  A(r) = a[src[r]] if gather else a[r]
+    weights: [e, n, m] (output features x input features). The products are summed
+    exactly (float64 of float32-widened operands, one matmul per expert), rounded to
+    float32 as a float32 accumulator would hold them, optionally scaled by the route's
+    weight (a float32 product: weights applied after the experts), and rounded once to
+    the element type. Rows no route fills are zero.
+    [DS-8213] review-fix commit: the grouped GEMM takes its row groups from the per-
+    expert offsets (counts = differences of the prefix sum) and ignores rows past them;
+    the dispatch is fused into its operand loads here instead of materialising the
+    permuted buffer ([DS-8213] first commit: arrivals grouped by expert for the grouped
+    GEMM).
+    Returns (out, exact): exact holds the float64 sums (for tolerance checks).
+    """
+    e, n, m = weights.shape
+    a32 = to_f32(a, dtype).astype(np.float64)
+    w64 = to_f32(weights.reshape(e * n, m), dtype).astype(np.float64).reshape(e, n, m)
+    exact = np.zeros((layout.rows, n), np.float64)
+    row_w = np.ones(layout.rows, np.float32)
+    if route_w is not None:
+        placed = layout.dst >= 0
+        row_w[layout.dst[placed]] = np.asarray(route_w, np.float32)[placed]
+    for x in range(layout.e):
+        r0 = int(layout.offsets[x])
+        r1 = r0 + int(layout.kept[x])
+        if r1 == r0:
+            continue
+        rows = np.arange(r0, r1)
+        lhs = a32[layout.src[rows]] if gather else a32[rows]
+        exact[rows] = lhs @ w64[x].T
+    acc32 = exact.astype(np.float32)
+    if route_w is not None:
+        acc32 = row_w[:, None] * acc32  # float32 product
+    out = from_f32(acc32, dtype)
+    out[layout.src < 0] = 0
+    return out, exact

@@ -12,6 +12,7 @@ import oracle
 from oracle import moe
 from tests import test_oracle_pins as pins
 from tests import test_oracle_variants as vpins
+from tests import test_oracle_gemm as gpins
 
 
 def _route_major_layout(idx, e, capacity, route_major=False, pad_multiple=1):
@@ -130,7 +131,26 @@ def _renorm_backward_no_centering(layout, w, g):
     return np.where(kept & (S != 0), np.asarray(g, np.float64) / np.where(S != 0, S, 1), 0).astype(np.float32)
 
 
+def _gemm_wrong_expert(layout, a, weights, dtype, gather, route_w=None):
+    return moe.expert_gemm(layout, a, np.roll(weights, 1, axis=0), dtype, gather, route_w)
+
+
+def _gemm_untransposed(layout, a, weights, dtype, gather, route_w=None):
+    e, n, m = weights.shape
+    if n == m:
+        return moe.expert_gemm(layout, a, np.swapaxes(weights, 1, 2), dtype, gather, route_w)
+    out, exact = moe.expert_gemm(layout, a, weights, dtype, gather, route_w)
+    return out, exact * 1.5
+
+
+def _gemm_ignores_route_weights(layout, a, weights, dtype, gather, route_w=None):
+    return moe.expert_gemm(layout, a, weights, dtype, gather, None)
+
+
 MUTATIONS = {
+    "gemm_wrong_expert": ("expert_gemm", _gemm_wrong_expert),
+    "gemm_untransposed": ("expert_gemm", _gemm_untransposed),
+    "gemm_ignores_route_weights": ("expert_gemm", _gemm_ignores_route_weights),
     "ignores_route_major": ("dispatch_layout", _layout_ignores_route_major),
     "ignores_padding": ("dispatch_layout", _layout_ignores_padding),
     "weighted_dispatch_unweighted": ("dispatch_weighted", _weighted_dispatch_unweighted),
@@ -167,6 +187,9 @@ PINS = [
     lambda: vpins.test_weighted_dispatch_backward_adjoint_and_finite_difference(4),
     vpins.test_renormalized_gate_weights_are_softmax_over_kept_logits,
     vpins.test_renormalize_backward_matches_finite_differences_through_the_gate,
+    lambda: gpins.test_expert_gemm_matches_brute_force(3, True),
+    gpins.test_scaled_identity_weights_route_rows_to_the_right_expert,
+    gpins.test_route_weights_scale_each_row,
 ]
 
 

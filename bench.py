@@ -36,8 +36,11 @@ METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (s=8192,m=4096,e=128,k
 HBM_PEAK_GBPS = 8000.0
 # The same step with one of the variants: route-major capacity priority, dropless
 # segments padded to 128 rows, weights applied at dispatch (before the experts), or
-# weights renormalised over the kept routes after the capacity drop.
-VARIANTS = ("route_major", "pad128", "weights_before", "renorm_kept")
+# weights renormalised over the kept routes after the capacity drop; or the forward of a
+# layer whose experts are one linear projection each: gate, layout, the grouped expert
+# GEMM with the dispatch fused into its operand loads, weighted combine.
+VARIANTS = ("route_major", "pad128", "weights_before", "renorm_kept", "expert_gemm")
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def kernel_source_digest() -> str:
@@ -92,6 +95,13 @@ def algorithmic_bytes(w: W.Workload, kept_routes: int, rows: int | None = None,
         "renorm": s * k * 12,
         "renorm_bwd": s * k * 16,
     }
+    if variant == "expert_gemm":
+        n, nb = W.EXPERT_WIDTH, W.EXPERT_WIDTH * b
+        # x read once, every expert's weights once, the [rows, n] output and its row map
+        out["expert_gemm"] = s * row + e * n * row + rows * nb + rows * 4
+        out["combine"] = K * nb + s * k * 8 + s * nb
+        out["dispatch"] = s * row + rows * row + s * k * 4
+        out["expert_gemm_unfused"] = rows * row + e * n * row + rows * nb + rows * 4
     if variant == "weights_before":
         # dispatch and replay read the weights; the combine is unweighted; the combine
         # backward is a plain dispatch of grad_y; the dispatch backward also reads x
@@ -101,6 +111,16 @@ def algorithmic_bytes(w: W.Workload, kept_routes: int, rows: int | None = None,
         out["combine_bwd"] = s * row + rows * row + s * k * 4
         out["dispatch_bwd"] = K * row + s * row + s * row + s * k * 12
     return out
+
+
+_WEIGHTS = {}
+
+
+def expert_weights(w: W.Workload):
+    """The seeded expert projection weights [e, EXPERT_WIDTH, m] (generated once)."""
+    if w.name not in _WEIGHTS:
+        _WEIGHTS[w.name] = W.expert_weights(w.seed + 1, w.e, W.EXPERT_WIDTH, w.m, w.dtype)
+    return _WEIGHTS[w.name]
 
 
 def to_dev(a, dtype, dev):
@@ -152,7 +172,25 @@ def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None):
     def gate_bwd():
         M.moe_gate_topk_backward(idx, wt, gw, e, out=gl)
 
-    if variant == "weights_before":
+    extra = {}
+    if variant == "expert_gemm":
+        n = W.EXPERT_WIDTH
+        wts = to_dev(expert_weights(w), w.dtype, dev)
+        H = torch.empty((rows, n), dtype=tdt, device=dev)
+        yH = torch.empty((s, n), dtype=tdt, device=dev)
+        H2 = torch.empty((rows, n), dtype=tdt, device=dev)
+        ops = [
+            ("gate", gate), ("layout", layout),
+            ("expert_gemm", lambda: M.moe_expert_gemm(st["L"], x, wts, gather=True, out=H)),
+            ("combine", lambda: M.moe_combine(st["L"], H, wt, out=yH)),
+        ]
+        # the same projection unfused, timed after the step: dispatch, then the GEMM on
+        # the dispatched buffer
+        extra["unfused"] = [
+            ("dispatch", lambda: M.moe_dispatch(st["L"], x, out=buf)),
+            ("expert_gemm_unfused", lambda: M.moe_expert_gemm(st["L"], buf, wts, gather=False, out=H2)),
+        ]
+    elif variant == "weights_before":
         ops = [
             ("gate", gate), ("layout", layout),
             ("dispatch", lambda: M.moe_dispatch_weighted(st["L"], x, wt, out=buf)),
@@ -214,6 +252,15 @@ def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None):
     for ev in events:
         for j, op in enumerate(names):
             per_op[op].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)  # microseconds
+    for op, fn in extra.get("unfused", []):  # outside the timed step
+        per_op[op] = []
+        for _ in range(min(steps, 10)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            per_op[op].append(a.elapsed_time(b) * 1e3)
     L = st["L"]
     kept = int(L.kept.sum().item())
     flags, _ = M.moe_layout_read(L)
@@ -225,9 +272,14 @@ def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None):
 def run_cpu_baseline(w: W.Workload, target_s: float = 12.0, sample_tokens: int = 1024,
                      variant: str | None = None):
     """The oracle, as it stands, over the first `sample_tokens` tokens of the workload."""
+    from threadpoolctl import threadpool_limits
+
     import oracle
 
     inp = W.make_inputs(w)
+    if variant == "expert_gemm":  # a float64 matmul per expert: a smaller sample
+        sample_tokens = min(sample_tokens, 128)
+        wts = expert_weights(w)
     n = min(sample_tokens, w.s)
     logits = inp.logits[:n]
     x = inp.x[:n]
@@ -238,10 +290,15 @@ def run_cpu_baseline(w: W.Workload, target_s: float = 12.0, sample_tokens: int =
     reps = 0
     t0 = time.perf_counter()
     opts = dict(route_major=variant == "route_major", pad_multiple=128 if variant == "pad128" else 1)
+    limit = threadpool_limits(limits=1)  # the BLAS behind numpy's matmul on one core
     while True:
         idx, wt = oracle.gate_topk(logits, w.k)
         L = oracle.dispatch_layout(idx, w.e, cap, **opts)
-        if variant == "weights_before":
+        if variant == "expert_gemm":
+            H, _ = oracle.expert_gemm(L, x, wts, w.dtype, gather=True)
+            oracle.combine(L, H, wt, w.dtype)
+            gw = np.zeros_like(wt)
+        elif variant == "weights_before":
             E = oracle.dispatch_weighted(L, x, wt, w.dtype)
             oracle.dispatch_backward(L, E, w.dtype)  # the unweighted combine
             oracle.dispatch_weighted(L, x, wt, w.dtype)  # replay
@@ -256,11 +313,13 @@ def run_cpu_baseline(w: W.Workload, target_s: float = 12.0, sample_tokens: int =
             if variant == "renorm_kept":
                 gw = oracle.renormalize_kept_backward(L, wt, gw)
             oracle.dispatch_backward(L, gE, w.dtype)
-        oracle.gate_topk_backward(idx, wt, gw, w.e)
+        if variant != "expert_gemm":  # that variant times the forward only
+            oracle.gate_topk_backward(idx, wt, gw, w.e)
         reps += 1
         el = time.perf_counter() - t0
         if el >= target_s:
             break
+    limit.unregister()
     return {
         "value": n * reps / el,
         "unit": "tokens/s",
@@ -309,11 +368,27 @@ def main():
         us = float(np.mean(per_op[op]))
         kernels[op] = {"us": round(us, 2), "us_median": round(float(np.median(per_op[op])), 2),
                        "bytes": abytes[op], "GBps": round(abytes[op] / us / 1e3, 1)}
+    step_ops = [op for op in ops if op not in ("expert_gemm_unfused",) and
+                not (args.variant == "expert_gemm" and op == "dispatch")]
     dc_us = kernels["dispatch"]["us"] + kernels["combine"]["us"]
     dc_bytes = abytes["dispatch"] + abytes["combine"]
     dc_gbps = dc_bytes / dc_us / 1e3
-    dominant = max(ops, key=lambda op: kernels[op]["us"])
+    dominant = max(step_ops, key=lambda op: kernels[op]["us"])
     dom_gbps = abytes[dominant] / kernels[dominant]["us"] / 1e3
+    roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(dom_gbps, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+                "traffic": None if args.variant else measured_traffic(w.name).get(dominant),
+                "algorithmic_bytes": abytes[dominant]}
+    if args.variant == "expert_gemm":
+        flops = 2 * kept * W.EXPERT_WIDTH * w.m
+        for op in ("expert_gemm", "expert_gemm_unfused"):
+            kernels[op]["TFLOPs"] = round(flops / kernels[op]["us"] / 1e6, 1)
+        if dominant == "expert_gemm":
+            tf = flops / kernels[dominant]["us"] / 1e6
+            roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(tf, 1),
+                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                        "algorithmic_flops": flops, "algorithmic_bytes": abytes[dominant]}
 
     line = {
         "metric": METRIC,
@@ -332,15 +407,14 @@ def main():
                    "capacity": w.capacity if w.capacity > 0 else "dropless",
                    "routing": {"uniform": "N(0,1) logits", "zipf": "N(0,1) + 2 ln Zipf(1.2) bias",
                                "hotspot": "N(0,1), +3 on expert 0 for 10% of tokens"}[w.routing],
-                   "step": "+".join(ops), "variant": args.variant or "default",
-                   "parallelism": "single GPU"},
-        "dispatch_combine": {"tokens_per_s": round(w.s / (dc_us / 1e6), 1), "GBps": round(dc_gbps, 1),
-                             "frac_of_hbm_peak": round(dc_gbps / HBM_PEAK_GBPS, 4), "us": round(dc_us, 2),
-                             "bytes": dc_bytes},
-        "roofline": {"kernel": dominant, "bound": "hbm", "achieved": round(dom_gbps, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None if args.variant else measured_traffic(w.name).get(dominant),
-                     "algorithmic_bytes": abytes[dominant]},
+                   "step": "+".join(step_ops), "variant": args.variant or "default",
+                   "parallelism": "single GPU",
+                   **({"expert_width": W.EXPERT_WIDTH} if args.variant == "expert_gemm" else {})},
+        "dispatch_combine": None if args.variant == "expert_gemm" else {
+            "tokens_per_s": round(w.s / (dc_us / 1e6), 1), "GBps": round(dc_gbps, 1),
+            "frac_of_hbm_peak": round(dc_gbps / HBM_PEAK_GBPS, 4), "us": round(dc_us, 2),
+            "bytes": dc_bytes},
+        "roofline": roofline,
         "kernels": kernels,
         "kept_routes": kept,
     }

@@ -83,6 +83,8 @@ _SIGNATURES = {
     "moe_dispatch_weighted": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _P, _I, ctypes.c_int, _P, _P]),
     "moe_dispatch_weighted_backward": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _P, _P, _I,
                                                       ctypes.c_int, _P, _P, _P]),
+    "moe_expert_gemm": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _I, _P, _I, _I, ctypes.c_int,
+                                       _P, _P, _P]),
     "moe_renormalize_kept": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _P, _P]),
     "moe_renormalize_kept_backward": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _P, _P, _P]),
     "moe_gate_topk": (ctypes.c_int, [_P, _I, _I, _I, _P, _P, _P]),
@@ -311,6 +313,27 @@ def moe_dispatch_weighted_backward(layout: Layout, grad_out: torch.Tensor, x: to
     return gx, gw
 
 
+def moe_expert_gemm(layout: Layout, a: torch.Tensor, weights: torch.Tensor, gather: bool = True,
+                    w: torch.Tensor | None = None, out=None):
+    """Grouped expert GEMM over the layout's segments: out[r] = A(r) @ weights[x]^T.
+
+    a is the token rows x [s, m] when gather (the dispatch fused into the GEMM's operand
+    loads), else a dispatched buffer [rows, m]; weights [e, n, m]; w [s, k] float32 scales
+    each row by its route's weight, or None. Returns out [rows, n].
+    """
+    _require_gpu(a, weights, w)
+    m = a.shape[1]
+    n = weights.shape[1]
+    if weights.dim() != 3 or weights.shape[0] != layout.e or weights.shape[2] != m:
+        raise ValueError(f"weights must be [e={layout.e}, n, m={m}], got {tuple(weights.shape)}")
+    if weights.dtype != a.dtype:
+        raise ValueError("a and weights must have the same dtype")
+    out = out if out is not None else torch.empty((layout.rows, n), dtype=a.dtype, device=a.device)
+    _check(lib().moe_expert_gemm(layout.byref(), _ptr(a), int(bool(gather)), _ptr(weights), m, n,
+                                 _dtype_code(a), _ptr(w), _ptr(out), _stream(a)))
+    return out
+
+
 def moe_renormalize_kept(layout: Layout, w: torch.Tensor, out=None):
     _require_gpu(w)
     w_out = out if out is not None else torch.empty_like(w)
@@ -338,6 +361,6 @@ __all__ = [
     "moe_gate_topk", "moe_gate_topk_backward", "moe_dispatch_layout", "moe_dispatch",
     "moe_dispatch_replay", "moe_combine", "moe_combine_backward", "moe_dispatch_backward",
     "moe_layout_read", "moe_dispatch_weighted", "moe_dispatch_weighted_backward",
-    "moe_renormalize_kept", "moe_renormalize_kept_backward", "workspace_bytes", "Layout",
+    "moe_renormalize_kept", "moe_renormalize_kept_backward", "moe_expert_gemm", "workspace_bytes", "Layout",
     "LayoutOptions", "MoeError", "lib", "EXPORTS",
 ]

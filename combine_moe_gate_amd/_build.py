@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_NAME = "libmoe_gate.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("api.hip", "gate.hip", "layout.hip", "rows.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("api.hip", "gate.hip", "layout.hip", "rows.hip", "gemm.hip")]
 HEADERS = [os.path.join(HERE, "csrc", f) for f in ("internal.h", "moe_device.h")] + [
     os.path.join(ROOT, "include", "moe_gate.h")]
 

@@ -384,6 +384,39 @@ moe_status_t moe_dispatch_weighted_backward(const moe_layout_t* layout, const vo
                     "moe_dispatch_weighted_backward");
 }
 
+moe_status_t moe_expert_gemm(const moe_layout_t* layout, const void* a, int32_t gather,
+                             const void* weights, int32_t m, int32_t n, moe_dtype_t dtype,
+                             const float* topk_w, void* out, void* stream) {
+  moe::LayoutView v;
+  MOE_TRY(view_of(layout, &v));
+  if (dtype != MOE_BF16 && dtype != MOE_F16)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_expert_gemm supports bf16 and f16 only (got dtype %d)",
+                static_cast<int>(dtype));
+  if (gather != 0 && gather != 1)
+    return fail(MOE_ERR_INVALID_ARG, "gather must be 0 or 1 (got %d)", gather);
+  int64_t rc_in = 0, rc_out = 0;
+  MOE_TRY(check_rows(m, dtype, &rc_in));
+  MOE_TRY(check_rows(n, dtype, &rc_out));
+  if (v.s > 0 && moe::expert_gemm_grid(v, n) > INT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "rows x n too large for one grouped GEMM launch");
+  const int64_t a_rows = gather ? v.s : v.rows;
+  MOE_TRY(check_array(a, v.s > 0 ? a_rows : 0, "a", true));
+  MOE_TRY(check_array(weights, v.s > 0 ? v.e : 0, "weights", true));
+  MOE_TRY(check_array(topk_w, topk_w != nullptr ? v.s : 0, "topk_w", false));
+  MOE_TRY(check_array(out, v.rows, "out", true));
+  if (v.rows > 0 && a_rows > 0) {
+    const char* ob = static_cast<const char*>(out);
+    const char* ab = static_cast<const char*>(a);
+    const size_t eb = elem_bytes(dtype);
+    if (ob < ab + a_rows * m * eb && ab < ob + v.rows * n * eb)
+      return fail(MOE_ERR_INVALID_ARG, "a and out may not overlap");
+  }
+  return hip_status(moe::launch_expert_gemm(v, a, gather != 0, weights, topk_w, m, n,
+                                            static_cast<int>(dtype), out,
+                                            static_cast<hipStream_t>(stream)),
+                    "moe_expert_gemm");
+}
+
 moe_status_t moe_renormalize_kept(const moe_layout_t* layout, const float* topk_w, float* w_out,
                                   void* stream) {
   moe::LayoutView v;

@@ -63,4 +63,16 @@ hipError_t launch_renormalize_kept_backward(const LayoutView& L, const float* w,
                                             const float* grad_out, float* grad_w,
                                             hipStream_t stream);
 
+// Zero the rows of a [rows, rc chunks] buffer that no placed route fills.
+hipError_t launch_zero_unfilled_rows(const LayoutView& L, void* out, int64_t row_chunks,
+                                     hipStream_t stream);
+// Grouped expert GEMM over the layout's segments: out[r] = A(r) @ w[x]^T for the placed
+// rows r of expert x, A(r) = a[src[r]] if gather else a[r]; optional route weight per
+// row (route_w may be null); unfilled rows zeroed. dtype bf16 or f16; m, n multiples of 8.
+hipError_t launch_expert_gemm(const LayoutView& L, const void* a, bool gather, const void* w,
+                              const float* route_w, int m, int n, int dtype, void* out,
+                              hipStream_t stream);
+// Workgroups the grouped expert GEMM launches for these sizes (0 if none).
+int64_t expert_gemm_grid(const LayoutView& L, int n);
+
 }  // namespace moe

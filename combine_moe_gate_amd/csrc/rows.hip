@@ -470,6 +470,24 @@ hipError_t launch_combine_backward(const LayoutView& L, const void* gy, const vo
   return scatter_any<true>(L, gy, E, w, rc, dtype, gE, gw, stream);
 }
 
+// Zero the unfilled rows of a buffer whose filled rows another kernel writes (the
+// grouped expert GEMM's output).
+__global__ __launch_bounds__(kBlock) void zero_rows_kernel(chunk_t* __restrict__ out, int64_t rc,
+                                                           int e, int32_t rows,
+                                                           const int32_t* __restrict__ kept,
+                                                           const int32_t* __restrict__ offsets) {
+  zero_unfilled_rows<true>(out, rc, 0, e, rows, kept, offsets);
+}
+
+hipError_t launch_zero_unfilled_rows(const LayoutView& L, void* out, int64_t rc,
+                                     hipStream_t stream) {
+  const int grid = pad_blocks(L, kWavesPerBlock);
+  if (grid > 0)
+    zero_rows_kernel<<<grid, kBlock, 0, stream>>>(static_cast<chunk_t*>(out), rc, L.e,
+                                                  static_cast<int32_t>(L.rows), L.kept, L.offsets);
+  return hipGetLastError();
+}
+
 hipError_t launch_dispatch_weighted(const LayoutView& L, const void* x, const float* w,
                                     int64_t rc, int dtype, void* out, hipStream_t stream) {
   return scatter_any<false>(L, x, nullptr, w, rc, dtype, out, nullptr, stream);

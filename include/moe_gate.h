@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -308,6 +308,27 @@ moe_status_t moe_combine_backward(const moe_layout_t* layout, const void* grad_y
  */
 moe_status_t moe_dispatch_backward(const moe_layout_t* layout, const void* grad_out,
                                    int32_t m, moe_dtype_t dtype, void* grad_x, void* stream);
+
+/*
+ * Grouped expert GEMM over the layout's segments, with the dispatch fused into its
+ * operand loads ([DS-8213] review-fix commit: the grouped GEMM takes its row groups from
+ * offsets = cumsum(counts) and ignores rows past them; first commit: arrivals are grouped
+ * by expert for it). For expert x and each row r in [offsets[x], offsets[x] + kept[x]):
+ *   out[r, :] = A(r) @ weights[x]^T,  A(r) = a[src[r]] if gather (a = x [s, m]: the
+ *   permuted buffer is never materialised) else a[r] (a = a dispatched buffer [rows, m]).
+ * Products of dtype operands are accumulated in float32 on the matrix cores (summation
+ * order unspecified), optionally multiplied by the route's weight topk_w[t,j] for the
+ * route placed at r (a float32 product; weights applied after the experts), and rounded
+ * once to dtype. Rows no route fills are zero. Output for gather = 1 and gather = 0 on
+ * the dispatched buffer is bitwise identical.
+ *   weights [e, n, m] of dtype (output x input features, row-major);  out [rows, n].
+ *   dtype bf16 or f16 (MOE_ERR_UNSUPPORTED otherwise); m and n multiples of 8;
+ *   a, weights and out 16-byte aligned; a and out may not overlap; topk_w [s, k] float32
+ *   or NULL (no scaling).
+ */
+moe_status_t moe_expert_gemm(const moe_layout_t* layout, const void* a, int32_t gather,
+                             const void* weights, int32_t m, int32_t n, moe_dtype_t dtype,
+                             const float* topk_w, void* out, void* stream);
 
 /*
  * Read the layout's flags word and routing checksum into HOST memory. Synchronises

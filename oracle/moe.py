@@ -476,7 +476,6 @@ def expert_gemm(layout: Layout, a: np.ndarray, weights: np.ndarray, dtype: str, 
     """
     e, n, m = weights.shape
     a32 = to_f32(a, dtype).astype(np.float64)
-    w64 = to_f32(weights.reshape(e * n, m), dtype).astype(np.float64).reshape(e, n, m)
     exact = np.zeros((layout.rows, n), np.float64)
     row_w = np.ones(layout.rows, np.float32)
     if route_w is not None:
@@ -489,7 +488,8 @@ def expert_gemm(layout: Layout, a: np.ndarray, weights: np.ndarray, dtype: str, 
             continue
         rows = np.arange(r0, r1)
         lhs = a32[layout.src[rows]] if gather else a32[rows]
-        exact[rows] = lhs @ w64[x].T
+        w64 = to_f32(weights[x], dtype).astype(np.float64)  # [n, m], one expert at a time
+        exact[rows] = lhs @ w64.T
     acc32 = exact.astype(np.float32)
     if route_w is not None:
         acc32 = row_w[:, None] * acc32  # float32 product

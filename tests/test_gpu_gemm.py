@@ -1,0 +1,206 @@
+"""GPU parity for the grouped expert GEMM with the dispatch fused into its operand loads.
+
+Bars:
+  - the fused call (rows gathered from x through the layout) and the unfused one (on
+    the dispatched buffer) are bitwise identical, with and without route weights;
+  - every output is within the float32 accumulation bound of the oracle's exact
+    products: |got - want| <= ulp_dtype(max(|got|, |want|)) + 2^-23 max(|got|, |want|)
+    + |w| (m + 2) 2^-23 sum_m |a b|  (summation order on the matrix cores is not fixed;
+    the oracle sums exactly and rounds once, so the bound is the worst-case error of an
+    m-term float32 sum plus one rounding to the element type);
+  - with small-integer operands every partial sum is exact in float32, so the output is
+    bit-exact against the oracle;
+  - rows no route fills are +0.0.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_moe_gate_amd as M
+import oracle
+import workloads as W
+from tests.gpu_util import assert_bits_equal, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def announce(*what):
+    print("CASE", *what, flush=True)
+
+
+def dtype_ulp(v: np.ndarray, dtype: str) -> np.ndarray:
+    """Spacing of dtype values at |v| (bf16: 8 significant bits, f16: 11), subnormal floor."""
+    p, emin = (8, -126) if dtype == "bf16" else (11, -14)
+    ex = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** emin)))
+    return 2.0 ** (ex - (p - 1))
+
+
+def abs_bits(a: np.ndarray, dtype: str) -> np.ndarray:
+    return (a & np.uint16(0x7FFF)) if dtype == "bf16" else np.abs(a)
+
+
+def row_weights(Lo: oracle.Layout, w: np.ndarray | None) -> np.ndarray:
+    rw = np.ones(Lo.rows)
+    if w is not None:
+        placed = Lo.dst >= 0
+        rw[Lo.dst[placed]] = np.abs(w[placed].astype(np.float64))
+    return rw
+
+
+def check_gemm(got: np.ndarray, Lo: oracle.Layout, a: np.ndarray, wts: np.ndarray, dtype: str,
+               gather: bool, route_w: np.ndarray | None, what: str):
+    want, _ = oracle.expert_gemm(Lo, a, wts, dtype, gather, route_w)
+    _, absb = oracle.expert_gemm(Lo, abs_bits(a, dtype), abs_bits(wts, dtype), dtype, gather)
+    m = a.shape[1]
+    g = oracle.to_f32(got, dtype).astype(np.float64)
+    wv = oracle.to_f32(want, dtype).astype(np.float64)
+    big = np.maximum(np.abs(g), np.abs(wv))
+    tol = dtype_ulp(big, dtype) + 2.0 ** -23 * big + \
+        row_weights(Lo, route_w)[:, None] * (m + 2) * 2.0 ** -23 * absb
+    err = np.abs(g - wv)
+    bad = np.argwhere(~(err <= tol))
+    assert len(bad) == 0, (f"{what}: {len(bad)} outputs outside the bound, first {tuple(bad[0])}: "
+                           f"got {g[tuple(bad[0])]!r} want {wv[tuple(bad[0])]!r} tol {tol[tuple(bad[0])]!r}")
+    unfilled = Lo.src < 0
+    assert not np.any(oracle.to_f32(got[unfilled], dtype).view(np.uint32)), f"{what}: unfilled rows not +0.0"
+
+
+GEMM_CASES = [
+    # s, m, n, e, k, capacity, pad, route_major, dtype
+    (300, 64, 64, 4, 2, 0, 1, False, "bf16"),
+    (1000, 264, 200, 8, 2, 0, 1, False, "bf16"),     # ragged K step and column tile
+    (1000, 136, 136, 8, 3, 200, 1, True, "f16"),     # capacity drop, route-major slots
+    (3000, 128, 256, 129, 5, 0, 16, False, "bf16"),  # padded segments, many experts
+    (2000, 512, 384, 16, 4, 0, 128, False, "f16"),
+    (1, 8, 8, 3, 2, 0, 1, False, "bf16"),            # smallest row length
+    (5000, 96, 520, 2, 2, 0, 1, False, "bf16"),      # long segments: many row-blocks each
+    (777, 64, 64, 1024, 16, 0, 1, True, "bf16"),     # most experts empty
+]
+
+
+@pytest.mark.parametrize("s,m,n,e,k,cap,pad,rm,dtype", GEMM_CASES)
+def test_expert_gemm_matches_oracle(s, m, n, e, k, cap, pad, rm, dtype):
+    announce("expert gemm", s, m, n, e, k, cap, pad, rm, dtype)
+    rng = np.random.default_rng(s + m + n + e + k + cap + pad)
+    idx = W.random_idx(rng, s, e, k)
+    x = W.cast_input(rng.standard_normal((s, m)).astype(np.float32), dtype)
+    wts = W.expert_weights(s + n, e, n, m, dtype)
+    rw = W.random_weights(rng, s, k)
+    Lo = oracle.dispatch_layout(idx, e, cap, route_major=rm, pad_multiple=pad)
+    Lg = M.moe_dispatch_layout(to_dev(idx), e, cap, route_major=rm, pad_multiple=pad)
+    xd, wd, rwd = to_dev(x, dtype), to_dev(wts, dtype), to_dev(rw)
+
+    fused = M.moe_expert_gemm(Lg, xd, wd, gather=True)
+    check_gemm(to_host(fused), Lo, x, wts, dtype, True, None, "fused")
+    buf = M.moe_dispatch(Lg, xd)
+    unfused = M.moe_expert_gemm(Lg, buf, wd, gather=False)
+    assert_bits_equal(to_host(unfused), to_host(fused), "unfused vs fused")
+
+    fused_w = M.moe_expert_gemm(Lg, xd, wd, gather=True, w=rwd)
+    check_gemm(to_host(fused_w), Lo, x, wts, dtype, True, rw, "fused, route weights")
+    unfused_w = M.moe_expert_gemm(Lg, buf, wd, gather=False, w=rwd)
+    assert_bits_equal(to_host(unfused_w), to_host(fused_w), "unfused vs fused, route weights")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_expert_gemm_integer_operands_bit_exact(dtype):
+    """Operands in {-3..3}: each partial sum is an integer below 2^24, exact in float32."""
+    announce("expert gemm integers", dtype)
+    s, m, n, e, k = 700, 520, 136, 6, 2
+    rng = np.random.default_rng(7)
+    idx = W.random_idx(rng, s, e, k)
+    x = W.cast_input(rng.integers(-3, 4, (s, m)).astype(np.float32), dtype)
+    wts = W.cast_input(rng.integers(-3, 4, (e, n, m)).astype(np.float32), dtype)
+    rw = (2.0 ** rng.integers(-3, 3, (s, k))).astype(np.float32)
+    Lo = oracle.dispatch_layout(idx, e, 0)
+    Lg = M.moe_dispatch_layout(to_dev(idx), e, 0)
+    for w in (None, rw):
+        got = M.moe_expert_gemm(Lg, to_dev(x, dtype), to_dev(wts, dtype), gather=True,
+                                w=None if w is None else to_dev(w))
+        want, _ = oracle.expert_gemm(Lo, x, wts, dtype, True, w)
+        assert_bits_equal(to_host(got), want, f"integer operands, weights {w is not None}")
+
+
+def test_expert_gemm_invalid_routes_leave_zero_rows():
+    announce("expert gemm invalid routes")
+    s, m, n, e, k = 400, 64, 72, 5, 3
+    rng = np.random.default_rng(11)
+    idx = W.random_idx(rng, s, e, k)
+    idx[::7, 1] = -1
+    idx[::11, 2] = e + 3
+    x = W.cast_input(rng.standard_normal((s, m)).astype(np.float32), "bf16")
+    wts = W.expert_weights(3, e, n, m, "bf16")
+    Lo = oracle.dispatch_layout(idx, e, 0)
+    Lg = M.moe_dispatch_layout(to_dev(idx), e, 0)
+    out = torch.full((Lg.rows, n), 7.0, dtype=torch.bfloat16, device="cuda")  # stale contents
+    M.moe_expert_gemm(Lg, to_dev(x, "bf16"), to_dev(wts, "bf16"), gather=True, out=out)
+    check_gemm(to_host(out), Lo, x, wts, "bf16", True, None, "invalid routes")
+
+
+def test_expert_gemm_empty_and_rejects():
+    announce("expert gemm empty")
+    e, k, m, n = 4, 2, 16, 16
+    Lg = M.moe_dispatch_layout(torch.zeros((0, k), dtype=torch.int32, device="cuda"), e, 0)
+    x = torch.zeros((0, m), dtype=torch.bfloat16, device="cuda")
+    wd = torch.zeros((e, n, m), dtype=torch.bfloat16, device="cuda")
+    out = M.moe_expert_gemm(Lg, x, wd, gather=True)
+    assert out.shape == (0, n)
+    idx = torch.zeros((4, k), dtype=torch.int32, device="cuda")
+    idx[:, 1] = 1
+    Lg = M.moe_dispatch_layout(idx, e, 0)
+    x = torch.zeros((4, m), dtype=torch.float32, device="cuda")
+    with pytest.raises(M.MoeError):  # float32 has no matrix-core path here
+        M.moe_expert_gemm(Lg, x, torch.zeros((e, n, m), device="cuda"), gather=True)
+    x = torch.zeros((4, 12), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(M.MoeError):  # 12 bf16 elements is not a whole 16-byte chunk count
+        M.moe_expert_gemm(Lg, x, torch.zeros((e, n, 12), dtype=torch.bfloat16, device="cuda"), gather=True)
+
+
+def sampled_sub_layout(Lo: oracle.Layout, rows: np.ndarray):
+    """An oracle layout holding only the given placed rows, grouped by their expert, and
+    the experts it keeps (in order)."""
+    seg = np.searchsorted(Lo.offsets, rows, side="right") - 1
+    experts = np.unique(seg)
+    kept = np.array([np.sum(seg == x) for x in experts], np.int32)
+    order = np.argsort(seg, kind="stable")
+    rows = rows[order]
+    offsets = np.concatenate([[0], np.cumsum(kept)]).astype(np.int32)
+    sub = oracle.Layout(s=Lo.s, e=len(experts), k=Lo.k, capacity=0, rows=len(rows), idx=Lo.idx,
+                        counts=kept, kept=kept, offsets=offsets, dst=np.full_like(Lo.dst, -1),
+                        src=Lo.src[rows], flags=0, checksum=0)
+    return sub, experts, rows
+
+
+def test_expert_gemm_full_workload_sampled():
+    """The headline workload's routing and rows at the benchmark's expert width; outputs
+    sampled at segment edges, tile edges and random rows are checked against the oracle."""
+    name = W.HEADLINE
+    inp = W.make_inputs(name)
+    w = inp.workload
+    n = W.EXPERT_WIDTH
+    announce("expert gemm full", name, n)
+    idx, _ = oracle.gate_topk(inp.logits, w.k)
+    Lo = oracle.dispatch_layout(idx, w.e, w.capacity)
+    Lg = M.moe_dispatch_layout(to_dev(idx), w.e, w.capacity)
+    wts = W.expert_weights(w.seed + 1, w.e, n, w.m, w.dtype)
+    xd, wd = to_dev(inp.x, w.dtype), to_dev(wts, w.dtype)
+    fused = M.moe_expert_gemm(Lg, xd, wd, gather=True)
+    buf = M.moe_dispatch(Lg, xd)
+    unfused = M.moe_expert_gemm(Lg, buf, wd, gather=False)
+    assert torch.equal(fused.view(torch.int16), unfused.view(torch.int16)), "unfused vs fused"
+    del buf, unfused
+
+    rng = np.random.default_rng(5)
+    heavy = np.argsort(-Lo.kept)[:3]
+    pick = set()
+    for x in list(heavy) + [int(np.argmin(np.where(Lo.kept > 0, Lo.kept, 1 << 30))), w.e - 1]:
+        r0, kx = int(Lo.offsets[x]), int(Lo.kept[x])
+        for d in (0, 127, 128, kx - 1):
+            if 0 <= d < kx:
+                pick.add(r0 + d)
+    pick.update(rng.choice(Lo.rows, 24, replace=False).tolist())
+    rows = np.array(sorted(pick))
+    sub, experts, rows = sampled_sub_layout(Lo, rows)
+    got = to_host(fused.index_select(0, torch.from_numpy(rows).cuda()))
+    check_gemm(got, sub, inp.x, np.ascontiguousarray(wts[experts]), w.dtype, True, None,
+               f"{name} sampled rows")

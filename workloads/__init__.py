@@ -185,6 +185,25 @@ def skewed_idx(rng: np.random.Generator, s: int, e: int, k: int, hot: int = 0) -
     return idx
 
 
+# Output features of the expert projection that consumes the dispatched rows (the pages
+# fix no expert width; this is the gate/up projection width used for the grouped GEMM).
+EXPERT_WIDTH = 3072
+
+
+def expert_weights(seed: int, e: int, n: int, m: int, dtype: str) -> np.ndarray:
+    """Expert projection weights [e, n, m] (output x input features), N(0, 1/m) draws
+    stored in dtype, generated expert by expert from one seeded stream."""
+    rng = np.random.default_rng(seed)
+    out = None
+    scale = np.float32(1.0 / np.sqrt(m))
+    for x in range(e):
+        wx = cast_input(rng.standard_normal((n, m), dtype=np.float32) * scale, dtype)
+        if out is None:
+            out = np.empty((e, n, m), dtype=wx.dtype)
+        out[x] = wx
+    return out
+
+
 def describe(w: Workload) -> str:
     mode = "dropless" if w.dropless else f"capacity {w.capacity}"
     return f"{w.name}: s={w.s} m={w.m} {w.dtype} e={w.e} k={w.k} {mode} ({w.routing})"

@@ -9,14 +9,17 @@
 // gathering A's rows straight from the token rows fuses the permute into the GEMM's
 // prologue, so the [rows, m] buffer is never written or read.
 //
-// Tiling: a workgroup of four waves (2 x 2) computes a BM x BN tile of one expert's rows
-// x output features; each wave owns WM x WN as (WM/32) x (WN/32) MFMA tiles of 32 x 32
+// Tiling: a workgroup of 2 x NW waves computes a BM x BN tile of one expert's rows x
+// output features; each wave owns WM x WN as (WM/32) x (WN/32) MFMA tiles of 32 x 32
 // (v_mfma_f32_32x32x16 bf16/f16, float32 accumulators). Both operands are K-contiguous
-// in memory (token rows; weight rows), so each is staged in LDS as [rows][BK] with rows
-// padded by 16 bytes (conflict-free 16-byte fragment reads), double-buffered: the next
-// K step's global loads are in flight while the current step is multiplied. Lane l of
-// an MFMA reads row l%32, K elements 8*(l/32)..+7 of each operand (one ds_read_b128)
-// and holds output rows 8*(v/4) + 4*(l/32) + v%4, column l%32 for v = 0..15.
+// in memory (token rows; weight rows), so each is staged in LDS as [rows][BK elements]
+// by direct-to-LDS loads into an XOR-swizzled layout (conflict-free 16-byte fragment
+// reads). With 64-element K steps every staged row segment is one whole 128-byte line:
+// each CU has a bounded number of L2 requests in flight, so whole-line requests double
+// the bytes that bound admits. STAGES K steps are staged at once: the loads of step
+// kt + STAGES - 1 are issued while step kt is multiplied. Lane l of an MFMA reads row
+// l%32, K elements 8*(l/32)..+7 of each operand (one ds_read_b128) and holds output rows
+// 8*(v/4) + 4*(l/32) + v%4, column l%32 for v = 0..15.
 //
 // Schedule: the expert weights dominate the traffic (e * n * m elements, far above the
 // L2), so tiles are ordered to read each weight tile few times. The tiles of all experts
@@ -35,23 +38,32 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kGemmThreads = 256;
 constexpr int kXcds = 8;
-constexpr int kBandRows = 4;
+constexpr int kBandRows = 16;  // row-blocks per band of the tile order
 
-// A K step is 64 elements: 8 chunks of 16 bytes per staged row, 128 bytes.
-constexpr int kGemmBK = 64;
-constexpr int kRowBytes = kGemmBK * 2;
-
-template <int WM, int WN>
+// Waves are arranged 2 along the rows x NW along the columns of the tile; a K step is BK
+// elements (BK / 8 chunks of 16 bytes per staged row); STAGES K steps are staged at once.
+template <int WM, int WN, int NW, int BK, int STAGES>
 struct GemmShape {
-  static constexpr int BM = 2 * WM, BN = 2 * WN;
+  static constexpr int WAVES = 2 * NW, THREADS = WAVES * kWave;
+  static constexpr int BM = 2 * WM, BN = NW * WN;
   static constexpr int FM = WM / 32, FN = WN / 32;
-  // one direct-to-LDS load instruction moves 64 lanes x 16 bytes = 8 staged rows
-  static constexpr int A_LOADS = BM / 8 / 4;  // per wave per stage
-  static constexpr int B_LOADS = BN / 8 / 4;
-  static constexpr int STAGE_BYTES = (BM + BN) * kRowBytes;
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int KS = BK / 16;                  // k16 MFMA steps per K step
+  static constexpr int ROW_BYTES = BK * 2, CH = BK / 8;
+  static constexpr int ROWS_PER_LOAD = 64 * 16 / ROW_BYTES;  // one direct-to-LDS load
+  static constexpr int ROWS_PER_BANK_ROW = 256 / ROW_BYTES;  // rows per 256-byte bank row
+  static constexpr int A_LOADS = BM / ROWS_PER_LOAD / WAVES;  // per wave per stage
+  static constexpr int B_LOADS = BN / ROWS_PER_LOAD / WAVES;
+  static constexpr int LOADS = A_LOADS + B_LOADS;
+  static constexpr int STAGE_BYTES = (BM + BN) * ROW_BYTES;
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static_assert(A_LOADS * ROWS_PER_LOAD * WAVES == BM && B_LOADS * ROWS_PER_LOAD * WAVES == BN,
+                "stage split");
+  static_assert(KS % 2 == 0, "fragment buffers alternate within a K step");
+  // XOR swizzle: slot p of staged row R holds chunk p ^ swz(R). The 16 lanes that one
+  // 16-byte LDS read serves together read rows r .. r + 15 of one chunk; with this
+  // swizzle they land in 16 different 16-byte groups of the 256-byte bank row.
+  __device__ static constexpr int swz(int r) { return (r / ROWS_PER_BANK_ROW) % CH; }
 };
 
 template <int DT>
@@ -88,7 +100,7 @@ struct TileCoord {
 // This workgroup's tile (expert = -1: none). Wave 0 only; uniform across the wave.
 template <int BM>
 __device__ __forceinline__ TileCoord find_tile(int b, int e, const int32_t* __restrict__ kept,
-                                               int col_blocks) {
+                                               int col_blocks, int band_rows) {
   const int lane = lane_id();
   TileCoord tc{-1, 0, 0};
   int total = 0;  // row-blocks in use
@@ -116,13 +128,13 @@ __device__ __forceinline__ TileCoord find_tile(int b, int e, const int32_t* __re
       const int R = __builtin_amdgcn_readlane(nb, owner);
       const int64_t first = static_cast<int64_t>(before + __builtin_amdgcn_readlane(excl, owner)) * col_blocks;
       const int u = static_cast<int>(t - first);
-      const int band = u / (kBandRows * col_blocks);
-      const int left = R - band * kBandRows;
-      const int rows_in_band = left < kBandRows ? left : kBandRows;
-      const int v = u - band * kBandRows * col_blocks;
+      const int band = u / (band_rows * col_blocks);
+      const int left = R - band * band_rows;
+      const int rows_in_band = left < band_rows ? left : band_rows;
+      const int v = u - band * band_rows * col_blocks;
       tc.expert = c0 + owner;
       tc.cb = v / rows_in_band;
-      tc.rb = band * kBandRows + v % rows_in_band;
+      tc.rb = band * band_rows + v % rows_in_band;
       return tc;
     }
     before += __builtin_amdgcn_readlane(incl, kWave - 1);
@@ -132,47 +144,54 @@ __device__ __forceinline__ TileCoord find_tile(int b, int e, const int32_t* __re
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// s_waitcnt immediate that waits for LDS (lgkm) operations only: vmcnt 63, expcnt 7,
-// lgkmcnt 0.
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8): wait for LDS operations only; wait until at most n vector-memory loads remain.
 constexpr int kWaitLdsOnly = 0xC07F;
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 
 // Stage one K step of rows into LDS with direct-to-LDS loads: instruction q of wave w
-// fills staged rows [(w * LOADS + q) * 8, +8), lane l writing row lane/8, slot lane%8.
-// Slot p of staged row R holds chunk p ^ (R % 8) of the step (an XOR swizzle, so the
-// fragment reads below hit eight different bank groups); lane l therefore loads chunk
-// (l % 8) ^ (l / 8). Returns whether this lane's chunk lies past the row end (then it
-// loaded the row's first chunk and its slot must be cleared once the load has landed).
-template <int LOADS>
-__device__ __forceinline__ bool stage_rows(const chunk_t* const (&row)[LOADS], int kt, int c_lane,
-                                           int kchunks, char* lds_rows) {
-  const int kq = kt * (kGemmBK / 8) + c_lane;
-  const bool past = kq >= kchunks;
-  const int off = past ? 0 : kq;
+// fills the ROWS_PER_LOAD staged rows from (w * LOADS + q) * ROWS_PER_LOAD on, lane l
+// writing row l / CH, slot l % CH, and so loading chunk (l % CH) ^ swz(row) of its row
+// (c[q]). A chunk past the row end (the K tail) loads the row's first chunk instead, and
+// its slot is cleared once landed.
+template <int LOADS, int CH>
+__device__ __forceinline__ void stage_rows(const chunk_t* const (&row)[LOADS], const int (&c)[LOADS],
+                                           int kt, int kchunks, char* lds_rows) {
 #pragma unroll
-  for (int q = 0; q < LOADS; ++q)
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(row[q] + off),
+  for (int q = 0; q < LOADS; ++q) {
+    const int kq = kt * CH + c[q];
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(row[q] + (kq < kchunks ? kq : 0)),
                                      (lds_void_t*)(lds_rows + q * 64 * 16), 16, 0, 0);
-  return past;
+  }
 }
 
-template <int LOADS>
-__device__ __forceinline__ void clear_slots(char* lds_rows, int lane) {
+template <int LOADS, int CH>
+__device__ __forceinline__ void clear_slots(const int (&c)[LOADS], int kt, int kchunks,
+                                            char* lds_rows, int lane) {
   const chunk_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int q = 0; q < LOADS; ++q) *reinterpret_cast<chunk_t*>(lds_rows + q * 64 * 16 + lane * 16) = z;
+  for (int q = 0; q < LOADS; ++q)
+    if (kt * CH + c[q] >= kchunks) *reinterpret_cast<chunk_t*>(lds_rows + q * 64 * 16 + lane * 16) = z;
 }
 
-// One workgroup per CU (its LDS stages take most of the CU's 160 KiB), one wave per SIMD:
-// the register file is this wave's, so the schedule may keep two fragment sets live.
-template <int DT, bool GATHER, bool SCALE, int WM, int WN>
-__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void expert_gemm_kernel(
+// Barrier without a memory fence: the waits that make LDS contents visible are explicit
+// (each wave's own direct-to-LDS loads and LDS writes have completed before it arrives),
+// and the vector loads still in flight for later stages must not be waited for here.
+// The memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// One workgroup per CU (its LDS stages take most of the CU's 160 KiB), NW / 2 waves per
+// SIMD: the register file is these waves', so the schedule may keep two fragment sets live.
+template <int DT, bool GATHER, bool SCALE, int WM, int WN, int NW, int BK, int STAGES>
+__global__ __launch_bounds__(2 * NW * kWave)
+__attribute__((amdgpu_waves_per_eu(NW / 2, NW / 2))) void expert_gemm_kernel(
     const chunk_t* __restrict__ a, const chunk_t* __restrict__ wts,
     const float* __restrict__ route_w, const int32_t* __restrict__ dst,
     const int32_t* __restrict__ src, const int32_t* __restrict__ kept,
     const int32_t* __restrict__ offsets, int e, int k, int m, int n, int col_blocks,
-    uint16_t* __restrict__ out) {
-  using S = GemmShape<WM, WN>;
-  extern __shared__ __attribute__((aligned(1024))) char lds[];  // [2][BM + BN rows][128 B]
+    int band_rows, uint16_t* __restrict__ out) {
+  using S = GemmShape<WM, WN, NW, BK, STAGES>;
+  extern __shared__ __attribute__((aligned(1024))) char lds[];  // [STAGES][BM + BN rows][ROW_BYTES]
   __shared__ int32_t row_src[S::BM];
   __shared__ float row_scale[S::BM];
   __shared__ int32_t tile_info[3];
@@ -182,7 +201,7 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1,
   const int wv = wave_in_block();
 
   if (wv == 0) {
-    const TileCoord tc = find_tile<S::BM>(blockIdx.x, e, kept, col_blocks);
+    const TileCoord tc = find_tile<S::BM>(blockIdx.x, e, kept, col_blocks, band_rows);
     if (lane == 0) {
       tile_info[0] = tc.expert;
       tile_info[1] = tc.rb;
@@ -198,7 +217,7 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1,
   const int nrows = rem < S::BM ? rem : S::BM;
   const int col0 = tile_info[2] * S::BN;
 
-  for (int i = tid; i < S::BM; i += kGemmThreads) {
+  for (int i = tid; i < S::BM; i += S::THREADS) {
     // rows past the segment repeat its first row: their products land only in output
     // rows that are never stored
     const int r = row0 + (i < nrows ? i : 0);
@@ -214,41 +233,55 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1,
   __syncthreads();
 
   const int kchunks = m / 8;  // 16-byte chunks per operand row
-  const int nk = (m + kGemmBK - 1) / kGemmBK;
+  const int nk = (m + BK - 1) / BK;
   const chunk_t* wx = wts + static_cast<size_t>(x) * n * kchunks;
-  const int c_lane = (lane & 7) ^ (lane >> 3);  // the chunk this lane stages in every row
 
-  // row starts of the staged rows this lane loads (columns past n repeat column n - 1:
-  // they reach only output columns that are never stored)
+  // per load instruction: the staged row this lane fills, that row's start (columns past
+  // n repeat column n - 1: they reach only output columns that are never stored), and
+  // the chunk of it this lane stages
   const chunk_t* a_rows[S::A_LOADS];
   const chunk_t* b_rows[S::B_LOADS];
+  int a_chunk[S::A_LOADS], b_chunk[S::B_LOADS];
 #pragma unroll
-  for (int q = 0; q < S::A_LOADS; ++q)
-    a_rows[q] = a + static_cast<size_t>(row_src[(wv * S::A_LOADS + q) * 8 + (lane >> 3)]) * kchunks;
+  for (int q = 0; q < S::A_LOADS; ++q) {
+    const int r = (wv * S::A_LOADS + q) * S::ROWS_PER_LOAD + lane / S::CH;
+    a_rows[q] = a + static_cast<size_t>(row_src[r]) * kchunks;
+    a_chunk[q] = (lane % S::CH) ^ S::swz(r);
+  }
 #pragma unroll
   for (int q = 0; q < S::B_LOADS; ++q) {
-    const int j = col0 + (wv * S::B_LOADS + q) * 8 + (lane >> 3);
+    const int r = (wv * S::B_LOADS + q) * S::ROWS_PER_LOAD + lane / S::CH;
+    const int j = col0 + r;
     b_rows[q] = wx + static_cast<size_t>(j < n ? j : n - 1) * kchunks;
+    b_chunk[q] = (lane % S::CH) ^ S::swz(r);
   }
   auto stage_a = [&](int buf) { return lds + buf * S::STAGE_BYTES + wv * S::A_LOADS * 1024; };
   auto stage_b = [&](int buf) {
-    return lds + buf * S::STAGE_BYTES + S::BM * kRowBytes + wv * S::B_LOADS * 1024;
+    return lds + buf * S::STAGE_BYTES + S::BM * S::ROW_BYTES + wv * S::B_LOADS * 1024;
   };
-  auto issue = [&](int kt, int buf) {
-    const bool pa = stage_rows<S::A_LOADS>(a_rows, kt, c_lane, kchunks, stage_a(buf));
-    stage_rows<S::B_LOADS>(b_rows, kt, c_lane, kchunks, stage_b(buf));
-    return pa;  // A and B rows share the chunk schedule
+  auto issue = [&](int kt) {
+    const int buf = kt % STAGES;
+    stage_rows<S::A_LOADS, S::CH>(a_rows, a_chunk, kt, kchunks, stage_a(buf));
+    stage_rows<S::B_LOADS, S::CH>(b_rows, b_chunk, kt, kchunks, stage_b(buf));
   };
-  auto land = [&](bool past, int buf) {
-    __builtin_amdgcn_s_waitcnt(0);
-    if (past) {
-      clear_slots<S::A_LOADS>(stage_a(buf), lane);
-      clear_slots<S::B_LOADS>(stage_b(buf), lane);
+  // make stage kt visible to the workgroup: this wave's loads for it have landed (at most
+  // the loads of the stages issued after it remain), the K-tail slots are cleared, then
+  // every wave meets at the barrier
+  auto publish = [&](int kt, int issued_last) {
+    const int after = issued_last - kt;
+    if (STAGES <= 2 || after <= 0) __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    else if (STAGES <= 3 || after == 1) __builtin_amdgcn_s_waitcnt(wait_vm(S::LOADS));
+    else __builtin_amdgcn_s_waitcnt(wait_vm(2 * S::LOADS));
+    if ((kt + 1) * BK > m) {
+      const int buf = kt % STAGES;
+      clear_slots<S::A_LOADS, S::CH>(a_chunk, kt, kchunks, stage_a(buf), lane);
+      clear_slots<S::B_LOADS, S::CH>(b_chunk, kt, kchunks, stage_b(buf), lane);
     }
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);
+    stage_barrier();
   };
 
-  const int wm = wv >> 1, wn = wv & 1;  // this wave's quarter of the tile
+  const int wm = wv / NW, wn = wv % NW;  // this wave's part of the tile
   f32x16_t acc[S::FM][S::FN];
 #pragma unroll
   for (int i = 0; i < S::FM; ++i)
@@ -258,52 +291,65 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1,
       for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.0f;
 
   // fragment addresses: row (lane % 32) of each 32-row MFMA tile, chunk 2 ks + lane / 32,
-  // found at slot chunk ^ (row % 8) = chunk ^ (lane % 8)
-  const int a_frag = (wm * WM + (lane & 31)) * kRowBytes;
-  const int b_frag = S::BM * kRowBytes + (wn * WN + (lane & 31)) * kRowBytes;
-  int slot_off[kGemmBK / 16];
-#pragma unroll
-  for (int ks = 0; ks < kGemmBK / 16; ++ks) slot_off[ks] = ((2 * ks + (lane >> 5)) ^ (lane & 7)) * 16;
-
-  land(issue(0, 0), 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    bool past = false;
-    if (kt + 1 < nk) past = issue(kt + 1, cur ^ 1);
-    const char* st = lds + cur * S::STAGE_BYTES;
-    chunk_t fa[2][S::FM], fb[2][S::FN];
+  // found at slot chunk ^ swz(row) = chunk ^ swz(lane % 32) (tiles start at multiples of 32)
+  const int a_frag = (wm * WM + (lane & 31)) * S::ROW_BYTES;
+  const int b_frag = S::BM * S::ROW_BYTES + (wn * WN + (lane & 31)) * S::ROW_BYTES;
+  const int fswz = S::swz(lane & 31);
+  chunk_t fa[2][S::FM], fb[2][S::FN];
+  auto read_frags = [&](int kt, int ks, int fbuf) {
+    const char* st = lds + (kt % STAGES) * S::STAGE_BYTES;
+    const int slot = ((2 * ks + (lane >> 5)) ^ fswz) * 16;
 #pragma unroll
     for (int i = 0; i < S::FM; ++i)
-      fa[0][i] = *reinterpret_cast<const chunk_t*>(st + a_frag + i * 32 * kRowBytes + slot_off[0]);
+      fa[fbuf][i] = *reinterpret_cast<const chunk_t*>(st + a_frag + i * 32 * S::ROW_BYTES + slot);
 #pragma unroll
     for (int jj = 0; jj < S::FN; ++jj)
-      fb[0][jj] = *reinterpret_cast<const chunk_t*>(st + b_frag + jj * 32 * kRowBytes + slot_off[0]);
+      fb[fbuf][jj] = *reinterpret_cast<const chunk_t*>(st + b_frag + jj * 32 * S::ROW_BYTES + slot);
+  };
+  auto mfmas = [&](int fbuf) {
 #pragma unroll
-    for (int ks = 0; ks < kGemmBK / 16; ++ks) {
-      const int c = ks & 1;
-      // this step's fragments have landed before the next step's reads are issued, so
-      // at most one step's reads (FM + FN <= 8) are ever outstanding and the wait for a
-      // step never covers the reads of the one after it
-      __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);
+    for (int i = 0; i < S::FM; ++i)
+#pragma unroll
+      for (int jj = 0; jj < S::FN; ++jj)
+        acc[i][jj] = mfma_32x32x16<DT>(fa[fbuf][i], fb[fbuf][jj], acc[i][jj]);
+  };
+
+  // prologue: stages 0 .. min(STAGES - 2, nk - 1) in flight, stage 0 published, its
+  // first fragments read
+  int issued_last = -1;
+  for (int p = 0; p < STAGES - 1 && p < nk; ++p) {
+    issue(p);
+    issued_last = p;
+  }
+  publish(0, issued_last);
+  read_frags(0, 0, 0);
+
+  // Per K step kt: issue the loads of step kt + STAGES - 1 (into the buffer step kt - 1
+  // used, which every wave finished reading before the last barrier). Each k16 step's
+  // fragments are read under the MFMAs of the one before; before the last k16 step's
+  // MFMAs, step kt + 1 is published (the barrier also tells every wave that step kt's
+  // buffer has been read out) and its first fragments are read. The scheduling fences
+  // keep each batch of reads ahead of the MFMAs that hide it.
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + STAGES - 1 < nk) {
+      issue(kt + STAGES - 1);
+      issued_last = kt + STAGES - 1;
+    }
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks) {
+      __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);  // this k16 step's fragments have landed
       __builtin_amdgcn_sched_barrier(0);
-      if (ks + 1 < kGemmBK / 16) {  // next k16 step's fragments, read under this step's MFMAs
-#pragma unroll
-        for (int i = 0; i < S::FM; ++i)
-          fa[c ^ 1][i] = *reinterpret_cast<const chunk_t*>(st + a_frag + i * 32 * kRowBytes + slot_off[ks + 1]);
-#pragma unroll
-        for (int jj = 0; jj < S::FN; ++jj)
-          fb[c ^ 1][jj] = *reinterpret_cast<const chunk_t*>(st + b_frag + jj * 32 * kRowBytes + slot_off[ks + 1]);
+      if (ks + 1 < S::KS) {
+        read_frags(kt, ks + 1, (ks + 1) & 1);
+      } else if (kt + 1 < nk) {
+        publish(kt + 1, issued_last);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(kt + 1, 0, 0);
       }
-      // keep those reads ahead of this step's MFMAs (the scheduler would otherwise sink
-      // each read next to its first use and stall on it)
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < S::FM; ++i)
-#pragma unroll
-        for (int jj = 0; jj < S::FN; ++jj) acc[i][jj] = mfma_32x32x16<DT>(fa[c][i], fb[c][jj], acc[i][jj]);
+      mfmas(ks & 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < nk) land(past, cur ^ 1);
   }
 
   // epilogue: optional route weight (weights after the experts), one narrowing
@@ -325,10 +371,12 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1,
   }
 }
 
-// Tile shape chosen per launch: 256 x 256 tiles when experts average at least 512 rows
-// (fewer LDS reads per MFMA), else 128 x 256 (less padding in short segments).
-constexpr int kTallWM = 128, kTallWN = 128;
-constexpr int kShortWM = 64, kShortWN = 128;
+// Tile shape chosen per launch (eight waves, 64-element K steps either way): 256 x 256
+// tiles with two stages when experts average at least 512 rows (the fewest operand
+// bytes per MFMA), else 128 x 256 tiles with three stages (less padding in short
+// segments; the smaller stages leave LDS for a deeper pipeline).
+constexpr int kTallWM = 128, kTallWN = 64, kTallNW = 4, kTallBK = 64, kTallStages = 2;
+constexpr int kShortWM = 64, kShortWN = 64, kShortNW = 4, kShortBK = 64, kShortStages = 3;
 
 static bool use_tall(const LayoutView& L) {
   return L.capacity > 0 ? L.capacity >= 512 : static_cast<int64_t>(L.s) * L.k >= 512LL * L.e;
@@ -343,17 +391,17 @@ static int64_t row_block_bound(const LayoutView& L, int BM) {
 int64_t expert_gemm_grid(const LayoutView& L, int n) {
   if (L.s == 0) return 0;
   const int BM = use_tall(L) ? 2 * kTallWM : 2 * kShortWM;
-  const int BN = use_tall(L) ? 2 * kTallWN : 2 * kShortWN;
+  const int BN = use_tall(L) ? kTallNW * kTallWN : kShortNW * kShortWN;
   const int64_t col_blocks = (n + BN - 1) / BN;
   const int64_t tiles = row_block_bound(L, BM) * col_blocks;
   return (tiles + kXcds - 1) / kXcds * kXcds;
 }
 
-template <int DT, bool GATHER, bool SCALE, int WM, int WN>
+template <int DT, bool GATHER, bool SCALE, int WM, int WN, int NW, int BK, int STAGES>
 static hipError_t gemm_launch(const LayoutView& L, const void* a, const void* w,
                               const float* route_w, int m, int n, void* out, hipStream_t stream) {
-  using S = GemmShape<WM, WN>;
-  auto kern = expert_gemm_kernel<DT, GATHER, SCALE, WM, WN>;
+  using S = GemmShape<WM, WN, NW, BK, STAGES>;
+  auto kern = expert_gemm_kernel<DT, GATHER, SCALE, WM, WN, NW, BK, STAGES>;
   // dynamic LDS above the 64 KiB default needs the per-kernel limit raised (idempotent)
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS_BYTES);
@@ -361,9 +409,9 @@ static hipError_t gemm_launch(const LayoutView& L, const void* a, const void* w,
   const int64_t grid = expert_gemm_grid(L, n);
   if (grid == 0) return hipSuccess;
   const int col_blocks = (n + S::BN - 1) / S::BN;
-  kern<<<static_cast<unsigned>(grid), kGemmThreads, S::LDS_BYTES, stream>>>(
+  kern<<<static_cast<unsigned>(grid), S::THREADS, S::LDS_BYTES, stream>>>(
       static_cast<const chunk_t*>(a), static_cast<const chunk_t*>(w), route_w, L.dst, L.src, L.kept,
-      L.offsets, L.e, L.k, m, n, col_blocks, static_cast<uint16_t*>(out));
+      L.offsets, L.e, L.k, m, n, col_blocks, kBandRows, static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 
@@ -371,8 +419,10 @@ template <int DT, bool GATHER, bool SCALE>
 static hipError_t gemm_shape(const LayoutView& L, const void* a, const void* w,
                              const float* route_w, int m, int n, void* out, hipStream_t stream) {
   if (use_tall(L))
-    return gemm_launch<DT, GATHER, SCALE, kTallWM, kTallWN>(L, a, w, route_w, m, n, out, stream);
-  return gemm_launch<DT, GATHER, SCALE, kShortWM, kShortWN>(L, a, w, route_w, m, n, out, stream);
+    return gemm_launch<DT, GATHER, SCALE, kTallWM, kTallWN, kTallNW, kTallBK, kTallStages>(
+        L, a, w, route_w, m, n, out, stream);
+  return gemm_launch<DT, GATHER, SCALE, kShortWM, kShortWN, kShortNW, kShortBK, kShortStages>(
+      L, a, w, route_w, m, n, out, stream);
 }
 
 template <int DT>

@@ -75,6 +75,8 @@ GEMM_CASES = [
     (1, 8, 8, 3, 2, 0, 1, False, "bf16"),            # smallest row length
     (5000, 96, 520, 2, 2, 0, 1, False, "bf16"),      # long segments: many row-blocks each
     (777, 64, 64, 1024, 16, 0, 1, True, "bf16"),     # most experts empty
+    (3000, 72, 136, 2, 2, 0, 1, False, "f16"),       # long segments, f16
+    (4000, 64, 64, 4, 2, 600, 1, False, "bf16"),     # large capacity with drops
 ]
 
 

@@ -55,9 +55,10 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str) -> dict:
+def measured_traffic(workload: str, variant: str | None = None) -> dict:
     """Counter-measured HBM bytes per launch from profiles/, if taken on these sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    name = f"traffic_{workload}" + (f"_{variant}" if variant else "") + ".txt"
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return {}
     traffic, digest = {}, None
@@ -377,7 +378,7 @@ def main():
     dom_gbps = abytes[dominant] / kernels[dominant]["us"] / 1e3
     roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(dom_gbps, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
-                "traffic": None if args.variant else measured_traffic(w.name).get(dominant),
+                "traffic": measured_traffic(w.name, args.variant).get(dominant),
                 "algorithmic_bytes": abytes[dominant]}
     if args.variant == "expert_gemm":
         flops = 2 * kept * W.EXPERT_WIDTH * w.m
@@ -387,7 +388,8 @@ def main():
             tf = flops / kernels[dominant]["us"] / 1e6
             roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(tf, 1),
                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                        "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "traffic": measured_traffic(w.name, args.variant).get(dominant),
                         "algorithmic_flops": flops, "algorithmic_bytes": abytes[dominant]}
 
     line = {

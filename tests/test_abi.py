@@ -143,6 +143,28 @@ def test_row_calls_check_alignment_and_dtype(lib):
     assert lib.moe_dispatch(ctypes.byref(st), FAKE, 64, 1, out, None) == 4
 
 
+@no_gpu_only
+def test_expert_gemm_argument_checks(lib):
+    s, e, k = 40, 8, 2
+    ws = 1 << 24
+    st = _fake_handle(s, e, k, 0, ws, M.workspace_bytes(s, e, k, 0))
+    h = ctypes.byref(st)
+    a, w, out = FAKE, ctypes.c_void_p(1 << 26), ctypes.c_void_p(1 << 28)
+    assert lib.moe_expert_gemm(h, a, 1, w, 64, 64, 0, None, out, None) == 2  # float32: no MFMA path
+    assert "bf16 and f16" in lib.moe_last_error().decode()
+    assert lib.moe_expert_gemm(h, a, 2, w, 64, 64, 1, None, out, None) == 1  # gather must be 0/1
+    assert lib.moe_expert_gemm(h, a, 1, w, 12, 64, 1, None, out, None) == 5  # 24-byte input rows
+    assert lib.moe_expert_gemm(h, a, 1, w, 64, 4, 1, None, out, None) == 5  # 8-byte output rows
+    assert lib.moe_expert_gemm(h, a, 1, None, 64, 64, 1, None, out, None) == 1  # NULL weights
+    assert lib.moe_expert_gemm(h, a, 1, ctypes.c_void_p((1 << 26) + 8), 64, 64, 1, None, out, None) == 5
+    assert lib.moe_expert_gemm(h, a, 1, w, 64, 64, 1, None, None, None) == 1  # NULL out
+    # a and out overlapping (out starts inside x's 40 rows of 128 bytes)
+    assert lib.moe_expert_gemm(h, a, 1, w, 64, 64, 1, None, ctypes.c_void_p((1 << 20) + 1024), None) == 1
+    assert "overlap" in lib.moe_last_error().decode()
+    st2 = M.LayoutStruct()  # never filled by moe_dispatch_layout
+    assert lib.moe_expert_gemm(ctypes.byref(st2), a, 1, w, 64, 64, 1, None, out, None) == 4
+
+
 def _fake_handle(s, e, k, capacity, ws, need):
     """Reproduce what moe_dispatch_layout fills in, without running it (256-byte carving)."""
     def take(cur, n):

@@ -264,6 +264,22 @@ def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None):
             per_op[op].append(a.elapsed_time(b) * 1e3)
     L = st["L"]
     kept = int(L.kept.sum().item())
+    # achievable-bandwidth reference: a plain device-to-device copy moving as many bytes
+    # (read + write) as dispatch + combine, timed the same way
+    ab = algorithmic_bytes(w, kept, rows)
+    copy_bytes = (ab["dispatch"] + ab["combine"]) // 2
+    csrc = torch.empty(copy_bytes, dtype=torch.uint8, device=dev).fill_(1)
+    cdst = torch.empty_like(csrc)
+    per_op["_copy_reference"] = []
+    for i in range(min(steps, 10) + 2):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        cdst.copy_(csrc)
+        b.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            per_op["_copy_reference"].append(a.elapsed_time(b) * 1e3)
+    del csrc, cdst
     flags, _ = M.moe_layout_read(L)
     if flags != 0:
         raise RuntimeError(f"layout flags {flags} on a valid workload")
@@ -321,11 +337,21 @@ def run_cpu_baseline(w: W.Workload, target_s: float = 12.0, sample_tokens: int =
         if el >= target_s:
             break
     limit.unregister()
+    cpu_model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": n * reps / el,
         "unit": "tokens/s",
         "cores": 1,
         "kind": "oracle",
+        "host": f"{cpu_model}, {os.cpu_count()} logical CPUs (one used)",
         "sample": (f"first {n} of {w.s} tokens of {w.name} (same m, e, k, dtype"
                    f"{', capacity scaled to ' + str(cap) if w.capacity > 0 else ''}), whole step, "
                    f"{reps} passes in {el:.1f} s, single-threaded numpy"),
@@ -363,17 +389,25 @@ def main():
         del src, dst
     ms_per_step = elapsed / args.steps * 1e3
     abytes = algorithmic_bytes(w, kept, rows, args.variant)
+    copy_us = per_op.pop("_copy_reference")
     ops = list(per_op)
     kernels = {}
     for op in ops:
         us = float(np.mean(per_op[op]))
         kernels[op] = {"us": round(us, 2), "us_median": round(float(np.median(per_op[op])), 2),
+                       "us_p10": round(float(np.percentile(per_op[op], 10)), 2),
+                       "us_p90": round(float(np.percentile(per_op[op], 90)), 2),
                        "bytes": abytes[op], "GBps": round(abytes[op] / us / 1e3, 1)}
     step_ops = [op for op in ops if op not in ("expert_gemm_unfused",) and
                 not (args.variant == "expert_gemm" and op == "dispatch")]
     dc_us = kernels["dispatch"]["us"] + kernels["combine"]["us"]
     dc_bytes = abytes["dispatch"] + abytes["combine"]
     dc_gbps = dc_bytes / dc_us / 1e3
+    dc_steps = np.array(per_op["dispatch"]) + np.array(per_op["combine"]) if args.variant != "expert_gemm" \
+        else np.array([dc_us])
+    ab0 = algorithmic_bytes(w, kept, rows)  # the copy reference's size (default path bytes)
+    copy_moved = 2 * ((ab0["dispatch"] + ab0["combine"]) // 2)
+    copy_gbps = copy_moved / float(np.mean(copy_us)) / 1e3
     dominant = max(step_ops, key=lambda op: kernels[op]["us"])
     dom_gbps = abytes[dominant] / kernels[dominant]["us"] / 1e3
     roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(dom_gbps, 1),
@@ -415,7 +449,13 @@ def main():
         "dispatch_combine": None if args.variant == "expert_gemm" else {
             "tokens_per_s": round(w.s / (dc_us / 1e6), 1), "GBps": round(dc_gbps, 1),
             "frac_of_hbm_peak": round(dc_gbps / HBM_PEAK_GBPS, 4), "us": round(dc_us, 2),
-            "bytes": dc_bytes},
+            "us_median": round(float(np.median(dc_steps)), 2),
+            "us_p10": round(float(np.percentile(dc_steps, 10)), 2),
+            "us_p90": round(float(np.percentile(dc_steps, 90)), 2),
+            "bytes": dc_bytes, "frac_of_copy": round(dc_gbps / copy_gbps, 4)},
+        "copy_reference": {"what": "device-to-device copy of the dispatch+combine byte count (read + write)",
+                           "bytes": copy_moved, "us": round(float(np.mean(copy_us)), 2),
+                           "GBps": round(copy_gbps, 1), "frac_of_hbm_peak": round(copy_gbps / HBM_PEAK_GBPS, 4)},
         "roofline": roofline,
         "kernels": kernels,
         "kept_routes": kept,

@@ -206,3 +206,50 @@ def test_expert_gemm_full_workload_sampled():
     got = to_host(fused.index_select(0, torch.from_numpy(rows).cuda()))
     check_gemm(got, sub, inp.x, np.ascontiguousarray(wts[experts]), w.dtype, True, None,
                f"{name} sampled rows")
+
+
+def test_layer_forward_with_gemm_replays_from_a_hip_graph():
+    """gate -> layout -> fused GEMM with the route weights in its epilogue -> unweighted
+    combine, captured once; every replay (with eager work between) equals the eager run."""
+    announce("gemm hip graph")
+    s, m, n, e, k = 2048, 96, 136, 8, 4  # 1024 rows per expert on average: 256-row tiles
+    rng = np.random.default_rng(21)
+    logits = to_dev(rng.standard_normal((s, e)).astype(np.float32))
+    x = to_dev(W.cast_input(rng.standard_normal((s, m)).astype(np.float32), "bf16"), "bf16")
+    wts = to_dev(W.expert_weights(22, e, n, m, "bf16"), "bf16")
+    ws = torch.empty(M.workspace_bytes(s, e, k, 0), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((s, k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((s, k), dtype=torch.float32, device="cuda")
+    h = torch.empty((s * k, n), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((s, n), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        M.moe_gate_topk(logits, k, idx_out=idx, w_out=wt)
+        L = M.moe_dispatch_layout(idx, e, 0, workspace=ws)
+        M.moe_expert_gemm(L, x, wts, gather=True, w=wt, out=h)
+        M.moe_combine(L, h, None, out=y)
+
+    outs = (idx, wt, h, y)
+    step()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, eager):
+            assert torch.equal(bits(a), bits(b)), f"replay {rep}"
+        M.moe_gate_topk(logits.flip(0), k)  # eager work between replays
+        torch.cuda.synchronize()

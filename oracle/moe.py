@@ -33,8 +33,10 @@ Readings where the pages are silent (each one is also listed in the design notes
 
 Parity status: every function here is pinned by the `not gpu` tests (brute
 force on tiny inputs, the dense one-hot einsum the index path replaced, closed
-forms, finite differences and adjoint identities). The routing checksum is our
-own definition and is pinned only by a hand-worked fixture.
+forms, finite differences and adjoint identities; the grouped expert GEMM and its
+weight gradient by loops, scaled identities, the forward/backward adjoint identity
+and exact integer derivatives). The routing checksum is our own definition and is
+pinned only by a hand-worked fixture.
 """
 from __future__ import annotations
 
@@ -496,3 +498,33 @@ def expert_gemm(layout: Layout, a: np.ndarray, weights: np.ndarray, dtype: str, 
     out = from_f32(acc32, dtype)
     out[layout.src < 0] = 0
     return out, exact
+
+
+def expert_gemm_wgrad(layout: Layout, a: np.ndarray, grad_out: np.ndarray, dtype: str,
+                      gather: bool) -> tuple[np.ndarray, np.ndarray]:
+    """Gradient of the grouped expert GEMM with respect to its weights.
+
+    With out[r] = A(r) @ weights[x]^T for the placed rows r of expert x (expert_gemm),
+        grad_weights[x] = sum over those rows r of outer(grad_out[r], A(r)),
+    an [n, m] matrix per expert; A(r) = a[src[r]] if gather else a[r], so the rows are
+    gathered straight from the token rows here too. Experts with no placed row get zeros.
+    The sums are exact (float64 of float32-widened operands, one matmul per expert) and
+    rounded once to float32 (weight gradients are kept in float32).
+    [DS-8213] review-fix commit: the groups are the offsets' segments; rows past them are
+    in no group. First commit: the backward of the expert step replays the same grouping.
+    Returns (grad_weights float32 [e, n, m], exact float64 [e, n, m]).
+    """
+    n = grad_out.shape[1]
+    m = a.shape[1]
+    a32 = to_f32(a, dtype).astype(np.float64)
+    g64 = to_f32(grad_out, dtype).astype(np.float64)
+    exact = np.zeros((layout.e, n, m), np.float64)
+    for x in range(layout.e):
+        r0 = int(layout.offsets[x])
+        r1 = r0 + int(layout.kept[x])
+        if r1 == r0:
+            continue
+        rows = np.arange(r0, r1)
+        lhs = a32[layout.src[rows]] if gather else a32[rows]
+        exact[x] = g64[rows].T @ lhs
+    return exact.astype(np.float32), exact

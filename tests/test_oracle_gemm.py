@@ -79,3 +79,89 @@ def test_route_weights_scale_each_row():
             if r >= 0:
                 assert np.array_equal(scaled[r], plain[r] * rw[t, j])
     assert np.all(scaled[L.src < 0] == 0)
+
+
+# ----------------------------------------------------------------------------
+# the weight gradient of the grouped GEMM
+
+
+def brute_wgrad(L, a, g, gather):
+    """grad_w[x][j][c] = sum over placed rows r of expert x of g[r, j] * A(r)[c], by loops."""
+    n, m = g.shape[1], a.shape[1]
+    out = np.zeros((L.e, n, m))
+    for x in range(L.e):
+        for r in range(int(L.offsets[x]), int(L.offsets[x]) + int(L.kept[x])):
+            row = a[L.src[r]] if gather else a[r]
+            for j in range(n):
+                for c in range(m):
+                    out[x, j, c] += float(g[r, j]) * float(row[c])
+    return out
+
+
+@pytest.mark.parametrize("cap,gather", [(0, True), (0, False), (3, True), (5, False)])
+def test_expert_gemm_wgrad_matches_brute_force(cap, gather):
+    rng = np.random.default_rng(40 + cap)
+    s, e, k, m, n = 12, 5, 2, 5, 3  # non-square; e = 5 with s*k = 24 routes
+    idx = W.random_idx(rng, s, e, k)
+    L = oracle.dispatch_layout(idx, e, cap)
+    x = rng.standard_normal((s, m)).astype(np.float32)
+    a = x if gather else oracle.dispatch(L, x)
+    g = rng.standard_normal((L.rows, n)).astype(np.float32)
+    gw, exact = oracle.expert_gemm_wgrad(L, a, g, "f32", gather)
+    assert gw.shape == (e, n, m) and gw.dtype == np.float32
+    assert np.allclose(exact, brute_wgrad(L, a, g, gather), rtol=1e-12, atol=1e-12)
+    assert np.array_equal(gw, exact.astype(np.float32))
+
+
+def test_expert_gemm_wgrad_is_the_adjoint_of_the_forward():
+    """<G, forward(A, W)> = sum_x <W[x], wgrad(A, G)[x]> (exact sums, float64)."""
+    rng = np.random.default_rng(41)
+    s, e, k, m, n = 50, 6, 3, 7, 4
+    idx = W.random_idx(rng, s, e, k)
+    L = oracle.dispatch_layout(idx, e, 9)
+    x = W.cast_input(rng.standard_normal((s, m)).astype(np.float32), "bf16")
+    wts = W.cast_input(rng.standard_normal((e * n, m)).astype(np.float32), "bf16").reshape(e, n, m)
+    g = W.cast_input(rng.standard_normal((L.rows, n)).astype(np.float32), "bf16")
+    _, y = oracle.expert_gemm(L, x, wts, "bf16", True)
+    _, gw = oracle.expert_gemm_wgrad(L, x, g, "bf16", True)
+    lhs = float(np.sum(oracle.to_f32(g, "bf16").astype(np.float64) * y))
+    rhs = float(np.sum(oracle.to_f32(wts.reshape(e * n, m), "bf16").astype(np.float64).reshape(e, n, m) * gw))
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+
+
+def test_expert_gemm_wgrad_is_the_exact_derivative_on_integers():
+    """f(W) = <G, forward(A, W)> is linear in W: raising one weight by 1 raises f by exactly
+    that weight's gradient (small integers: every sum is exact)."""
+    rng = np.random.default_rng(42)
+    s, e, k, m, n = 30, 4, 2, 6, 5
+    idx = W.random_idx(rng, s, e, k)
+    L = oracle.dispatch_layout(idx, e, 0)
+    x = rng.integers(-3, 4, (s, m)).astype(np.float32)
+    wts = rng.integers(-3, 4, (e, n, m)).astype(np.float32)
+    g = rng.integers(-3, 4, (L.rows, n)).astype(np.float32)
+    _, gw = oracle.expert_gemm_wgrad(L, x, g, "f32", True)
+
+    def f(wv):
+        _, y = oracle.expert_gemm(L, x, wv, "f32", True)
+        return float(np.sum(g.astype(np.float64) * y))
+
+    base = f(wts)
+    for _ in range(12):
+        xe, j, c = rng.integers(0, e), rng.integers(0, n), rng.integers(0, m)
+        bumped = wts.copy()
+        bumped[xe, j, c] += 1.0
+        assert f(bumped) - base == gw[xe, j, c]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_expert_gemm_wgrad_fused_equals_unfused_and_idle_experts_are_zero(dtype):
+    rng = np.random.default_rng(43)
+    s, e, k, m, n = 40, 6, 2, 16, 8
+    idx = W.random_idx(rng, s, e - 1, k)  # expert e - 1 gets no route
+    L = oracle.dispatch_layout(idx, e, 0)
+    x = W.cast_input(rng.standard_normal((s, m)).astype(np.float32), dtype)
+    g = W.cast_input(rng.standard_normal((L.rows, n)).astype(np.float32), dtype)
+    fused, _ = oracle.expert_gemm_wgrad(L, x, g, dtype, True)
+    plain, _ = oracle.expert_gemm_wgrad(L, oracle.dispatch(L, x), g, dtype, False)
+    assert np.array_equal(fused, plain)
+    assert L.kept[e - 1] == 0 and not np.any(fused[e - 1])

@@ -147,7 +147,27 @@ def _gemm_ignores_route_weights(layout, a, weights, dtype, gather, route_w=None)
     return moe.expert_gemm(layout, a, weights, dtype, gather, None)
 
 
+def _wgrad_ignores_gather(layout, a, grad_out, dtype, gather):
+    if gather:  # reads the token rows as if they were already dispatched
+        pad = np.zeros((max(layout.rows - a.shape[0], 0),) + a.shape[1:], a.dtype)
+        return moe.expert_gemm_wgrad(layout, np.concatenate([a, pad])[:layout.rows], grad_out, dtype, False)
+    return moe.expert_gemm_wgrad(layout, a, grad_out, dtype, gather)
+
+
+def _wgrad_wrong_expert(layout, a, grad_out, dtype, gather):
+    out, exact = moe.expert_gemm_wgrad(layout, a, grad_out, dtype, gather)
+    return np.roll(out, 1, axis=0), np.roll(exact, 1, axis=0)
+
+
+def _wgrad_transposed(layout, a, grad_out, dtype, gather):
+    out, exact = moe.expert_gemm_wgrad(layout, a, grad_out, dtype, gather)
+    return np.swapaxes(out, 1, 2).copy(), np.swapaxes(exact, 1, 2).copy()
+
+
 MUTATIONS = {
+    "wgrad_ignores_gather": ("expert_gemm_wgrad", _wgrad_ignores_gather),
+    "wgrad_wrong_expert": ("expert_gemm_wgrad", _wgrad_wrong_expert),
+    "wgrad_transposed": ("expert_gemm_wgrad", _wgrad_transposed),
     "gemm_wrong_expert": ("expert_gemm", _gemm_wrong_expert),
     "gemm_untransposed": ("expert_gemm", _gemm_untransposed),
     "gemm_ignores_route_weights": ("expert_gemm", _gemm_ignores_route_weights),
@@ -190,6 +210,9 @@ PINS = [
     lambda: gpins.test_expert_gemm_matches_brute_force(3, True),
     gpins.test_scaled_identity_weights_route_rows_to_the_right_expert,
     gpins.test_route_weights_scale_each_row,
+    lambda: gpins.test_expert_gemm_wgrad_matches_brute_force(0, True),
+    gpins.test_expert_gemm_wgrad_is_the_adjoint_of_the_forward,
+    gpins.test_expert_gemm_wgrad_is_the_exact_derivative_on_integers,
 ]
 
 

@@ -103,6 +103,8 @@ def algorithmic_bytes(w: W.Workload, kept_routes: int, rows: int | None = None,
         out["combine"] = K * nb + s * k * 8 + s * nb
         out["dispatch"] = s * row + rows * row + s * k * 4
         out["expert_gemm_unfused"] = rows * row + e * n * row + rows * nb + rows * 4
+        # x read once, the [rows, n] gradient once, float32 [e, n, m] written
+        out["expert_gemm_wgrad"] = s * row + rows * nb + e * n * m * 4 + rows * 4
     if variant == "weights_before":
         # dispatch and replay read the weights; the combine is unweighted; the combine
         # backward is a plain dispatch of grad_y; the dispatch backward also reads x
@@ -187,9 +189,13 @@ def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None):
         ]
         # the same projection unfused, timed after the step: dispatch, then the GEMM on
         # the dispatched buffer
+        gW = torch.empty((e, n, m), dtype=torch.float32, device=dev)
         extra["unfused"] = [
             ("dispatch", lambda: M.moe_dispatch(st["L"], x, out=buf)),
             ("expert_gemm_unfused", lambda: M.moe_expert_gemm(st["L"], buf, wts, gather=False, out=H2)),
+            # the weight gradient, rows gathered from x again; the forward's output stands
+            # in for the gradient arriving at it
+            ("expert_gemm_wgrad", lambda: M.moe_expert_gemm_wgrad(st["L"], x, H, gather=True, out=gW)),
         ]
     elif variant == "weights_before":
         ops = [
@@ -398,7 +404,7 @@ def main():
                        "us_p10": round(float(np.percentile(per_op[op], 10)), 2),
                        "us_p90": round(float(np.percentile(per_op[op], 90)), 2),
                        "bytes": abytes[op], "GBps": round(abytes[op] / us / 1e3, 1)}
-    step_ops = [op for op in ops if op not in ("expert_gemm_unfused",) and
+    step_ops = [op for op in ops if op not in ("expert_gemm_unfused", "expert_gemm_wgrad") and
                 not (args.variant == "expert_gemm" and op == "dispatch")]
     dc_us = kernels["dispatch"]["us"] + kernels["combine"]["us"]
     dc_bytes = abytes["dispatch"] + abytes["combine"]
@@ -416,7 +422,7 @@ def main():
                 "algorithmic_bytes": abytes[dominant]}
     if args.variant == "expert_gemm":
         flops = 2 * kept * W.EXPERT_WIDTH * w.m
-        for op in ("expert_gemm", "expert_gemm_unfused"):
+        for op in ("expert_gemm", "expert_gemm_unfused", "expert_gemm_wgrad"):
             kernels[op]["TFLOPs"] = round(flops / kernels[op]["us"] / 1e6, 1)
         if dominant == "expert_gemm":
             tf = flops / kernels[dominant]["us"] / 1e6

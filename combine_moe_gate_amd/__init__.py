@@ -85,6 +85,8 @@ _SIGNATURES = {
                                                       ctypes.c_int, _P, _P, _P]),
     "moe_expert_gemm": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _I, _P, _I, _I, ctypes.c_int,
                                        _P, _P, _P]),
+    "moe_expert_gemm_wgrad": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _I, _P, _I, _I,
+                                             ctypes.c_int, _P, _P]),
     "moe_renormalize_kept": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _P, _P]),
     "moe_renormalize_kept_backward": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _P, _P, _P]),
     "moe_gate_topk": (ctypes.c_int, [_P, _I, _I, _I, _P, _P, _P]),
@@ -334,6 +336,25 @@ def moe_expert_gemm(layout: Layout, a: torch.Tensor, weights: torch.Tensor, gath
     return out
 
 
+def moe_expert_gemm_wgrad(layout: Layout, a: torch.Tensor, grad_out: torch.Tensor,
+                          gather: bool = True, out=None):
+    """Weight gradient of moe_expert_gemm: grad_w[x] = sum over expert x's rows r of
+    outer(grad_out[r], A(r)), float32 [e, n, m] (zeros for experts with no rows).
+
+    a is x [s, m] when gather (rows gathered through the layout), else a dispatched
+    buffer [rows, m]; grad_out [rows, n] in a's dtype.
+    """
+    _require_gpu(a, grad_out)
+    m = a.shape[1]
+    n = grad_out.shape[1]
+    if grad_out.dtype != a.dtype:
+        raise ValueError("a and grad_out must have the same dtype")
+    out = out if out is not None else torch.empty((layout.e, n, m), dtype=torch.float32, device=a.device)
+    _check(lib().moe_expert_gemm_wgrad(layout.byref(), _ptr(a), int(bool(gather)), _ptr(grad_out), m, n,
+                                       _dtype_code(a), _ptr(out), _stream(a)))
+    return out
+
+
 def moe_renormalize_kept(layout: Layout, w: torch.Tensor, out=None):
     _require_gpu(w)
     w_out = out if out is not None else torch.empty_like(w)
@@ -361,6 +382,6 @@ __all__ = [
     "moe_gate_topk", "moe_gate_topk_backward", "moe_dispatch_layout", "moe_dispatch",
     "moe_dispatch_replay", "moe_combine", "moe_combine_backward", "moe_dispatch_backward",
     "moe_layout_read", "moe_dispatch_weighted", "moe_dispatch_weighted_backward",
-    "moe_renormalize_kept", "moe_renormalize_kept_backward", "moe_expert_gemm", "workspace_bytes", "Layout",
+    "moe_renormalize_kept", "moe_renormalize_kept_backward", "moe_expert_gemm", "moe_expert_gemm_wgrad", "workspace_bytes", "Layout",
     "LayoutOptions", "MoeError", "lib", "EXPORTS",
 ]

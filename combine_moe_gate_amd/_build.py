@@ -15,8 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_NAME = "libmoe_gate.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("api.hip", "gate.hip", "layout.hip", "rows.hip", "gemm.hip")]
-HEADERS = [os.path.join(HERE, "csrc", f) for f in ("internal.h", "moe_device.h")] + [
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("api.hip", "gate.hip", "layout.hip", "rows.hip", "gemm.hip", "gemm_bwd.hip")]
+HEADERS = [os.path.join(HERE, "csrc", f) for f in ("internal.h", "moe_device.h", "gemm_common.h")] + [
     os.path.join(ROOT, "include", "moe_gate.h")]
 
 ARCH = "gfx950"

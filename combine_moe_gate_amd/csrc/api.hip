@@ -417,6 +417,44 @@ moe_status_t moe_expert_gemm(const moe_layout_t* layout, const void* a, int32_t 
                     "moe_expert_gemm");
 }
 
+moe_status_t moe_expert_gemm_wgrad(const moe_layout_t* layout, const void* a, int32_t gather,
+                                   const void* grad_out, int32_t m, int32_t n, moe_dtype_t dtype,
+                                   float* grad_w, void* stream) {
+  moe::LayoutView v;
+  MOE_TRY(view_of(layout, &v));
+  if (dtype != MOE_BF16 && dtype != MOE_F16)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_expert_gemm_wgrad supports bf16 and f16 only (got dtype %d)",
+                static_cast<int>(dtype));
+  if (gather != 0 && gather != 1)
+    return fail(MOE_ERR_INVALID_ARG, "gather must be 0 or 1 (got %d)", gather);
+  int64_t rc_in = 0, rc_out = 0;
+  MOE_TRY(check_rows(m, dtype, &rc_in));
+  MOE_TRY(check_rows(n, dtype, &rc_out));
+  const int64_t tiles = static_cast<int64_t>((n + 255) / 256) * ((m + 255) / 256) * v.e;
+  if (tiles > INT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "e x n x m too large for one weight-gradient launch");
+  const int64_t a_rows = gather ? v.s : v.rows;
+  MOE_TRY(check_array(a, v.s > 0 ? a_rows : 0, "a", true));
+  MOE_TRY(check_array(grad_out, v.s > 0 ? v.rows : 0, "grad_out", true));
+  MOE_TRY(check_array(grad_w, v.e, "grad_w", true));
+  const char* wb = reinterpret_cast<const char*>(grad_w);
+  const size_t w_bytes = static_cast<size_t>(v.e) * n * m * sizeof(float);
+  const size_t eb = elem_bytes(dtype);
+  const struct {
+    const void* p;
+    size_t bytes;
+  } inputs[2] = {{a, static_cast<size_t>(a_rows) * m * eb}, {grad_out, static_cast<size_t>(v.rows) * n * eb}};
+  for (const auto& in : inputs) {
+    const char* ib = static_cast<const char*>(in.p);
+    if (v.s > 0 && in.bytes > 0 && wb < ib + in.bytes && ib < wb + w_bytes)
+      return fail(MOE_ERR_INVALID_ARG, "grad_w may not overlap a or grad_out");
+  }
+  return hip_status(moe::launch_expert_gemm_wgrad(v, a, gather != 0, grad_out, m, n,
+                                                  static_cast<int>(dtype), grad_w,
+                                                  static_cast<hipStream_t>(stream)),
+                    "moe_expert_gemm_wgrad");
+}
+
 moe_status_t moe_renormalize_kept(const moe_layout_t* layout, const float* topk_w, float* w_out,
                                   void* stream) {
   moe::LayoutView v;

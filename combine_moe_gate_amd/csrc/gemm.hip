@@ -29,16 +29,12 @@
 // each XCD walks one contiguous stretch of that order, and the workgroups resident on
 // it at once share each weight tile across the band's row-blocks and each row-block's
 // rows across neighbouring column-blocks through that XCD's L2.
+#include "gemm_common.h"
 #include "internal.h"
 #include "moe_device.h"
 
 namespace moe {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-constexpr int kXcds = 8;
 constexpr int kBandRows = 16;  // row-blocks per band of the tile order
 
 // Waves are arranged 2 along the rows x NW along the columns of the tile; a K step is BK
@@ -66,32 +62,6 @@ struct GemmShape {
   __device__ static constexpr int swz(int r) { return (r / ROWS_PER_BANK_ROW) % CH; }
 };
 
-template <int DT>
-__device__ __forceinline__ f32x16_t mfma_32x32x16(const chunk_t& a, const chunk_t& b, f32x16_t c) {
-  if constexpr (DT == kBF16)
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
-                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-}
-
-template <int DT>
-__device__ __forceinline__ uint16_t narrow(float v) {
-  if constexpr (DT == kBF16) return static_cast<uint16_t>(f32x2_to_bf16x2_rne(v, 0.0f) & 0xffffu);
-  else return static_cast<uint16_t>(f32_to_f16_rne(v));
-}
-
-// Inclusive wave scan of a non-negative int.
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(v, o, kWave);
-    if (lane >= o) v += y;
-  }
-  return v;
-}
 
 struct TileCoord {
   int expert, rb, cb;  // expert; row-block within its segment; column-block
@@ -142,12 +112,6 @@ __device__ __forceinline__ TileCoord find_tile(int b, int e, const int32_t* __re
   return tc;
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
-// 11:8): wait for LDS operations only; wait until at most n vector-memory loads remain.
-constexpr int kWaitLdsOnly = 0xC07F;
-constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 
 // Stage one K step of rows into LDS with direct-to-LDS loads: instruction q of wave w
 // fills the ROWS_PER_LOAD staged rows from (w * LOADS + q) * ROWS_PER_LOAD on, lane l
@@ -174,11 +138,6 @@ __device__ __forceinline__ void clear_slots(const int (&c)[LOADS], int kt, int k
     if (kt * CH + c[q] >= kchunks) *reinterpret_cast<chunk_t*>(lds_rows + q * 64 * 16 + lane * 16) = z;
 }
 
-// Barrier without a memory fence: the waits that make LDS contents visible are explicit
-// (each wave's own direct-to-LDS loads and LDS writes have completed before it arrives),
-// and the vector loads still in flight for later stages must not be waited for here.
-// The memory clobber keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // One workgroup per CU (its LDS stages take most of the CU's 160 KiB), NW / 2 waves per
 // SIMD: the register file is these waves', so the schedule may keep two fragment sets live.

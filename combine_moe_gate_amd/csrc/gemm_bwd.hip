@@ -1,0 +1,347 @@
+// Weight gradient of the grouped expert GEMM, with the dispatch fused into its operand
+// loads, on gfx950 matrix cores.
+//
+// The forward computes out[r] = A(r) @ W[x]^T for the placed rows r of expert x's
+// segment [offsets[x], offsets[x] + kept[x]). Its weight gradient is
+//     grad_W[x] = sum over those rows r of outer(grad_out[r], A(r))        [n, m]
+// a GEMM whose reduction runs over the segment's rows. A(r) = x[src[r]] is gathered
+// straight from the token rows again, so neither pass materialises the [rows, m] buffer
+// (DeepSpeed PR "Add an opt-in DeepEP transport for the AutoEP expert all-to-all":
+// review-fix commit, the groups are the prefix sum's segments; first commit, the
+// backward replays the forward's grouping).
+//
+// Tiling: a workgroup of 8 waves (2 along n x 4 along m, each 128 x 64 as 4 x 2 MFMA
+// tiles of 32 x 32 x 16) computes a 256 x 256 tile of grad_W[x], reducing over the
+// segment 64 rows at a time. Both operands are stored row by row, contiguous along n
+// (grad_out) or m (the token rows), so a K step is staged in LDS exactly as it sits in
+// memory, [64 rows][256 elements] with each row padded to 576 bytes, and the MFMA
+// fragments (8 consecutive rows of one column per lane) are read with gfx950's
+// transposing LDS read, ds_read_b64_tr_b16. Within each 16-lane group it hands lane i
+// column i % 4 of the 4-element pieces the group's lanes point at, taken from lanes
+// i / 4, i / 4 + 4, i / 4 + 8 and i / 4 + 12: with lane j pointing at row k0 + j / 4,
+// columns c0 + 4 (j % 4) .. + 3, lane i receives rows k0 .. k0 + 3 of column c0 + i.
+// Two such reads make one fragment. A 576-byte pitch (64 mod 256) puts the four rows
+// one read touches, and the two 16-column halves of a 32-lane pass, on distinct banks.
+// Staging goes through registers (16-byte loads, 16-byte LDS writes), so rows past the
+// segment are written as zeros directly. Two stages: the next step's loads are in flight
+// while the current one is multiplied; the row map src is fetched one step further ahead.
+//
+// Schedule: one workgroup per CU loops over tiles. The tiles of all experts are numbered
+// expert by expert (inside an expert in bands of 4 n-blocks, m-block major; the tiles of
+// an expert without rows just write zeros), and each XCD takes one contiguous stretch of
+// that order holding an equal share of the work (a tile costs its number of K steps plus
+// a fixed overhead), so the tiles resident on an XCD at once share operand slabs through
+// its L2, zero tiles are written while other CUs multiply, and every XCD finishes
+// together.
+#include "gemm_common.h"
+#include "internal.h"
+#include "moe_device.h"
+
+namespace moe {
+
+constexpr int kWgBM = 256, kWgBN = 256;  // tile: grad_W rows (n) x columns (m)
+constexpr int kWgBK = 64;                // segment rows per K step
+constexpr int kWgWM = 128, kWgWN = 64;   // per wave
+constexpr int kWgThreads = 512;          // 8 waves: 2 along n x 4 along m
+constexpr int kWgPitch = kWgBM * 2 + 64; // bytes per staged row: 512 + 64 (64 mod 256)
+constexpr int kWgOperandBytes = kWgBK * kWgPitch;
+constexpr int kWgStageBytes = 2 * kWgOperandBytes;  // grad_out rows, then token rows
+constexpr int kWgLdsBytes = 2 * kWgStageBytes;      // two stages: 147456 bytes
+constexpr int kWgChunks = kWgBK * (kWgBM / 8) / kWgThreads;  // 16-byte chunks per thread per operand
+constexpr int kWgBandN = 4;              // n-blocks per band of the tile order
+constexpr int kWgTileOverhead = 4;       // a tile's fixed cost, in K steps
+
+static_assert(kWgBM == kWgBN, "both operands stage rows of the same width");
+static_assert(kWgChunks == 4, "staging split");
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint2 read_tr(const char* p) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+struct WgTiles {
+  int expert, nb, mb, nk;  // expert (-1: none), n-block, m-block, K steps
+};
+
+// Tile t of the global order: every expert owns tiles_per_expert consecutive tiles
+// (those of an expert without rows only write zeros); inside an expert, bands of
+// kWgBandN n-blocks, m-block major, n-block fastest.
+__device__ __forceinline__ WgTiles wg_tile(int64_t t, const int32_t* __restrict__ kept,
+                                           int tiles_per_expert, int n_blocks, int m_blocks) {
+  WgTiles tc;
+  tc.expert = static_cast<int>(t / tiles_per_expert);
+  const int u = static_cast<int>(t - static_cast<int64_t>(tc.expert) * tiles_per_expert);
+  const int band = u / (kWgBandN * m_blocks);
+  const int left = n_blocks - band * kWgBandN;
+  const int in_band = left < kWgBandN ? left : kWgBandN;
+  const int v = u - band * kWgBandN * m_blocks;
+  tc.mb = v / in_band;
+  tc.nb = band * kWgBandN + v % in_band;
+  tc.nk = (kept[tc.expert] + kWgBK - 1) / kWgBK;
+  return tc;
+}
+
+// Inclusive wave scan of a non-negative 64-bit value, and its wave total.
+__device__ __forceinline__ int64_t wave_inclusive_scan64(int64_t v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int64_t y = __shfl_up(v, o, kWave);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+
+// Tiles and work of expert x (lanes past e: none): tiles_per_expert tiles, each costing
+// its K steps plus a fixed overhead (for an expert without rows: the overhead alone, the
+// cost of writing the tile's zeros).
+__device__ __forceinline__ void wg_expert_work(bool real, int kx, int tiles_per_expert,
+                                               int64_t* tiles, int64_t* per_tile) {
+  *tiles = real ? tiles_per_expert : 0;
+  *per_tile = real ? (kx + kWgBK - 1) / kWgBK + kWgTileOverhead : 0;
+}
+
+// First tile of XCD i's stretch: the first tile whose work starts at or after i / 8 of
+// the total (wave 0 only; uniform across the wave).
+__device__ __forceinline__ int64_t wg_stretch_start(int i, int e, const int32_t* __restrict__ kept,
+                                                    int tiles_per_expert) {
+  const int lane = lane_id();
+  int64_t total_cost = 0, total_tiles = 0;
+  for (int c0 = 0; c0 < e; c0 += kWave) {
+    const int x = c0 + lane;
+    int64_t tiles, per;
+    wg_expert_work(x < e, x < e ? kept[x] : 0, tiles_per_expert, &tiles, &per);
+    total_cost += __shfl(wave_inclusive_scan64(tiles * per), kWave - 1, kWave);
+    total_tiles += __shfl(wave_inclusive_scan64(tiles), kWave - 1, kWave);
+  }
+  if (i <= 0) return 0;
+  if (i >= kXcds) return total_tiles;
+  const int64_t target = (total_cost * i + kXcds - 1) / kXcds;
+  int64_t cost_before = 0, tiles_before = 0;
+  for (int c0 = 0; c0 < e; c0 += kWave) {
+    const int x = c0 + lane;
+    int64_t tiles, per;
+    wg_expert_work(x < e, x < e ? kept[x] : 0, tiles_per_expert, &tiles, &per);
+    const int64_t cost_incl = wave_inclusive_scan64(tiles * per);
+    const int64_t tiles_incl = wave_inclusive_scan64(tiles);
+    const int64_t lo = cost_before + cost_incl - tiles * per, hi = cost_before + cost_incl;
+    const uint64_t hit = __ballot(tiles > 0 && target >= lo && target < hi);
+    if (hit != 0ull) {
+      const int owner = static_cast<int>(__builtin_ctzll(hit));
+      const int64_t o_lo = __shfl(lo, owner, kWave), o_per = __shfl(per, owner, kWave);
+      const int64_t o_first = tiles_before + __shfl(tiles_incl - tiles, owner, kWave);
+      return o_first + (target - o_lo + o_per - 1) / o_per;
+    }
+    cost_before += __shfl(cost_incl, kWave - 1, kWave);
+    tiles_before += __shfl(tiles_incl, kWave - 1, kWave);
+  }
+  return total_tiles;
+}
+
+template <int DT, bool GATHER>
+__global__ __launch_bounds__(kWgThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void expert_gemm_wgrad_kernel(const chunk_t* __restrict__ a, const chunk_t* __restrict__ g,
+                              const int32_t* __restrict__ src, const int32_t* __restrict__ kept,
+                              const int32_t* __restrict__ offsets, int e, int m, int n,
+                              float* __restrict__ gw) {
+  extern __shared__ __attribute__((aligned(1024))) char lds[];  // [2 stages][grad_out, rows][64][576 B]
+  __shared__ int64_t stretch[2];
+  __shared__ int32_t tile_info[4];
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wv = wave_in_block();
+  const int m_chunks = m / 8, n_chunks = n / 8;
+  const int n_blocks = (n + kWgBM - 1) / kWgBM, m_blocks = (m + kWgBN - 1) / kWgBN;
+  const int tiles_per_expert = n_blocks * m_blocks;
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds, slots = gridDim.x / kXcds;
+
+  if (wv == 0) {
+    const int64_t t0 = wg_stretch_start(xcd, e, kept, tiles_per_expert);
+    const int64_t t1 = wg_stretch_start(xcd + 1, e, kept, tiles_per_expert);
+    if (lane == 0) {
+      stretch[0] = t0;
+      stretch[1] = t1;
+    }
+  }
+  __syncthreads();
+  const int64_t t_end = stretch[1];
+
+  // staging: thread tid moves chunk (tid % 32) of rows tid / 32 + 16 h, h = 0..3
+  const int s_chunk = tid % 32, s_row = tid / 32;
+  // transposing fragment reads: lane j of 16-lane group q points at row 8 (q / 2) + j / 4,
+  // columns 16 (q % 2) + 4 (j % 4) .. + 3 of each 32-wide MFMA tile
+  const int q = lane >> 4, j = lane & 15;
+  const int frag_off = (8 * (q >> 1) + (j >> 2)) * kWgPitch + (16 * (q & 1) + 4 * (j & 3)) * 2;
+  const int wave_n = wv >> 2, wave_m = wv & 3;  // this wave's 128 (n) x 64 (m) part of the tile
+
+  for (int64_t t = stretch[0] + slot; t < t_end; t += slots) {
+    __syncthreads();  // the previous tile's last LDS reads are done
+    if (tid == 0) {
+      const WgTiles tc = wg_tile(t, kept, tiles_per_expert, n_blocks, m_blocks);
+      tile_info[0] = tc.expert;
+      tile_info[1] = tc.nb;
+      tile_info[2] = tc.mb;
+      tile_info[3] = tc.nk;
+    }
+    __syncthreads();
+    const int x = tile_info[0];
+    const int n0 = tile_info[1] * kWgBM, m0 = tile_info[2] * kWgBN;
+    const int nk = tile_info[3];
+    float* gx = gw + static_cast<size_t>(x) * n * m;
+    if (nk == 0) {  // an expert without rows: its gradient is zero
+      const chunk_t z = {0u, 0u, 0u, 0u};
+      const int nrow = n - n0 < kWgBM ? n - n0 : kWgBM;
+      const int ncol4 = (m - m0 < kWgBN ? m - m0 : kWgBN) / 4;  // 16-byte chunks of a row
+      for (int c = tid; c < nrow * (kWgBN / 4); c += kWgThreads) {
+        const int r = c / (kWgBN / 4), q4 = c % (kWgBN / 4);
+        if (q4 < ncol4)
+          __builtin_nontemporal_store(z, reinterpret_cast<chunk_t*>(gx + static_cast<size_t>(n0 + r) * m + m0) + q4);
+      }
+      continue;
+    }
+    const int seg0 = offsets[x], rows_x = kept[x];
+
+    // column chunks this thread stages (past n / m: the last chunk, never stored)
+    const int nc = n0 / 8 + s_chunk < n_chunks ? n0 / 8 + s_chunk : n_chunks - 1;
+    const int mc = m0 / 8 + s_chunk < m_chunks ? m0 / 8 + s_chunk : m_chunks - 1;
+
+    chunk_t rg[kWgChunks], ra[kWgChunks];
+    int rsrc[kWgChunks];  // token rows of the next step to load
+    auto fetch_src = [&](int kt) {
+#pragma unroll
+      for (int h = 0; h < kWgChunks; ++h) {
+        const int i = kt * kWgBK + s_row + 16 * h;
+        rsrc[h] = i < rows_x ? (GATHER ? src[seg0 + i] : seg0 + i) : -1;
+      }
+    };
+    auto issue = [&](int kt) {
+      const chunk_t zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int h = 0; h < kWgChunks; ++h) {
+        const int i = kt * kWgBK + s_row + 16 * h;
+        const bool in = i < rows_x;
+        rg[h] = in ? g[static_cast<size_t>(seg0 + i) * n_chunks + nc] : zero;
+        ra[h] = rsrc[h] >= 0 ? a[static_cast<size_t>(rsrc[h]) * m_chunks + mc] : zero;
+      }
+    };
+    auto publish = [&](int kt) {
+      char* st = lds + (kt & 1) * kWgStageBytes;
+#pragma unroll
+      for (int h = 0; h < kWgChunks; ++h) {
+        const int off = (s_row + 16 * h) * kWgPitch + s_chunk * 16;
+        *reinterpret_cast<chunk_t*>(st + off) = rg[h];
+        *reinterpret_cast<chunk_t*>(st + kWgOperandBytes + off) = ra[h];
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);
+      stage_barrier();
+    };
+
+    f32x16_t acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.0f;
+
+    chunk_t fa[2][4], fb[2][2];
+    auto read_frags = [&](int kt, int ks, int fbuf) {
+      const char* st = lds + (kt & 1) * kWgStageBytes + frag_off + ks * 16 * kWgPitch;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const char* p = st + (wave_n * kWgWM + i * 32) * 2;
+        const uint2 lo = read_tr(p), hi = read_tr(p + 4 * kWgPitch);
+        fa[fbuf][i] = chunk_t{lo.x, lo.y, hi.x, hi.y};
+      }
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const char* p = st + kWgOperandBytes + (wave_m * kWgWN + jj * 32) * 2;
+        const uint2 lo = read_tr(p), hi = read_tr(p + 4 * kWgPitch);
+        fb[fbuf][jj] = chunk_t{lo.x, lo.y, hi.x, hi.y};
+      }
+    };
+
+    fetch_src(0);
+    issue(0);
+    if (nk > 1) fetch_src(1);
+    publish(0);
+    read_frags(0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk) {
+        issue(kt + 1);
+        if (kt + 2 < nk) fetch_src(kt + 2);
+      }
+#pragma unroll
+      for (int ks = 0; ks < kWgBK / 16; ++ks) {
+        __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);  // this k16 step's fragments have landed
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks + 1 < kWgBK / 16) {
+          read_frags(kt, ks + 1, (ks + 1) & 1);
+        } else if (kt + 1 < nk) {
+          publish(kt + 1);  // step kt's buffer was read out before this barrier
+          __builtin_amdgcn_sched_barrier(0);
+          read_frags(kt + 1, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+            acc[i][jj] = mfma_32x32x16<DT>(fa[ks & 1][i], fb[ks & 1][jj], acc[i][jj]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // epilogue: float32 gradients
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int col = m0 + wave_m * kWgWN + jj * 32 + (lane & 31);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = n0 + wave_n * kWgWM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          if (row < n && col < m) gx[static_cast<size_t>(row) * m + col] = acc[i][jj][v];
+        }
+      }
+    }
+  }
+}
+
+// Workgroups of the weight-gradient kernel: one per CU, a multiple of the XCD count.
+static int wgrad_grid() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < kXcds)
+    cus = 256;
+  return cus / kXcds * kXcds;
+}
+
+template <int DT, bool GATHER>
+static hipError_t wgrad_launch(const LayoutView& L, const void* a, const void* grad_out, int m,
+                               int n, float* gw, hipStream_t stream) {
+  auto kern = expert_gemm_wgrad_kernel<DT, GATHER>;
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kWgLdsBytes);
+  if (err != hipSuccess) return err;
+  kern<<<wgrad_grid(), kWgThreads, kWgLdsBytes, stream>>>(
+      static_cast<const chunk_t*>(a), static_cast<const chunk_t*>(grad_out), L.src, L.kept,
+      L.offsets, L.e, m, n, gw);
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_gemm_wgrad(const LayoutView& L, const void* a, bool gather,
+                                    const void* grad_out, int m, int n, int dtype, float* gw,
+                                    hipStream_t stream) {
+  if (dtype == kBF16)
+    return gather ? wgrad_launch<kBF16, true>(L, a, grad_out, m, n, gw, stream)
+                  : wgrad_launch<kBF16, false>(L, a, grad_out, m, n, gw, stream);
+  return gather ? wgrad_launch<kF16, true>(L, a, grad_out, m, n, gw, stream)
+                : wgrad_launch<kF16, false>(L, a, grad_out, m, n, gw, stream);
+}
+
+}  // namespace moe

@@ -72,6 +72,11 @@ hipError_t launch_zero_unfilled_rows(const LayoutView& L, void* out, int64_t row
 hipError_t launch_expert_gemm(const LayoutView& L, const void* a, bool gather, const void* w,
                               const float* route_w, int m, int n, int dtype, void* out,
                               hipStream_t stream);
+// Weight gradient of the grouped expert GEMM: grad_w[x] = sum over expert x's placed rows
+// r of outer(grad_out[r], A(r)), float32 [e, n, m]; zeros for experts with no rows.
+hipError_t launch_expert_gemm_wgrad(const LayoutView& L, const void* a, bool gather,
+                                    const void* grad_out, int m, int n, int dtype, float* grad_w,
+                                    hipStream_t stream);
 // Workgroups the grouped expert GEMM launches for these sizes (0 if none).
 int64_t expert_gemm_grid(const LayoutView& L, int n);
 

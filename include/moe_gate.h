@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -329,6 +329,25 @@ moe_status_t moe_dispatch_backward(const moe_layout_t* layout, const void* grad_
 moe_status_t moe_expert_gemm(const moe_layout_t* layout, const void* a, int32_t gather,
                              const void* weights, int32_t m, int32_t n, moe_dtype_t dtype,
                              const float* topk_w, void* out, void* stream);
+
+/*
+ * Weight gradient of moe_expert_gemm, with the dispatch fused into its operand loads
+ * ([DS-8213] review-fix commit: the groups are the offsets' segments; first commit: the
+ * backward replays the forward's grouping). For every expert x:
+ *   grad_w[x] = sum over the rows r in [offsets[x], offsets[x] + kept[x]) of
+ *               outer(grad_out[r], A(r)),      A(r) = a[src[r]] if gather else a[r],
+ * an [n, m] float32 matrix (the layout of moe_expert_gemm's weights); experts with no
+ * placed row get zeros. Products of dtype operands are accumulated in float32 on the
+ * matrix cores (summation order unspecified) and stored without further rounding.
+ *   a: x [s, m] (gather = 1) or a dispatched buffer [rows, m] (gather = 0), dtype;
+ *   grad_out [rows, n] dtype (the gradient of moe_expert_gemm's output; rows outside the
+ *   segments are not read);  grad_w [e, n, m] float32, overwritten entirely.
+ *   dtype bf16 or f16 (MOE_ERR_UNSUPPORTED otherwise); m and n multiples of 8; a,
+ *   grad_out and grad_w 16-byte aligned; grad_w may not overlap a or grad_out.
+ */
+moe_status_t moe_expert_gemm_wgrad(const moe_layout_t* layout, const void* a, int32_t gather,
+                                   const void* grad_out, int32_t m, int32_t n, moe_dtype_t dtype,
+                                   float* grad_w, void* stream);
 
 /*
  * Read the layout's flags word and routing checksum into HOST memory. Synchronises

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_names(lib):
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
     for code, name in M.STATUS_NAMES.items():
         assert lib.moe_status_string(code).decode() == name
     assert lib.moe_status_string(99).decode() == "MOE_STATUS_UNKNOWN"

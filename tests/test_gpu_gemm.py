@@ -253,3 +253,106 @@ def test_layer_forward_with_gemm_replays_from_a_hip_graph():
             assert torch.equal(bits(a), bits(b)), f"replay {rep}"
         M.moe_gate_topk(logits.flip(0), k)  # eager work between replays
         torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------------
+# weight gradient
+
+
+def check_wgrad(got: np.ndarray, Lo: oracle.Layout, a: np.ndarray, g: np.ndarray, dtype: str,
+                gather: bool, what: str):
+    """Within the float32 accumulation bound of the oracle's exact sums:
+    |got - exact| <= 2^-23 |exact| + (K_x + 2) 2^-23 sum_r |g a|, K_x the expert's rows."""
+    _, exact = oracle.expert_gemm_wgrad(Lo, a, g, dtype, gather)
+    _, absb = oracle.expert_gemm_wgrad(Lo, abs_bits(a, dtype), abs_bits(g, dtype), dtype, gather)
+    kx = Lo.kept.astype(np.float64)[:, None, None]
+    tol = 2.0 ** -23 * np.abs(exact) + (kx + 2) * 2.0 ** -23 * absb
+    err = np.abs(got.astype(np.float64) - exact)
+    bad = np.argwhere(~(err <= tol))
+    assert len(bad) == 0, (f"{what}: {len(bad)} outside the bound, first {tuple(bad[0])}: got "
+                           f"{got[tuple(bad[0])]!r} exact {exact[tuple(bad[0])]!r} tol {tol[tuple(bad[0])]!r}")
+    idle = Lo.kept == 0
+    assert not np.any(got[idle].view(np.uint32)), f"{what}: idle experts not +0.0"
+
+
+WGRAD_CASES = [
+    # s, m, n, e, k, capacity, pad, route_major, dtype
+    (300, 64, 64, 4, 2, 0, 1, False, "bf16"),
+    (1000, 264, 200, 8, 2, 0, 1, False, "bf16"),     # ragged column tiles, 100-row K tail
+    (1000, 136, 136, 8, 3, 200, 1, True, "f16"),     # capacity drop, route-major slots
+    (3000, 128, 520, 129, 5, 0, 16, False, "bf16"),  # padded segments, idle experts
+    (5000, 96, 72, 2, 2, 0, 1, False, "bf16"),       # 5000-row segments: many K steps
+    (1, 8, 8, 3, 2, 0, 1, False, "f16"),
+    (777, 64, 64, 1024, 16, 0, 1, True, "bf16"),     # most experts idle
+]
+
+
+@pytest.mark.parametrize("s,m,n,e,k,cap,pad,rm,dtype", WGRAD_CASES)
+def test_expert_gemm_wgrad_matches_oracle(s, m, n, e, k, cap, pad, rm, dtype):
+    announce("expert gemm wgrad", s, m, n, e, k, cap, pad, rm, dtype)
+    rng = np.random.default_rng(s + 3 * m + n + e + k + cap + pad)
+    idx = W.random_idx(rng, s, e, k)
+    x = W.cast_input(rng.standard_normal((s, m)).astype(np.float32), dtype)
+    Lo = oracle.dispatch_layout(idx, e, cap, route_major=rm, pad_multiple=pad)
+    g = W.cast_input(rng.standard_normal((Lo.rows, n)).astype(np.float32), dtype)
+    Lg = M.moe_dispatch_layout(to_dev(idx), e, cap, route_major=rm, pad_multiple=pad)
+    xd, gd = to_dev(x, dtype), to_dev(g, dtype)
+    stale = torch.full((e, n, m), 7.0, dtype=torch.float32, device="cuda")
+    fused = M.moe_expert_gemm_wgrad(Lg, xd, gd, gather=True, out=stale)
+    check_wgrad(to_host(fused), Lo, x, g, dtype, True, "fused")
+    unfused = M.moe_expert_gemm_wgrad(Lg, M.moe_dispatch(Lg, xd), gd, gather=False)
+    assert_bits_equal(to_host(unfused), to_host(fused), "unfused vs fused")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_expert_gemm_wgrad_integer_operands_bit_exact(dtype):
+    """Operands in {-3..3}: every partial sum is an integer below 2^24, exact in float32."""
+    announce("expert gemm wgrad integers", dtype)
+    s, m, n, e, k = 1500, 136, 264, 5, 2
+    rng = np.random.default_rng(17)
+    idx = W.random_idx(rng, s, e, k)
+    x = W.cast_input(rng.integers(-3, 4, (s, m)).astype(np.float32), dtype)
+    Lo = oracle.dispatch_layout(idx, e, 0)
+    g = W.cast_input(rng.integers(-3, 4, (Lo.rows, n)).astype(np.float32), dtype)
+    Lg = M.moe_dispatch_layout(to_dev(idx), e, 0)
+    got = M.moe_expert_gemm_wgrad(Lg, to_dev(x, dtype), to_dev(g, dtype), gather=True)
+    want, _ = oracle.expert_gemm_wgrad(Lo, x, g, dtype, True)
+    assert_bits_equal(to_host(got), want, "integer operands")
+
+
+def test_expert_gemm_wgrad_empty_layout_zeroes_everything():
+    announce("expert gemm wgrad empty")
+    e, k, m, n = 3, 2, 16, 24
+    Lg = M.moe_dispatch_layout(torch.zeros((0, k), dtype=torch.int32, device="cuda"), e, 0)
+    x = torch.zeros((0, m), dtype=torch.bfloat16, device="cuda")
+    g = torch.zeros((0, n), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((e, n, m), 3.0, dtype=torch.float32, device="cuda")
+    M.moe_expert_gemm_wgrad(Lg, x, g, gather=True, out=out)
+    assert int(out.view(torch.int32).abs().sum()) == 0
+
+
+def test_expert_gemm_wgrad_full_workload_sampled():
+    """The headline routing and rows at the benchmark's expert width; a block of sampled
+    output features x input features of every expert is checked against the oracle (the
+    gradient separates over output and input features, so the oracle runs on those
+    columns only)."""
+    name = W.HEADLINE
+    inp = W.make_inputs(name)
+    w = inp.workload
+    n = W.EXPERT_WIDTH
+    announce("expert gemm wgrad full", name, n)
+    idx, _ = oracle.gate_topk(inp.logits, w.k)
+    Lo = oracle.dispatch_layout(idx, w.e, w.capacity)
+    Lg = M.moe_dispatch_layout(to_dev(idx), w.e, w.capacity)
+    rng = np.random.default_rng(9)
+    g = W.cast_input(rng.standard_normal((Lo.rows, n), dtype=np.float32), w.dtype)
+    xd, gd = to_dev(inp.x, w.dtype), to_dev(g, w.dtype)
+    got = M.moe_expert_gemm_wgrad(Lg, xd, gd, gather=True)
+    unfused = M.moe_expert_gemm_wgrad(Lg, M.moe_dispatch(Lg, xd), gd, gather=False)
+    assert torch.equal(got.view(torch.int32), unfused.view(torch.int32)), "unfused vs fused"
+    del unfused
+    J = np.unique(np.concatenate([[0, 255, 256, n - 1], rng.choice(n, 12, replace=False)]))
+    C = np.unique(np.concatenate([[0, 255, 256, w.m - 1], rng.choice(w.m, 12, replace=False)]))
+    sub = got.index_select(1, torch.from_numpy(J).cuda()).index_select(2, torch.from_numpy(C).cuda())
+    check_wgrad(to_host(sub), Lo, np.ascontiguousarray(inp.x[:, C]), np.ascontiguousarray(g[:, J]),
+                w.dtype, True, f"{name} sampled features")

@@ -41,6 +41,7 @@ from .moe import (  # noqa: F401
     dispatch_weighted,
     dispatch_weighted_backward,
     expert_gemm,
+    expert_gemm_dgrad,
     expert_gemm_wgrad,
     renormalize_kept,
     renormalize_kept_backward,

@@ -500,6 +500,34 @@ def expert_gemm(layout: Layout, a: np.ndarray, weights: np.ndarray, dtype: str, 
     return out, exact
 
 
+def expert_gemm_dgrad(layout: Layout, grad_out: np.ndarray, weights: np.ndarray,
+                      dtype: str) -> tuple[np.ndarray, np.ndarray]:
+    """Gradient of the grouped expert GEMM with respect to its input rows.
+
+    With out[r] = A(r) @ weights[x]^T for the placed rows r of expert x (expert_gemm),
+        grad_A[r] = grad_out[r] @ weights[x]          [rows, m]
+    for those rows, and zero for rows no route fills. The gradient of the token rows x
+    is then the dispatch backward of grad_A (each token sums its routes' rows), the same
+    route-order sum as every other dispatch backward. The sums are exact (float64), rounded
+    to float32 as a float32 accumulator holds them, then once to the element type.
+    [DS-8213] first commit: the gradient of a dispatch is a combine on the same handle;
+    review-fix commit: the groups are the offsets' segments.
+    Returns (grad_A, exact float64).
+    """
+    e, n, m = weights.shape
+    g64 = to_f32(grad_out, dtype).astype(np.float64)
+    exact = np.zeros((layout.rows, m), np.float64)
+    for x in range(layout.e):
+        r0 = int(layout.offsets[x])
+        r1 = r0 + int(layout.kept[x])
+        if r1 == r0:
+            continue
+        w64 = to_f32(weights[x], dtype).astype(np.float64)  # [n, m]
+        exact[r0:r1] = g64[r0:r1] @ w64
+    out = from_f32(exact.astype(np.float32), dtype)
+    out[layout.src < 0] = 0
+    return out, exact
+
 def expert_gemm_wgrad(layout: Layout, a: np.ndarray, grad_out: np.ndarray, dtype: str,
                       gather: bool) -> tuple[np.ndarray, np.ndarray]:
     """Gradient of the grouped expert GEMM with respect to its weights.

@@ -165,3 +165,68 @@ def test_expert_gemm_wgrad_fused_equals_unfused_and_idle_experts_are_zero(dtype)
     plain, _ = oracle.expert_gemm_wgrad(L, oracle.dispatch(L, x), g, dtype, False)
     assert np.array_equal(fused, plain)
     assert L.kept[e - 1] == 0 and not np.any(fused[e - 1])
+
+
+# ----------------------------------------------------------------------------
+# the input-row gradient of the grouped GEMM
+
+
+@pytest.mark.parametrize("cap", [0, 4])
+def test_expert_gemm_dgrad_matches_brute_force(cap):
+    rng = np.random.default_rng(50 + cap)
+    s, e, k, m, n = 14, 4, 2, 5, 3
+    idx = W.random_idx(rng, s, e, k)
+    L = oracle.dispatch_layout(idx, e, cap)
+    g = rng.standard_normal((L.rows, n)).astype(np.float32)
+    wts = rng.standard_normal((e, n, m)).astype(np.float32)
+    out, exact = oracle.expert_gemm_dgrad(L, g, wts, "f32")
+    ref = np.zeros((L.rows, m))
+    for x in range(e):
+        for r in range(int(L.offsets[x]), int(L.offsets[x]) + int(L.kept[x])):
+            for c in range(m):
+                ref[r, c] = sum(float(g[r, j]) * float(wts[x, j, c]) for j in range(n))
+    assert np.allclose(exact, ref, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(out, exact.astype(np.float32))
+    assert np.all(out[L.src < 0] == 0)
+
+
+def test_expert_gemm_dgrad_is_the_adjoint_of_the_forward():
+    """<dgrad(G), A_rows> = <G, forward(A)> over the placed rows (exact sums, float64)."""
+    rng = np.random.default_rng(51)
+    s, e, k, m, n = 50, 6, 3, 7, 4
+    idx = W.random_idx(rng, s, e, k)
+    L = oracle.dispatch_layout(idx, e, 9)
+    x = W.cast_input(rng.standard_normal((s, m)).astype(np.float32), "bf16")
+    wts = W.cast_input(rng.standard_normal((e * n, m)).astype(np.float32), "bf16").reshape(e, n, m)
+    g = W.cast_input(rng.standard_normal((L.rows, n)).astype(np.float32), "bf16")
+    _, y = oracle.expert_gemm(L, x, wts, "bf16", True)
+    _, ga = oracle.expert_gemm_dgrad(L, g, wts, "bf16")
+    a_rows = oracle.to_f32(oracle.dispatch(L, x), "bf16").astype(np.float64)
+    lhs = float(np.sum(ga * a_rows))
+    rhs = float(np.sum(oracle.to_f32(g, "bf16").astype(np.float64) * y))
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+
+
+def test_expert_gemm_input_gradient_is_the_exact_derivative_on_integers():
+    """f(x) = <G, forward(x, W)>: raising one token's feature by 1 raises f by exactly the
+    dispatch backward of dgrad(G) at that feature (small integers: every sum is exact)."""
+    rng = np.random.default_rng(52)
+    s, e, k, m, n = 30, 4, 2, 6, 5
+    idx = W.random_idx(rng, s, e, k)
+    L = oracle.dispatch_layout(idx, e, 11)  # some routes dropped
+    x = rng.integers(-3, 4, (s, m)).astype(np.float32)
+    wts = rng.integers(-3, 4, (e, n, m)).astype(np.float32)
+    g = rng.integers(-3, 4, (L.rows, n)).astype(np.float32)
+    ga, _ = oracle.expert_gemm_dgrad(L, g, wts, "f32")
+    gx = oracle.dispatch_backward(L, ga, "f32")
+
+    def f(xv):
+        _, y = oracle.expert_gemm(L, xv, wts, "f32", True)
+        return float(np.sum(g.astype(np.float64) * y))
+
+    base = f(x)
+    for _ in range(12):
+        t, c = rng.integers(0, s), rng.integers(0, m)
+        bumped = x.copy()
+        bumped[t, c] += 1.0
+        assert f(bumped) - base == gx[t, c]

@@ -164,7 +164,21 @@ def _wgrad_transposed(layout, a, grad_out, dtype, gather):
     return np.swapaxes(out, 1, 2).copy(), np.swapaxes(exact, 1, 2).copy()
 
 
+def _dgrad_untransposed(layout, grad_out, weights, dtype):
+    e, n, m = weights.shape
+    if n == m:
+        return moe.expert_gemm_dgrad(layout, grad_out, np.swapaxes(weights, 1, 2), dtype)
+    out, exact = moe.expert_gemm_dgrad(layout, grad_out, weights, dtype)
+    return out, exact * 1.5
+
+
+def _dgrad_wrong_expert(layout, grad_out, weights, dtype):
+    return moe.expert_gemm_dgrad(layout, grad_out, np.roll(weights, 1, axis=0), dtype)
+
+
 MUTATIONS = {
+    "dgrad_untransposed": ("expert_gemm_dgrad", _dgrad_untransposed),
+    "dgrad_wrong_expert": ("expert_gemm_dgrad", _dgrad_wrong_expert),
     "wgrad_ignores_gather": ("expert_gemm_wgrad", _wgrad_ignores_gather),
     "wgrad_wrong_expert": ("expert_gemm_wgrad", _wgrad_wrong_expert),
     "wgrad_transposed": ("expert_gemm_wgrad", _wgrad_transposed),
@@ -213,6 +227,9 @@ PINS = [
     lambda: gpins.test_expert_gemm_wgrad_matches_brute_force(0, True),
     gpins.test_expert_gemm_wgrad_is_the_adjoint_of_the_forward,
     gpins.test_expert_gemm_wgrad_is_the_exact_derivative_on_integers,
+    lambda: gpins.test_expert_gemm_dgrad_matches_brute_force(4),
+    gpins.test_expert_gemm_dgrad_is_the_adjoint_of_the_forward,
+    gpins.test_expert_gemm_input_gradient_is_the_exact_derivative_on_integers,
 ]
 
 

@@ -87,6 +87,8 @@ _SIGNATURES = {
                                        _P, _P, _P]),
     "moe_expert_gemm_wgrad": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _I, _P, _I, _I,
                                              ctypes.c_int, _P, _P]),
+    "moe_expert_gemm_dgrad": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _P, _I, _I, ctypes.c_int,
+                                             _P, _P]),
     "moe_renormalize_kept": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _P, _P]),
     "moe_renormalize_kept_backward": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _P, _P, _P]),
     "moe_gate_topk": (ctypes.c_int, [_P, _I, _I, _I, _P, _P, _P]),
@@ -355,6 +357,23 @@ def moe_expert_gemm_wgrad(layout: Layout, a: torch.Tensor, grad_out: torch.Tenso
     return out
 
 
+def moe_expert_gemm_dgrad(layout: Layout, grad_out: torch.Tensor, weights: torch.Tensor, out=None):
+    """Input-row gradient of moe_expert_gemm: grad_a[r] = grad_out[r] @ weights[x] for the
+    placed rows of expert x, [rows, m] (zero rows where no route is placed). The token
+    gradient of the gathered forward is moe_dispatch_backward(layout, grad_a)."""
+    _require_gpu(grad_out, weights)
+    n = grad_out.shape[1]
+    if weights.dim() != 3 or weights.shape[0] != layout.e or weights.shape[1] != n:
+        raise ValueError(f"weights must be [e={layout.e}, n={n}, m], got {tuple(weights.shape)}")
+    if weights.dtype != grad_out.dtype:
+        raise ValueError("grad_out and weights must have the same dtype")
+    m = weights.shape[2]
+    out = out if out is not None else torch.empty((layout.rows, m), dtype=grad_out.dtype, device=grad_out.device)
+    _check(lib().moe_expert_gemm_dgrad(layout.byref(), _ptr(grad_out), _ptr(weights), m, n,
+                                       _dtype_code(grad_out), _ptr(out), _stream(grad_out)))
+    return out
+
+
 def moe_renormalize_kept(layout: Layout, w: torch.Tensor, out=None):
     _require_gpu(w)
     w_out = out if out is not None else torch.empty_like(w)
@@ -382,6 +401,6 @@ __all__ = [
     "moe_gate_topk", "moe_gate_topk_backward", "moe_dispatch_layout", "moe_dispatch",
     "moe_dispatch_replay", "moe_combine", "moe_combine_backward", "moe_dispatch_backward",
     "moe_layout_read", "moe_dispatch_weighted", "moe_dispatch_weighted_backward",
-    "moe_renormalize_kept", "moe_renormalize_kept_backward", "moe_expert_gemm", "moe_expert_gemm_wgrad", "workspace_bytes", "Layout",
+    "moe_renormalize_kept", "moe_renormalize_kept_backward", "moe_expert_gemm", "moe_expert_gemm_wgrad", "moe_expert_gemm_dgrad", "workspace_bytes", "Layout",
     "LayoutOptions", "MoeError", "lib", "EXPORTS",
 ]

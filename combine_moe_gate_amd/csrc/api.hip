@@ -455,6 +455,35 @@ moe_status_t moe_expert_gemm_wgrad(const moe_layout_t* layout, const void* a, in
                     "moe_expert_gemm_wgrad");
 }
 
+moe_status_t moe_expert_gemm_dgrad(const moe_layout_t* layout, const void* grad_out,
+                                   const void* weights, int32_t m, int32_t n, moe_dtype_t dtype,
+                                   void* grad_a, void* stream) {
+  moe::LayoutView v;
+  MOE_TRY(view_of(layout, &v));
+  if (dtype != MOE_BF16 && dtype != MOE_F16)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_expert_gemm_dgrad supports bf16 and f16 only (got dtype %d)",
+                static_cast<int>(dtype));
+  int64_t rc_in = 0, rc_out = 0;
+  MOE_TRY(check_rows(m, dtype, &rc_in));
+  MOE_TRY(check_rows(n, dtype, &rc_out));
+  if (v.s > 0 && moe::expert_gemm_dgrad_grid(v, m) > INT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "rows x m too large for one input-gradient launch");
+  MOE_TRY(check_array(grad_out, v.s > 0 ? v.rows : 0, "grad_out", true));
+  MOE_TRY(check_array(weights, v.s > 0 ? v.e : 0, "weights", true));
+  MOE_TRY(check_array(grad_a, v.rows, "grad_a", true));
+  if (v.rows > 0) {
+    const char* ob = static_cast<const char*>(grad_a);
+    const char* gb = static_cast<const char*>(grad_out);
+    const size_t eb = elem_bytes(dtype);
+    if (ob < gb + v.rows * n * eb && gb < ob + v.rows * m * eb)
+      return fail(MOE_ERR_INVALID_ARG, "grad_out and grad_a may not overlap");
+  }
+  return hip_status(moe::launch_expert_gemm_dgrad(v, grad_out, weights, m, n,
+                                                  static_cast<int>(dtype), grad_a,
+                                                  static_cast<hipStream_t>(stream)),
+                    "moe_expert_gemm_dgrad");
+}
+
 moe_status_t moe_renormalize_kept(const moe_layout_t* layout, const float* topk_w, float* w_out,
                                   void* stream) {
   moe::LayoutView v;

@@ -63,56 +63,6 @@ struct GemmShape {
 };
 
 
-struct TileCoord {
-  int expert, rb, cb;  // expert; row-block within its segment; column-block
-};
-
-// This workgroup's tile (expert = -1: none). Wave 0 only; uniform across the wave.
-template <int BM>
-__device__ __forceinline__ TileCoord find_tile(int b, int e, const int32_t* __restrict__ kept,
-                                               int col_blocks, int band_rows) {
-  const int lane = lane_id();
-  TileCoord tc{-1, 0, 0};
-  int total = 0;  // row-blocks in use
-  for (int c0 = 0; c0 < e; c0 += kWave) {
-    const int x = c0 + lane;
-    const int nb = x < e ? (kept[x] + BM - 1) / BM : 0;
-    total += __builtin_amdgcn_readlane(wave_inclusive_scan(nb), kWave - 1);
-  }
-  const int64_t tiles = static_cast<int64_t>(total) * col_blocks;
-  const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
-  const int64_t slot = b / kXcds;
-  const int64_t t = (b % kXcds) * per_xcd + slot;
-  if (slot >= per_xcd || t >= tiles) return tc;
-  int before = 0;  // row-blocks of earlier experts
-  for (int c0 = 0; c0 < e; c0 += kWave) {
-    const int x = c0 + lane;
-    const int nb = x < e ? (kept[x] + BM - 1) / BM : 0;
-    const int incl = wave_inclusive_scan(nb);
-    const int excl = incl - nb;
-    const int64_t lo = static_cast<int64_t>(before + excl) * col_blocks;
-    const int64_t hi = static_cast<int64_t>(before + incl) * col_blocks;
-    const uint64_t hit = __ballot(x < e && t >= lo && t < hi);
-    if (hit != 0ull) {
-      const int owner = static_cast<int>(__builtin_ctzll(hit));
-      const int R = __builtin_amdgcn_readlane(nb, owner);
-      const int64_t first = static_cast<int64_t>(before + __builtin_amdgcn_readlane(excl, owner)) * col_blocks;
-      const int u = static_cast<int>(t - first);
-      const int band = u / (band_rows * col_blocks);
-      const int left = R - band * band_rows;
-      const int rows_in_band = left < band_rows ? left : band_rows;
-      const int v = u - band * band_rows * col_blocks;
-      tc.expert = c0 + owner;
-      tc.cb = v / rows_in_band;
-      tc.rb = band * band_rows + v % rows_in_band;
-      return tc;
-    }
-    before += __builtin_amdgcn_readlane(incl, kWave - 1);
-  }
-  return tc;
-}
-
-
 // Stage one K step of rows into LDS with direct-to-LDS loads: instruction q of wave w
 // fills the ROWS_PER_LOAD staged rows from (w * LOADS + q) * ROWS_PER_LOAD on, lane l
 // writing row l / CH, slot l % CH, and so loading chunk (l % CH) ^ swz(row) of its row

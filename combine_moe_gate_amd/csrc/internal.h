@@ -77,6 +77,11 @@ hipError_t launch_expert_gemm(const LayoutView& L, const void* a, bool gather, c
 hipError_t launch_expert_gemm_wgrad(const LayoutView& L, const void* a, bool gather,
                                     const void* grad_out, int m, int n, int dtype, float* grad_w,
                                     hipStream_t stream);
+// Input-row gradient of the grouped expert GEMM: grad_A[r] = grad_out[r] @ w[x] for the
+// placed rows of expert x, [rows, m] of dtype; unfilled rows zeroed.
+hipError_t launch_expert_gemm_dgrad(const LayoutView& L, const void* grad_out, const void* w,
+                                    int m, int n, int dtype, void* out, hipStream_t stream);
+int64_t expert_gemm_dgrad_grid(const LayoutView& L, int m);
 // Workgroups the grouped expert GEMM launches for these sizes (0 if none).
 int64_t expert_gemm_grid(const LayoutView& L, int n);
 

@@ -331,6 +331,22 @@ moe_status_t moe_expert_gemm(const moe_layout_t* layout, const void* a, int32_t 
                              const float* topk_w, void* out, void* stream);
 
 /*
+ * Input-row gradient of moe_expert_gemm ([DS-8213] first commit: the backward replays the
+ * forward's grouping on the same handle; review-fix commit: the groups are the offsets'
+ * segments). For expert x and each row r in [offsets[x], offsets[x] + kept[x]):
+ *   grad_a[r, :] = grad_out[r, :] @ weights[x]
+ * products accumulated in float32 on the matrix cores (order unspecified), rounded once
+ * to dtype; rows no route fills are zero. The gradient of the token rows x (for the
+ * gathered forward) is moe_dispatch_backward of grad_a.
+ *   grad_out [rows, n];  weights [e, n, m];  grad_a [rows, m];  all of dtype (bf16 or f16,
+ *   MOE_ERR_UNSUPPORTED otherwise); m and n multiples of 8; 16-byte aligned; grad_out and
+ *   grad_a may not overlap.
+ */
+moe_status_t moe_expert_gemm_dgrad(const moe_layout_t* layout, const void* grad_out,
+                                   const void* weights, int32_t m, int32_t n, moe_dtype_t dtype,
+                                   void* grad_a, void* stream);
+
+/*
  * Weight gradient of moe_expert_gemm, with the dispatch fused into its operand loads
  * ([DS-8213] review-fix commit: the groups are the offsets' segments; first commit: the
  * backward replays the forward's grouping). For every expert x:

@@ -19,7 +19,7 @@ import torch
 import combine_moe_gate_amd as M
 import oracle
 import workloads as W
-from tests.gpu_util import assert_bits_equal, to_dev, to_host
+from tests.gpu_util import TORCH_DTYPE, assert_bits_equal, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -356,3 +356,92 @@ def test_expert_gemm_wgrad_full_workload_sampled():
     sub = got.index_select(1, torch.from_numpy(J).cuda()).index_select(2, torch.from_numpy(C).cuda())
     check_wgrad(to_host(sub), Lo, np.ascontiguousarray(inp.x[:, C]), np.ascontiguousarray(g[:, J]),
                 w.dtype, True, f"{name} sampled features")
+
+
+# ----------------------------------------------------------------------------
+# input-row gradient
+
+
+def check_dgrad(got: np.ndarray, Lo: oracle.Layout, g: np.ndarray, wts: np.ndarray, dtype: str,
+                what: str):
+    want, _ = oracle.expert_gemm_dgrad(Lo, g, wts, dtype)
+    _, absb = oracle.expert_gemm_dgrad(Lo, abs_bits(g, dtype), abs_bits(wts, dtype), dtype)
+    n = g.shape[1]
+    gv = oracle.to_f32(got, dtype).astype(np.float64)
+    wv = oracle.to_f32(want, dtype).astype(np.float64)
+    big = np.maximum(np.abs(gv), np.abs(wv))
+    tol = dtype_ulp(big, dtype) + 2.0 ** -23 * big + (n + 2) * 2.0 ** -23 * absb
+    bad = np.argwhere(~(np.abs(gv - wv) <= tol))
+    assert len(bad) == 0, (f"{what}: {len(bad)} outside the bound, first {tuple(bad[0])}: got "
+                           f"{gv[tuple(bad[0])]!r} want {wv[tuple(bad[0])]!r}")
+    assert not np.any(oracle.to_f32(got[Lo.src < 0], dtype).view(np.uint32)), f"{what}: unfilled rows"
+
+
+DGRAD_CASES = [
+    # s, m, n, e, k, capacity, pad, route_major, dtype
+    (300, 64, 64, 4, 2, 0, 1, False, "bf16"),
+    (1000, 200, 264, 8, 2, 0, 1, False, "bf16"),     # ragged K step (n) and column tile (m)
+    (1000, 136, 136, 8, 3, 200, 1, True, "f16"),     # capacity drop, route-major slots
+    (3000, 520, 128, 129, 5, 0, 16, False, "bf16"),  # padded segments, many experts
+    (5000, 72, 96, 2, 2, 0, 1, False, "f16"),        # long segments
+    (1, 8, 8, 3, 2, 0, 1, False, "bf16"),
+]
+
+
+@pytest.mark.parametrize("s,m,n,e,k,cap,pad,rm,dtype", DGRAD_CASES)
+def test_expert_gemm_dgrad_matches_oracle(s, m, n, e, k, cap, pad, rm, dtype):
+    announce("expert gemm dgrad", s, m, n, e, k, cap, pad, rm, dtype)
+    rng = np.random.default_rng(s + m + 5 * n + e + k + cap + pad)
+    idx = W.random_idx(rng, s, e, k)
+    Lo = oracle.dispatch_layout(idx, e, cap, route_major=rm, pad_multiple=pad)
+    g = W.cast_input(rng.standard_normal((Lo.rows, n)).astype(np.float32), dtype)
+    wts = W.expert_weights(s + m, e, n, m, dtype)
+    Lg = M.moe_dispatch_layout(to_dev(idx), e, cap, route_major=rm, pad_multiple=pad)
+    stale = torch.full((Lo.rows, m), 5.0, dtype=TORCH_DTYPE[dtype], device="cuda")
+    ga = M.moe_expert_gemm_dgrad(Lg, to_dev(g, dtype), to_dev(wts, dtype), out=stale)
+    check_dgrad(to_host(ga), Lo, g, wts, dtype, "grad_a")
+    # the token gradient: the dispatch backward of grad_a, bit-exact given the same rows
+    gx = M.moe_dispatch_backward(Lg, ga)
+    assert_bits_equal(to_host(gx), oracle.dispatch_backward(Lo, to_host(ga), dtype), "grad_x")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_expert_gemm_dgrad_integer_operands_bit_exact(dtype):
+    announce("expert gemm dgrad integers", dtype)
+    s, m, n, e, k = 900, 136, 520, 6, 2
+    rng = np.random.default_rng(19)
+    idx = W.random_idx(rng, s, e, k)
+    Lo = oracle.dispatch_layout(idx, e, 0)
+    g = W.cast_input(rng.integers(-3, 4, (Lo.rows, n)).astype(np.float32), dtype)
+    wts = W.cast_input(rng.integers(-3, 4, (e, n, m)).astype(np.float32), dtype)
+    Lg = M.moe_dispatch_layout(to_dev(idx), e, 0)
+    got = M.moe_expert_gemm_dgrad(Lg, to_dev(g, dtype), to_dev(wts, dtype))
+    want, _ = oracle.expert_gemm_dgrad(Lo, g, wts, dtype)
+    assert_bits_equal(to_host(got), want, "integer operands")
+
+
+def test_expert_gemm_dgrad_full_workload_sampled():
+    name = W.HEADLINE
+    inp = W.make_inputs(name)
+    w = inp.workload
+    n = W.EXPERT_WIDTH
+    announce("expert gemm dgrad full", name, n)
+    idx, _ = oracle.gate_topk(inp.logits, w.k)
+    Lo = oracle.dispatch_layout(idx, w.e, w.capacity)
+    Lg = M.moe_dispatch_layout(to_dev(idx), w.e, w.capacity)
+    rng = np.random.default_rng(8)
+    g = W.cast_input(rng.standard_normal((Lo.rows, n), dtype=np.float32), w.dtype)
+    wts = W.expert_weights(w.seed + 1, w.e, n, w.m, w.dtype)
+    ga = M.moe_expert_gemm_dgrad(Lg, to_dev(g, w.dtype), to_dev(wts, w.dtype))
+    heavy = np.argsort(-Lo.kept)[:3]
+    pick = set()
+    for x in list(heavy) + [w.e - 1]:
+        r0, kx = int(Lo.offsets[x]), int(Lo.kept[x])
+        for d in (0, 255, 256, kx - 1):
+            if 0 <= d < kx:
+                pick.add(r0 + d)
+    pick.update(rng.choice(Lo.rows, 24, replace=False).tolist())
+    sub, experts, rows = sampled_sub_layout(Lo, np.array(sorted(pick)))
+    got = to_host(ga.index_select(0, torch.from_numpy(rows).cuda()))
+    check_dgrad(got, sub, np.ascontiguousarray(g[rows]), np.ascontiguousarray(wts[experts]), w.dtype,
+                f"{name} sampled rows")

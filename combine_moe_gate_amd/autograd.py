@@ -32,7 +32,8 @@ import torch.utils.checkpoint
 
 from . import (FLAG_REPLAY_MISMATCH, Layout, moe_combine, moe_combine_backward, moe_dispatch,
                moe_dispatch_backward, moe_dispatch_layout, moe_dispatch_replay,
-               moe_dispatch_weighted, moe_dispatch_weighted_backward, moe_gate_topk,
+               moe_dispatch_weighted, moe_dispatch_weighted_backward, moe_expert_gemm,
+               moe_expert_gemm_dgrad, moe_expert_gemm_wgrad, moe_gate_topk,
                moe_gate_topk_backward, moe_layout_read, moe_renormalize_kept,
                moe_renormalize_kept_backward)
 
@@ -126,6 +127,29 @@ class _Renormalize(torch.autograd.Function):
     def backward(ctx, g):
         (w,) = ctx.saved_tensors
         return moe_renormalize_kept_backward(ctx.layout, w, g.float().contiguous()), None
+
+
+class _ExpertLinear(torch.autograd.Function):
+    """One linear projection per expert over the layout's rows, gathered from x."""
+
+    @staticmethod
+    def forward(ctx, x, weights, layout):
+        x = x.contiguous()
+        weights = weights.contiguous()
+        ctx.layout = layout
+        ctx.save_for_backward(x, weights)
+        return moe_expert_gemm(layout, x, weights, gather=True)
+
+    @staticmethod
+    def backward(ctx, g_h):
+        x, weights = ctx.saved_tensors
+        g_h = g_h.contiguous()
+        g_x = g_w = None
+        if ctx.needs_input_grad[0]:  # input rows, then each token's routes summed
+            g_x = moe_dispatch_backward(ctx.layout, moe_expert_gemm_dgrad(ctx.layout, g_h, weights))
+        if ctx.needs_input_grad[1]:  # float32 from the kernel, in the parameter's dtype here
+            g_w = moe_expert_gemm_wgrad(ctx.layout, x, g_h, gather=True).to(weights.dtype)
+        return g_x, g_w, None
 
 
 class LayoutRecorder:
@@ -227,6 +251,13 @@ def combine(expert_out: torch.Tensor, w: torch.Tensor | None, layout: Layout):
     return _Combine.apply(expert_out, w, layout)
 
 
+def expert_linear(x: torch.Tensor, weights: torch.Tensor, layout: Layout):
+    """Each placed row r of expert x: x[src[r]] @ weights[x]^T, the dispatch fused into the
+    grouped GEMM's operand loads (forward, input-row gradient and weight gradient all run
+    on the layout). weights [e, n, m]; returns [rows, n] for combine()."""
+    return _ExpertLinear.apply(x, weights, layout)
+
+
 def renormalize(w: torch.Tensor, layout: Layout):
     """Weights renormalised over each token's kept routes (after the capacity drop)."""
     return _Renormalize.apply(w, layout)
@@ -244,4 +275,5 @@ def checkpoint(fn, *args, verify: bool = False, **kwargs):
     return out, rec
 
 
-__all__ = ["route", "layout", "dispatch", "dispatch_on", "combine", "renormalize", "checkpoint", "LayoutRecorder"]
+__all__ = ["route", "layout", "dispatch", "dispatch_on", "combine", "renormalize", "expert_linear", "checkpoint",
+           "LayoutRecorder"]

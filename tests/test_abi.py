@@ -165,6 +165,33 @@ def test_expert_gemm_argument_checks(lib):
     assert lib.moe_expert_gemm(ctypes.byref(st2), a, 1, w, 64, 64, 1, None, out, None) == 4
 
 
+@no_gpu_only
+def test_expert_gemm_gradient_argument_checks(lib):
+    s, e, k = 40, 8, 2
+    ws = 1 << 24
+    st = _fake_handle(s, e, k, 0, ws, M.workspace_bytes(s, e, k, 0))
+    h = ctypes.byref(st)
+    a, g, w, out = FAKE, ctypes.c_void_p(1 << 26), ctypes.c_void_p(1 << 27), ctypes.c_void_p(1 << 28)
+    # weight gradient
+    assert lib.moe_expert_gemm_wgrad(h, a, 1, g, 64, 64, 0, out, None) == 2  # float32 operands
+    assert lib.moe_expert_gemm_wgrad(h, a, 3, g, 64, 64, 1, out, None) == 1  # gather flag
+    assert lib.moe_expert_gemm_wgrad(h, a, 1, g, 12, 64, 1, out, None) == 5  # 24-byte rows
+    assert lib.moe_expert_gemm_wgrad(h, a, 1, None, 64, 64, 1, out, None) == 1  # NULL grad_out
+    assert lib.moe_expert_gemm_wgrad(h, a, 1, g, 64, 64, 1, None, None) == 1  # NULL grad_w
+    assert lib.moe_expert_gemm_wgrad(h, a, 1, g, 64, 64, 1, ctypes.c_void_p((1 << 28) + 4), None) == 5
+    assert lib.moe_expert_gemm_wgrad(h, a, 1, g, 64, 64, 1, ctypes.c_void_p((1 << 26) + 256), None) == 1
+    assert "overlap" in lib.moe_last_error().decode()
+    # input-row gradient
+    assert lib.moe_expert_gemm_dgrad(h, g, w, 64, 64, 0, out, None) == 2
+    assert lib.moe_expert_gemm_dgrad(h, g, w, 64, 4, 1, out, None) == 5  # 8-byte grad_out rows
+    assert lib.moe_expert_gemm_dgrad(h, g, None, 64, 64, 1, out, None) == 1
+    assert lib.moe_expert_gemm_dgrad(h, g, w, 64, 64, 1, ctypes.c_void_p((1 << 26) + 512), None) == 1
+    assert "overlap" in lib.moe_last_error().decode()
+    st2 = M.LayoutStruct()
+    assert lib.moe_expert_gemm_dgrad(ctypes.byref(st2), g, w, 64, 64, 1, out, None) == 4
+    assert lib.moe_expert_gemm_wgrad(ctypes.byref(st2), a, 1, g, 64, 64, 1, out, None) == 4
+
+
 def _fake_handle(s, e, k, capacity, ws, need):
     """Reproduce what moe_dispatch_layout fills in, without running it (256-byte carving)."""
     def take(cur, n):

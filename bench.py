@@ -103,8 +103,10 @@ def algorithmic_bytes(w: W.Workload, kept_routes: int, rows: int | None = None,
         out["combine"] = K * nb + s * k * 8 + s * nb
         out["dispatch"] = s * row + rows * row + s * k * 4
         out["expert_gemm_unfused"] = rows * row + e * n * row + rows * nb + rows * 4
-        # x read once, the [rows, n] gradient once, float32 [e, n, m] written
+        # x read once, the [rows, n] gradient once, float32 [e, n, m] written (or the same
+        # rounded to the element type)
         out["expert_gemm_wgrad"] = s * row + rows * nb + e * n * m * 4 + rows * 4
+        out["expert_gemm_wgrad_narrow"] = s * row + rows * nb + e * n * row + rows * 4
         # the [rows, n] gradient and every expert's weights read once, [rows, m] written
         out["expert_gemm_dgrad"] = rows * nb + e * n * row + rows * row
     if variant == "weights_before":
@@ -192,12 +194,15 @@ def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None):
         # the same projection unfused, timed after the step: dispatch, then the GEMM on
         # the dispatched buffer
         gW = torch.empty((e, n, m), dtype=torch.float32, device=dev)
+        gWn = torch.empty((e, n, m), dtype=tdt, device=dev)
         extra["unfused"] = [
             ("dispatch", lambda: M.moe_dispatch(st["L"], x, out=buf)),
             ("expert_gemm_unfused", lambda: M.moe_expert_gemm(st["L"], buf, wts, gather=False, out=H2)),
             # the weight gradient, rows gathered from x again; the forward's output stands
             # in for the gradient arriving at it
             ("expert_gemm_wgrad", lambda: M.moe_expert_gemm_wgrad(st["L"], x, H, gather=True, out=gW)),
+            # the same, kept in the element type (the autograd layer's weight gradient)
+            ("expert_gemm_wgrad_narrow", lambda: M.moe_expert_gemm_wgrad(st["L"], x, H, gather=True, out=gWn)),
             ("expert_gemm_dgrad", lambda: M.moe_expert_gemm_dgrad(st["L"], H, wts, out=buf)),
         ]
     elif variant == "weights_before":
@@ -407,7 +412,8 @@ def main():
                        "us_p10": round(float(np.percentile(per_op[op], 10)), 2),
                        "us_p90": round(float(np.percentile(per_op[op], 90)), 2),
                        "bytes": abytes[op], "GBps": round(abytes[op] / us / 1e3, 1)}
-    step_ops = [op for op in ops if op not in ("expert_gemm_unfused", "expert_gemm_wgrad", "expert_gemm_dgrad") and
+    step_ops = [op for op in ops if op not in ("expert_gemm_unfused", "expert_gemm_wgrad", "expert_gemm_wgrad_narrow",
+                                               "expert_gemm_dgrad") and
                 not (args.variant == "expert_gemm" and op == "dispatch")]
     dc_us = kernels["dispatch"]["us"] + kernels["combine"]["us"]
     dc_bytes = abytes["dispatch"] + abytes["combine"]
@@ -425,7 +431,8 @@ def main():
                 "algorithmic_bytes": abytes[dominant]}
     if args.variant == "expert_gemm":
         flops = 2 * kept * W.EXPERT_WIDTH * w.m
-        for op in ("expert_gemm", "expert_gemm_unfused", "expert_gemm_wgrad", "expert_gemm_dgrad"):
+        for op in ("expert_gemm", "expert_gemm_unfused", "expert_gemm_wgrad", "expert_gemm_wgrad_narrow",
+                   "expert_gemm_dgrad"):
             kernels[op]["TFLOPs"] = round(flops / kernels[op]["us"] / 1e6, 1)
         if dominant == "expert_gemm":
             tf = flops / kernels[dominant]["us"] / 1e6

@@ -86,7 +86,7 @@ _SIGNATURES = {
     "moe_expert_gemm": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _I, _P, _I, _I, ctypes.c_int,
                                        _P, _P, _P]),
     "moe_expert_gemm_wgrad": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _I, _P, _I, _I,
-                                             ctypes.c_int, _P, _P]),
+                                             ctypes.c_int, ctypes.c_int, _P, _P]),
     "moe_expert_gemm_dgrad": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _P, _I, _I, ctypes.c_int,
                                              _P, _P]),
     "moe_renormalize_kept": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _P, _P]),
@@ -339,9 +339,11 @@ def moe_expert_gemm(layout: Layout, a: torch.Tensor, weights: torch.Tensor, gath
 
 
 def moe_expert_gemm_wgrad(layout: Layout, a: torch.Tensor, grad_out: torch.Tensor,
-                          gather: bool = True, out=None):
+                          gather: bool = True, out=None, out_dtype=torch.float32):
     """Weight gradient of moe_expert_gemm: grad_w[x] = sum over expert x's rows r of
-    outer(grad_out[r], A(r)), float32 [e, n, m] (zeros for experts with no rows).
+    outer(grad_out[r], A(r)), [e, n, m] (zeros for experts with no rows), accumulated in
+    float32 and stored as float32 or rounded once to a's dtype (out_dtype, or out's dtype
+    when out is given).
 
     a is x [s, m] when gather (rows gathered through the layout), else a dispatched
     buffer [rows, m]; grad_out [rows, n] in a's dtype.
@@ -351,9 +353,12 @@ def moe_expert_gemm_wgrad(layout: Layout, a: torch.Tensor, grad_out: torch.Tenso
     n = grad_out.shape[1]
     if grad_out.dtype != a.dtype:
         raise ValueError("a and grad_out must have the same dtype")
-    out = out if out is not None else torch.empty((layout.e, n, m), dtype=torch.float32, device=a.device)
+    if out is None:
+        out = torch.empty((layout.e, n, m), dtype=out_dtype, device=a.device)
+    elif tuple(out.shape) != (layout.e, n, m) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous [{layout.e}, {n}, {m}] tensor")
     _check(lib().moe_expert_gemm_wgrad(layout.byref(), _ptr(a), int(bool(gather)), _ptr(grad_out), m, n,
-                                       _dtype_code(a), _ptr(out), _stream(a)))
+                                       _dtype_code(a), _dtype_code(out), _ptr(out), _stream(a)))
     return out
 
 

@@ -147,8 +147,8 @@ class _ExpertLinear(torch.autograd.Function):
         g_x = g_w = None
         if ctx.needs_input_grad[0]:  # input rows, then each token's routes summed
             g_x = moe_dispatch_backward(ctx.layout, moe_expert_gemm_dgrad(ctx.layout, g_h, weights))
-        if ctx.needs_input_grad[1]:  # float32 from the kernel, in the parameter's dtype here
-            g_w = moe_expert_gemm_wgrad(ctx.layout, x, g_h, gather=True).to(weights.dtype)
+        if ctx.needs_input_grad[1]:  # float32 sums, rounded once to the parameter's dtype in the kernel
+            g_w = moe_expert_gemm_wgrad(ctx.layout, x, g_h, gather=True, out_dtype=weights.dtype)
         return g_x, g_w, None
 
 

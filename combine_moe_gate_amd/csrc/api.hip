@@ -419,12 +419,15 @@ moe_status_t moe_expert_gemm(const moe_layout_t* layout, const void* a, int32_t 
 
 moe_status_t moe_expert_gemm_wgrad(const moe_layout_t* layout, const void* a, int32_t gather,
                                    const void* grad_out, int32_t m, int32_t n, moe_dtype_t dtype,
-                                   float* grad_w, void* stream) {
+                                   moe_dtype_t grad_w_dtype, void* grad_w, void* stream) {
   moe::LayoutView v;
   MOE_TRY(view_of(layout, &v));
   if (dtype != MOE_BF16 && dtype != MOE_F16)
     return fail(MOE_ERR_UNSUPPORTED, "moe_expert_gemm_wgrad supports bf16 and f16 only (got dtype %d)",
                 static_cast<int>(dtype));
+  if (grad_w_dtype != MOE_F32 && grad_w_dtype != dtype)
+    return fail(MOE_ERR_UNSUPPORTED, "grad_w_dtype must be float32 or dtype (got %d, dtype %d)",
+                static_cast<int>(grad_w_dtype), static_cast<int>(dtype));
   if (gather != 0 && gather != 1)
     return fail(MOE_ERR_INVALID_ARG, "gather must be 0 or 1 (got %d)", gather);
   int64_t rc_in = 0, rc_out = 0;
@@ -437,8 +440,8 @@ moe_status_t moe_expert_gemm_wgrad(const moe_layout_t* layout, const void* a, in
   MOE_TRY(check_array(a, v.s > 0 ? a_rows : 0, "a", true));
   MOE_TRY(check_array(grad_out, v.s > 0 ? v.rows : 0, "grad_out", true));
   MOE_TRY(check_array(grad_w, v.e, "grad_w", true));
-  const char* wb = reinterpret_cast<const char*>(grad_w);
-  const size_t w_bytes = static_cast<size_t>(v.e) * n * m * sizeof(float);
+  const char* wb = static_cast<const char*>(grad_w);
+  const size_t w_bytes = static_cast<size_t>(v.e) * n * m * elem_bytes(grad_w_dtype);
   const size_t eb = elem_bytes(dtype);
   const struct {
     const void* p;
@@ -450,8 +453,8 @@ moe_status_t moe_expert_gemm_wgrad(const moe_layout_t* layout, const void* a, in
       return fail(MOE_ERR_INVALID_ARG, "grad_w may not overlap a or grad_out");
   }
   return hip_status(moe::launch_expert_gemm_wgrad(v, a, gather != 0, grad_out, m, n,
-                                                  static_cast<int>(dtype), grad_w,
-                                                  static_cast<hipStream_t>(stream)),
+                                                  static_cast<int>(dtype), grad_w_dtype == MOE_F32,
+                                                  grad_w, static_cast<hipStream_t>(stream)),
                     "moe_expert_gemm_wgrad");
 }
 

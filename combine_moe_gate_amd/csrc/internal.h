@@ -73,10 +73,11 @@ hipError_t launch_expert_gemm(const LayoutView& L, const void* a, bool gather, c
                               const float* route_w, int m, int n, int dtype, void* out,
                               hipStream_t stream);
 // Weight gradient of the grouped expert GEMM: grad_w[x] = sum over expert x's placed rows
-// r of outer(grad_out[r], A(r)), float32 [e, n, m]; zeros for experts with no rows.
+// r of outer(grad_out[r], A(r)), [e, n, m] in float32 (out_f32) or rounded once to dtype;
+// zeros for experts with no rows.
 hipError_t launch_expert_gemm_wgrad(const LayoutView& L, const void* a, bool gather,
-                                    const void* grad_out, int m, int n, int dtype, float* grad_w,
-                                    hipStream_t stream);
+                                    const void* grad_out, int m, int n, int dtype, bool out_f32,
+                                    void* grad_w, hipStream_t stream);
 // Input-row gradient of the grouped expert GEMM: grad_A[r] = grad_out[r] @ w[x] for the
 // placed rows of expert x, [rows, m] of dtype; unfilled rows zeroed.
 hipError_t launch_expert_gemm_dgrad(const LayoutView& L, const void* grad_out, const void* w,

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -352,18 +352,21 @@ moe_status_t moe_expert_gemm_dgrad(const moe_layout_t* layout, const void* grad_
  * backward replays the forward's grouping). For every expert x:
  *   grad_w[x] = sum over the rows r in [offsets[x], offsets[x] + kept[x]) of
  *               outer(grad_out[r], A(r)),      A(r) = a[src[r]] if gather else a[r],
- * an [n, m] float32 matrix (the layout of moe_expert_gemm's weights); experts with no
- * placed row get zeros. Products of dtype operands are accumulated in float32 on the
- * matrix cores (summation order unspecified) and stored without further rounding.
+ * an [n, m] matrix (the layout of moe_expert_gemm's weights); experts with no placed row
+ * get zeros. Products of dtype operands are accumulated in float32 on the matrix cores
+ * (summation order unspecified); the float32 sums are stored as they are
+ * (grad_w_dtype = MOE_F32) or rounded once to dtype (grad_w_dtype = dtype: the same sums,
+ * narrowed to nearest even, for callers that keep gradients in the weights' type).
  *   a: x [s, m] (gather = 1) or a dispatched buffer [rows, m] (gather = 0), dtype;
  *   grad_out [rows, n] dtype (the gradient of moe_expert_gemm's output; rows outside the
- *   segments are not read);  grad_w [e, n, m] float32, overwritten entirely.
- *   dtype bf16 or f16 (MOE_ERR_UNSUPPORTED otherwise); m and n multiples of 8; a,
- *   grad_out and grad_w 16-byte aligned; grad_w may not overlap a or grad_out.
+ *   segments are not read);  grad_w [e, n, m] of grad_w_dtype, overwritten entirely.
+ *   dtype bf16 or f16 (MOE_ERR_UNSUPPORTED otherwise); grad_w_dtype MOE_F32 or dtype
+ *   (MOE_ERR_UNSUPPORTED otherwise); m and n multiples of 8; a, grad_out and grad_w
+ *   16-byte aligned; grad_w may not overlap a or grad_out.
  */
 moe_status_t moe_expert_gemm_wgrad(const moe_layout_t* layout, const void* a, int32_t gather,
                                    const void* grad_out, int32_t m, int32_t n, moe_dtype_t dtype,
-                                   float* grad_w, void* stream);
+                                   moe_dtype_t grad_w_dtype, void* grad_w, void* stream);
 
 /*
  * Read the layout's flags word and routing checksum into HOST memory. Synchronises

@@ -529,7 +529,7 @@ def expert_gemm_dgrad(layout: Layout, grad_out: np.ndarray, weights: np.ndarray,
     return out, exact
 
 def expert_gemm_wgrad(layout: Layout, a: np.ndarray, grad_out: np.ndarray, dtype: str,
-                      gather: bool) -> tuple[np.ndarray, np.ndarray]:
+                      gather: bool, out_dtype: str = "f32") -> tuple[np.ndarray, np.ndarray]:
     """Gradient of the grouped expert GEMM with respect to its weights.
 
     With out[r] = A(r) @ weights[x]^T for the placed rows r of expert x (expert_gemm),
@@ -537,11 +537,15 @@ def expert_gemm_wgrad(layout: Layout, a: np.ndarray, grad_out: np.ndarray, dtype
     an [n, m] matrix per expert; A(r) = a[src[r]] if gather else a[r], so the rows are
     gathered straight from the token rows here too. Experts with no placed row get zeros.
     The sums are exact (float64 of float32-widened operands, one matmul per expert) and
-    rounded once to float32 (weight gradients are kept in float32).
+    rounded once to float32 (weight gradients are usually kept in float32); with
+    out_dtype equal to dtype that float32 value is then rounded to nearest even in the
+    element type, for gradients kept in the weights' own type.
     [DS-8213] review-fix commit: the groups are the offsets' segments; rows past them are
     in no group. First commit: the backward of the expert step replays the same grouping.
-    Returns (grad_weights float32 [e, n, m], exact float64 [e, n, m]).
+    Returns (grad_weights [e, n, m] of out_dtype, exact float64 [e, n, m]).
     """
+    if out_dtype not in ("f32", dtype):
+        raise ValueError(f"out_dtype must be f32 or {dtype}")
     n = grad_out.shape[1]
     m = a.shape[1]
     a32 = to_f32(a, dtype).astype(np.float64)
@@ -555,4 +559,4 @@ def expert_gemm_wgrad(layout: Layout, a: np.ndarray, grad_out: np.ndarray, dtype
         rows = np.arange(r0, r1)
         lhs = a32[layout.src[rows]] if gather else a32[rows]
         exact[x] = g64[rows].T @ lhs
-    return exact.astype(np.float32), exact
+    return from_f32(exact.astype(np.float32), out_dtype), exact

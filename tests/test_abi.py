@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_names(lib):
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
     for code, name in M.STATUS_NAMES.items():
         assert lib.moe_status_string(code).decode() == name
     assert lib.moe_status_string(99).decode() == "MOE_STATUS_UNKNOWN"
@@ -173,13 +173,14 @@ def test_expert_gemm_gradient_argument_checks(lib):
     h = ctypes.byref(st)
     a, g, w, out = FAKE, ctypes.c_void_p(1 << 26), ctypes.c_void_p(1 << 27), ctypes.c_void_p(1 << 28)
     # weight gradient
-    assert lib.moe_expert_gemm_wgrad(h, a, 1, g, 64, 64, 0, out, None) == 2  # float32 operands
-    assert lib.moe_expert_gemm_wgrad(h, a, 3, g, 64, 64, 1, out, None) == 1  # gather flag
-    assert lib.moe_expert_gemm_wgrad(h, a, 1, g, 12, 64, 1, out, None) == 5  # 24-byte rows
-    assert lib.moe_expert_gemm_wgrad(h, a, 1, None, 64, 64, 1, out, None) == 1  # NULL grad_out
-    assert lib.moe_expert_gemm_wgrad(h, a, 1, g, 64, 64, 1, None, None) == 1  # NULL grad_w
-    assert lib.moe_expert_gemm_wgrad(h, a, 1, g, 64, 64, 1, ctypes.c_void_p((1 << 28) + 4), None) == 5
-    assert lib.moe_expert_gemm_wgrad(h, a, 1, g, 64, 64, 1, ctypes.c_void_p((1 << 26) + 256), None) == 1
+    assert lib.moe_expert_gemm_wgrad(h, a, 1, g, 64, 64, 0, 0, out, None) == 2  # float32 operands
+    assert lib.moe_expert_gemm_wgrad(h, a, 1, g, 64, 64, 1, 2, out, None) == 2  # f16 grad_w of bf16
+    assert lib.moe_expert_gemm_wgrad(h, a, 3, g, 64, 64, 1, 0, out, None) == 1  # gather flag
+    assert lib.moe_expert_gemm_wgrad(h, a, 1, g, 12, 64, 1, 0, out, None) == 5  # 24-byte rows
+    assert lib.moe_expert_gemm_wgrad(h, a, 1, None, 64, 64, 1, 0, out, None) == 1  # NULL grad_out
+    assert lib.moe_expert_gemm_wgrad(h, a, 1, g, 64, 64, 1, 0, None, None) == 1  # NULL grad_w
+    assert lib.moe_expert_gemm_wgrad(h, a, 1, g, 64, 64, 1, 0, ctypes.c_void_p((1 << 28) + 4), None) == 5
+    assert lib.moe_expert_gemm_wgrad(h, a, 1, g, 64, 64, 1, 0, ctypes.c_void_p((1 << 26) + 256), None) == 1
     assert "overlap" in lib.moe_last_error().decode()
     # input-row gradient
     assert lib.moe_expert_gemm_dgrad(h, g, w, 64, 64, 0, out, None) == 2
@@ -189,7 +190,7 @@ def test_expert_gemm_gradient_argument_checks(lib):
     assert "overlap" in lib.moe_last_error().decode()
     st2 = M.LayoutStruct()
     assert lib.moe_expert_gemm_dgrad(ctypes.byref(st2), g, w, 64, 64, 1, out, None) == 4
-    assert lib.moe_expert_gemm_wgrad(ctypes.byref(st2), a, 1, g, 64, 64, 1, out, None) == 4
+    assert lib.moe_expert_gemm_wgrad(ctypes.byref(st2), a, 1, g, 64, 64, 1, 0, out, None) == 4
 
 
 def _fake_handle(s, e, k, capacity, ws, need):

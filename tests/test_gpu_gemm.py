@@ -275,6 +275,24 @@ def check_wgrad(got: np.ndarray, Lo: oracle.Layout, a: np.ndarray, g: np.ndarray
     assert not np.any(got[idle].view(np.uint32)), f"{what}: idle experts not +0.0"
 
 
+def check_wgrad_narrowed(got: np.ndarray, Lo: oracle.Layout, a: np.ndarray, g: np.ndarray, dtype: str,
+                         what: str):
+    """Gradients rounded to the element type: the float32 bound above plus one rounding,
+    |got - exact| <= 2^-23 |exact| + (K_x + 2) 2^-23 sum_r |g a| + ulp_dtype(max(|got|, |exact|))."""
+    _, exact = oracle.expert_gemm_wgrad(Lo, a, g, dtype, True)
+    _, absb = oracle.expert_gemm_wgrad(Lo, abs_bits(a, dtype), abs_bits(g, dtype), dtype, True)
+    kx = Lo.kept.astype(np.float64)[:, None, None]
+    g64 = oracle.to_f32(got, dtype).astype(np.float64)
+    big = np.maximum(np.abs(g64), np.abs(exact))
+    tol = 2.0 ** -23 * np.abs(exact) + (kx + 2) * 2.0 ** -23 * absb + dtype_ulp(big, dtype)
+    err = np.abs(g64 - exact)
+    bad = np.argwhere(~(err <= tol))
+    assert len(bad) == 0, (f"{what}: {len(bad)} outside the bound, first {tuple(bad[0])}: got "
+                           f"{g64[tuple(bad[0])]!r} exact {exact[tuple(bad[0])]!r} tol {tol[tuple(bad[0])]!r}")
+    idle = Lo.kept == 0
+    assert not np.any(oracle.to_f32(got[idle], dtype).view(np.uint32)), f"{what}: idle experts not +0.0"
+
+
 WGRAD_CASES = [
     # s, m, n, e, k, capacity, pad, route_major, dtype
     (300, 64, 64, 4, 2, 0, 1, False, "bf16"),
@@ -302,6 +320,13 @@ def test_expert_gemm_wgrad_matches_oracle(s, m, n, e, k, cap, pad, rm, dtype):
     check_wgrad(to_host(fused), Lo, x, g, dtype, True, "fused")
     unfused = M.moe_expert_gemm_wgrad(Lg, M.moe_dispatch(Lg, xd), gd, gather=False)
     assert_bits_equal(to_host(unfused), to_host(fused), "unfused vs fused")
+    # kept in the element type: the same float32 sums, each rounded once to nearest even
+    stale_n = torch.full((e, n, m), 7.0, dtype=TORCH_DTYPE[dtype], device="cuda")
+    narrowed = M.moe_expert_gemm_wgrad(Lg, xd, gd, gather=True, out=stale_n)
+    assert narrowed.dtype == TORCH_DTYPE[dtype]
+    assert torch.equal(narrowed.view(torch.int16), fused.to(TORCH_DTYPE[dtype]).view(torch.int16)), \
+        "narrowed output is not the rounding of the float32 output"
+    check_wgrad_narrowed(to_host(narrowed), Lo, x, g, dtype, "narrowed")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
@@ -318,6 +343,12 @@ def test_expert_gemm_wgrad_integer_operands_bit_exact(dtype):
     got = M.moe_expert_gemm_wgrad(Lg, to_dev(x, dtype), to_dev(g, dtype), gather=True)
     want, _ = oracle.expert_gemm_wgrad(Lo, x, g, dtype, True)
     assert_bits_equal(to_host(got), want, "integer operands")
+    if dtype == "bf16":
+        assert np.abs(want).max() > 256  # sums that bf16 has to round
+    got_n = M.moe_expert_gemm_wgrad(Lg, to_dev(x, dtype), to_dev(g, dtype), gather=True,
+                                    out_dtype=TORCH_DTYPE[dtype])
+    want_n, _ = oracle.expert_gemm_wgrad(Lo, x, g, dtype, True, out_dtype=dtype)
+    assert_bits_equal(to_host(got_n), want_n, "integer operands, narrowed output")
 
 
 def test_expert_gemm_wgrad_empty_layout_zeroes_everything():
@@ -351,6 +382,10 @@ def test_expert_gemm_wgrad_full_workload_sampled():
     unfused = M.moe_expert_gemm_wgrad(Lg, M.moe_dispatch(Lg, xd), gd, gather=False)
     assert torch.equal(got.view(torch.int32), unfused.view(torch.int32)), "unfused vs fused"
     del unfused
+    narrowed = M.moe_expert_gemm_wgrad(Lg, xd, gd, gather=True, out_dtype=TORCH_DTYPE[w.dtype])
+    assert torch.equal(narrowed.view(torch.int16), got.to(TORCH_DTYPE[w.dtype]).view(torch.int16)), \
+        "narrowed output is not the rounding of the float32 output"
+    del narrowed
     J = np.unique(np.concatenate([[0, 255, 256, n - 1], rng.choice(n, 12, replace=False)]))
     C = np.unique(np.concatenate([[0, 255, 256, w.m - 1], rng.choice(w.m, 12, replace=False)]))
     sub = got.index_select(1, torch.from_numpy(J).cuda()).index_select(2, torch.from_numpy(C).cuda())

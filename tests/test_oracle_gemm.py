@@ -167,6 +167,35 @@ def test_expert_gemm_wgrad_fused_equals_unfused_and_idle_experts_are_zero(dtype)
     assert L.kept[e - 1] == 0 and not np.any(fused[e - 1])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_expert_gemm_wgrad_narrowed_output_rounds_to_nearest_even(dtype):
+    """Gradients kept in the element type: column sums of ones that land between two
+    representable values. bf16 holds 8 significant bits, so 257 (a tie) goes to the even
+    256, 259 (a tie) to 260, 258 stays; f16 holds 11 bits, the same at 2049 / 2050 / 2051.
+    Sums below 2^24 are exact in float32, so the element-type rounding is the only one."""
+    base = 256 if dtype == "bf16" else 2048
+    counts = [base + 1, base + 2, base + 3, 1, 0, base - 1, 7, base]
+    want = [base, base + 2, base + 4, 1, 0, base - 1, 7, base]
+    s, m, n = counts[0] + 2, 8, len(counts)
+    idx = np.zeros((s, 1), np.int32)  # every token to the one expert
+    L = oracle.dispatch_layout(idx, 1, 0)
+    ones = 1.0 if dtype == "f16" else 0x3F80  # 1.0 in the element type
+    x = np.full((s, m), ones, np.float16 if dtype == "f16" else np.uint16)
+    g32 = np.zeros((L.rows, n), np.float32)
+    for j, c in enumerate(counts):
+        g32[:c, j] = 1.0
+    g = g32.astype(np.float16) if dtype == "f16" else (g32.view(np.uint32) >> 16).astype(np.uint16)
+    got, exact = oracle.expert_gemm_wgrad(L, x, g, dtype, True, out_dtype=dtype)
+    assert np.array_equal(exact[0, :, 0], counts)
+    got32 = oracle.to_f32(got, dtype)
+    assert got.dtype == (np.float16 if dtype == "f16" else np.uint16)
+    assert np.array_equal(got32[0], np.repeat(np.array(want, np.float32)[:, None], m, axis=1))
+    f32, _ = oracle.expert_gemm_wgrad(L, x, g, dtype, True)
+    assert f32.dtype == np.float32 and np.array_equal(f32[0, :, 0], counts)
+    with pytest.raises(ValueError):
+        oracle.expert_gemm_wgrad(L, x, g, dtype, True, out_dtype="f16" if dtype == "bf16" else "bf16")
+
+
 # ----------------------------------------------------------------------------
 # the input-row gradient of the grouped GEMM
 

@@ -147,21 +147,34 @@ def _gemm_ignores_route_weights(layout, a, weights, dtype, gather, route_w=None)
     return moe.expert_gemm(layout, a, weights, dtype, gather, None)
 
 
-def _wgrad_ignores_gather(layout, a, grad_out, dtype, gather):
+def _wgrad_ignores_gather(layout, a, grad_out, dtype, gather, out_dtype="f32"):
     if gather:  # reads the token rows as if they were already dispatched
         pad = np.zeros((max(layout.rows - a.shape[0], 0),) + a.shape[1:], a.dtype)
-        return moe.expert_gemm_wgrad(layout, np.concatenate([a, pad])[:layout.rows], grad_out, dtype, False)
-    return moe.expert_gemm_wgrad(layout, a, grad_out, dtype, gather)
+        return moe.expert_gemm_wgrad(layout, np.concatenate([a, pad])[:layout.rows], grad_out, dtype, False,
+                                     out_dtype)
+    return moe.expert_gemm_wgrad(layout, a, grad_out, dtype, gather, out_dtype)
 
 
-def _wgrad_wrong_expert(layout, a, grad_out, dtype, gather):
-    out, exact = moe.expert_gemm_wgrad(layout, a, grad_out, dtype, gather)
+def _wgrad_wrong_expert(layout, a, grad_out, dtype, gather, out_dtype="f32"):
+    out, exact = moe.expert_gemm_wgrad(layout, a, grad_out, dtype, gather, out_dtype)
     return np.roll(out, 1, axis=0), np.roll(exact, 1, axis=0)
 
 
-def _wgrad_transposed(layout, a, grad_out, dtype, gather):
-    out, exact = moe.expert_gemm_wgrad(layout, a, grad_out, dtype, gather)
+def _wgrad_transposed(layout, a, grad_out, dtype, gather, out_dtype="f32"):
+    out, exact = moe.expert_gemm_wgrad(layout, a, grad_out, dtype, gather, out_dtype)
     return np.swapaxes(out, 1, 2).copy(), np.swapaxes(exact, 1, 2).copy()
+
+
+def _wgrad_narrows_by_truncation(layout, a, grad_out, dtype, gather, out_dtype="f32"):
+    out, exact = moe.expert_gemm_wgrad(layout, a, grad_out, dtype, gather, "f32")
+    if out_dtype == "bf16":
+        return (out.view(np.uint32) >> np.uint32(16)).astype(np.uint16), exact
+    if out_dtype == "f16":  # round toward zero: step down where nearest rounded away
+        h = out.astype(np.float16)
+        away = np.abs(h.astype(np.float32)) > np.abs(out)
+        h[away] = np.nextafter(h[away], np.float16(0))
+        return h, exact
+    return out, exact
 
 
 def _dgrad_untransposed(layout, grad_out, weights, dtype):
@@ -182,6 +195,7 @@ MUTATIONS = {
     "wgrad_ignores_gather": ("expert_gemm_wgrad", _wgrad_ignores_gather),
     "wgrad_wrong_expert": ("expert_gemm_wgrad", _wgrad_wrong_expert),
     "wgrad_transposed": ("expert_gemm_wgrad", _wgrad_transposed),
+    "wgrad_narrows_by_truncation": ("expert_gemm_wgrad", _wgrad_narrows_by_truncation),
     "gemm_wrong_expert": ("expert_gemm", _gemm_wrong_expert),
     "gemm_untransposed": ("expert_gemm", _gemm_untransposed),
     "gemm_ignores_route_weights": ("expert_gemm", _gemm_ignores_route_weights),
@@ -227,6 +241,8 @@ PINS = [
     lambda: gpins.test_expert_gemm_wgrad_matches_brute_force(0, True),
     gpins.test_expert_gemm_wgrad_is_the_adjoint_of_the_forward,
     gpins.test_expert_gemm_wgrad_is_the_exact_derivative_on_integers,
+    lambda: gpins.test_expert_gemm_wgrad_narrowed_output_rounds_to_nearest_even("bf16"),
+    lambda: gpins.test_expert_gemm_wgrad_narrowed_output_rounds_to_nearest_even("f16"),
     lambda: gpins.test_expert_gemm_dgrad_matches_brute_force(4),
     gpins.test_expert_gemm_dgrad_is_the_adjoint_of_the_forward,
     gpins.test_expert_gemm_input_gradient_is_the_exact_derivative_on_integers,

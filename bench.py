@@ -205,6 +205,23 @@ def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None):
             ("expert_gemm_wgrad_narrow", lambda: M.moe_expert_gemm_wgrad(st["L"], x, H, gather=True, out=gWn)),
             ("expert_gemm_dgrad", lambda: M.moe_expert_gemm_dgrad(st["L"], H, wts, out=buf)),
         ]
+        # the whole layer as a training step through the autograd wrappers: gate, layout,
+        # the fused projection and the weighted combine forward; then the gradients of
+        # the tokens, the expert weights (kept in their type) and the router logits
+        from combine_moe_gate_amd import autograd as A
+        wts.requires_grad_(True)
+        gyn = torch.randn((s, n), generator=torch.Generator(device=dev).manual_seed(7), device=dev,
+                          dtype=torch.float32).to(tdt)
+
+        def layer_step():
+            xl = x.detach().requires_grad_(True)
+            ll = logits.detach().requires_grad_(True)
+            idx_l, w_l = A.route(ll, k)
+            L_l, _ = A.layout(idx_l, e, cap)
+            y_l = A.combine(A.expert_linear(xl, wts, L_l), w_l, L_l)
+            torch.autograd.grad(y_l, (xl, wts, ll), gyn)
+
+        extra["layer"] = [("layer_train_step", layer_step)]
     elif variant == "weights_before":
         ops = [
             ("gate", gate), ("layout", layout),
@@ -267,8 +284,9 @@ def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None):
     for ev in events:
         for j, op in enumerate(names):
             per_op[op].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)  # microseconds
-    for op, fn in extra.get("unfused", []):  # outside the timed step
+    for op, fn in extra.get("unfused", []) + extra.get("layer", []):  # outside the timed step
         per_op[op] = []
+        fn()  # the first call sets up the autograd graph and allocator
         for _ in range(min(steps, 10)):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
@@ -404,6 +422,7 @@ def main():
     ms_per_step = elapsed / args.steps * 1e3
     abytes = algorithmic_bytes(w, kept, rows, args.variant)
     copy_us = per_op.pop("_copy_reference")
+    layer_us = per_op.pop("layer_train_step", None)
     ops = list(per_op)
     kernels = {}
     for op in ops:
@@ -473,6 +492,12 @@ def main():
                            "bytes": copy_moved, "us": round(float(np.mean(copy_us)), 2),
                            "GBps": round(copy_gbps, 1), "frac_of_hbm_peak": round(copy_gbps / HBM_PEAK_GBPS, 4)},
         "roofline": roofline,
+        "layer_train_step": None if layer_us is None else {
+            "what": "autograd forward + backward of the layer: gate, layout, fused expert GEMM, weighted "
+                    "combine; gradients of tokens, expert weights (element type) and router logits",
+            "us": round(float(np.mean(layer_us)), 2), "us_median": round(float(np.median(layer_us)), 2),
+            "tokens_per_s": round(w.s / (float(np.mean(layer_us)) / 1e6), 1),
+            "gemm_TFLOPs": round(3 * 2 * kept * W.EXPERT_WIDTH * w.m / float(np.mean(layer_us)) / 1e6, 1)},
         "kernels": kernels,
         "kept_routes": kept,
     }

@@ -108,6 +108,9 @@ _SIGNATURES = {
 EXPORTS = tuple(_SIGNATURES)
 
 
+ABI_VERSION = 5  # MOE_ABI_VERSION of include/moe_gate.h that _SIGNATURES follows
+
+
 def lib() -> ctypes.CDLL:
     """Load libmoe_gate.so (built in-tree); raise if it is missing."""
     global _lib
@@ -116,6 +119,12 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(
                 f"{LIB_PATH} is missing: build it first (python -m combine_moe_gate_amd._build)")
         handle = ctypes.CDLL(LIB_PATH)
+        handle.moe_abi_version.restype = ctypes.c_int
+        handle.moe_abi_version.argtypes = []
+        built = handle.moe_abi_version()
+        if built != ABI_VERSION:  # the signatures below would not match the library's
+            raise RuntimeError(f"{LIB_PATH} implements ABI version {built}, this binding expects "
+                               f"{ABI_VERSION}: rebuild it (python -m combine_moe_gate_amd._build)")
         for name, (res, args) in _SIGNATURES.items():
             fn = getattr(handle, name)
             fn.restype = res

@@ -36,7 +36,9 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_names(lib):
-    assert lib.moe_abi_version() == 5
+    header = open(os.path.join(os.path.dirname(__file__), "..", "include", "moe_gate.h")).read()
+    declared = int(re.search(r"#define MOE_ABI_VERSION (\d+)", header).group(1))
+    assert lib.moe_abi_version() == declared == M.ABI_VERSION == 5
     for code, name in M.STATUS_NAMES.items():
         assert lib.moe_status_string(code).decode() == name
     assert lib.moe_status_string(99).decode() == "MOE_STATUS_UNKNOWN"
@@ -163,6 +165,15 @@ def test_expert_gemm_argument_checks(lib):
     assert "overlap" in lib.moe_last_error().decode()
     st2 = M.LayoutStruct()  # never filled by moe_dispatch_layout
     assert lib.moe_expert_gemm(ctypes.byref(st2), a, 1, w, 64, 64, 1, None, out, None) == 4
+
+
+@no_gpu_only
+def test_binding_refuses_a_library_of_another_abi_version(monkeypatch):
+    """A library built for other signatures is refused at load, before any call."""
+    monkeypatch.setattr(M, "_lib", None)
+    monkeypatch.setattr(M, "ABI_VERSION", M.ABI_VERSION + 1)
+    with pytest.raises(RuntimeError, match="ABI version"):
+        M.lib()
 
 
 @no_gpu_only

@@ -137,7 +137,7 @@ def to_dev(a, dtype, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None):
+def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None, flush_mib: int = 0):
     import torch
 
     import combine_moe_gate_amd as M
@@ -269,6 +269,10 @@ def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None):
         if ev is not None:
             ev[len(ops)].record()
 
+    # cold-cache mode: before each step, outside its events, read flush_mib MiB of scratch
+    # so that neither L2 nor the Infinity Cache holds the step's data (a read leaves clean
+    # lines behind, whose eviction costs the step no write-back)
+    scratch = torch.zeros((flush_mib << 20) // 4, dtype=torch.float32, device=dev) if flush_mib > 0 else None
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -276,9 +280,14 @@ def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
+        if scratch is not None:
+            scratch.sum()
         step(events[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    if scratch is not None:  # the steps alone, from their events: the flushes are not counted
+        elapsed = sum(ev[0].elapsed_time(ev[len(ops)]) for ev in events) / 1e3
+        del scratch
 
     per_op = {op: [] for op in names}
     for ev in events:
@@ -400,6 +409,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--variant", choices=VARIANTS, default=None,
                     help="time the step with one of the variants instead of the default path")
+    ap.add_argument("--flush-mib", type=int, default=0, metavar="MIB",
+                    help="cold caches: read MIB MiB of scratch before each timed step, outside its "
+                         "events (the step time is then summed from the events, without the flushes)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run one plain device-to-device copy of MIB MiB "
                          "(a known-size reference for hardware memory counters)")
@@ -410,7 +422,7 @@ def main():
         sys.exit(2)
 
     w = W.WORKLOADS[args.workload]
-    elapsed, per_op, kept, rows = run_gpu(w, args.steps, args.warmup, args.variant)
+    elapsed, per_op, kept, rows = run_gpu(w, args.steps, args.warmup, args.variant, args.flush_mib)
     if args.calibrate_copy > 0:
         import torch
         src = torch.ones(args.calibrate_copy << 20, dtype=torch.uint8, device="cuda:0")
@@ -480,6 +492,7 @@ def main():
                                "hotspot": "N(0,1), +3 on expert 0 for 10% of tokens"}[w.routing],
                    "step": "+".join(step_ops), "variant": args.variant or "default",
                    "parallelism": "single GPU",
+                   **({"flush_mib_before_each_step": args.flush_mib} if args.flush_mib > 0 else {}),
                    **({"expert_width": W.EXPERT_WIDTH} if args.variant == "expert_gemm" else {})},
         "dispatch_combine": None if args.variant == "expert_gemm" else {
             "tokens_per_s": round(w.s / (dc_us / 1e6), 1), "GBps": round(dc_gbps, 1),

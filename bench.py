@@ -442,6 +442,7 @@ def main():
         kernels[op] = {"us": round(us, 2), "us_median": round(float(np.median(per_op[op])), 2),
                        "us_p10": round(float(np.percentile(per_op[op], 10)), 2),
                        "us_p90": round(float(np.percentile(per_op[op], 90)), 2),
+                       "us_min": round(float(np.min(per_op[op])), 2),
                        "bytes": abytes[op], "GBps": round(abytes[op] / us / 1e3, 1)}
     step_ops = [op for op in ops if op not in ("expert_gemm_unfused", "expert_gemm_wgrad", "expert_gemm_wgrad_narrow",
                                                "expert_gemm_dgrad") and
@@ -500,6 +501,7 @@ def main():
             "us_median": round(float(np.median(dc_steps)), 2),
             "us_p10": round(float(np.percentile(dc_steps, 10)), 2),
             "us_p90": round(float(np.percentile(dc_steps, 90)), 2),
+            "us_min": round(float(np.min(dc_steps)), 2),
             "bytes": dc_bytes, "frac_of_copy": round(dc_gbps / copy_gbps, 4)},
         "copy_reference": {"what": "device-to-device copy of the dispatch+combine byte count (read + write)",
                            "bytes": copy_moved, "us": round(float(np.mean(copy_us)), 2),

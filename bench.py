@@ -349,9 +349,14 @@ def run_cpu_baseline(w: W.Workload, target_s: float = 12.0, sample_tokens: int =
     t0 = time.perf_counter()
     opts = dict(route_major=variant == "route_major", pad_multiple=128 if variant == "pad128" else 1)
     limit = threadpool_limits(limits=1)  # the BLAS behind numpy's matmul on one core
+    part_s = {"gate": 0.0, "layout": 0.0, "dispatch_combine": 0.0}  # default path only
     while True:
+        ta = time.perf_counter()
         idx, wt = oracle.gate_topk(logits, w.k)
+        tb = time.perf_counter()
         L = oracle.dispatch_layout(idx, w.e, cap, **opts)
+        part_s["gate"] += tb - ta
+        part_s["layout"] += time.perf_counter() - tb
         if variant == "expert_gemm":
             H, _ = oracle.expert_gemm(L, x, wts, w.dtype, gather=True)
             oracle.combine(L, H, wt, w.dtype)
@@ -364,8 +369,10 @@ def run_cpu_baseline(w: W.Workload, target_s: float = 12.0, sample_tokens: int =
             _, gw = oracle.dispatch_weighted_backward(L, gE, x, wt, w.dtype)
         else:
             wc = oracle.renormalize_kept(L, wt) if variant == "renorm_kept" else wt
+            ta = time.perf_counter()
             E = oracle.dispatch(L, x)
             oracle.combine(L, E, wc, w.dtype)
+            part_s["dispatch_combine"] += time.perf_counter() - ta
             E2, _ = oracle.dispatch_replay(L, x, idx)
             gE, gw = oracle.combine_backward(L, gy, E2, wc, w.dtype)
             if variant == "renorm_kept":
@@ -393,6 +400,7 @@ def run_cpu_baseline(w: W.Workload, target_s: float = 12.0, sample_tokens: int =
         "cores": 1,
         "kind": "oracle",
         "host": f"{cpu_model}, {os.cpu_count()} logical CPUs (one used)",
+        "parts_tokens_per_s": {p: round(n * reps / t, 1) for p, t in part_s.items() if t > 0},
         "sample": (f"first {n} of {w.s} tokens of {w.name} (same m, e, k, dtype"
                    f"{', capacity scaled to ' + str(cap) if w.capacity > 0 else ''}), whole step, "
                    f"{reps} passes in {el:.1f} s, single-threaded numpy"),

@@ -208,9 +208,10 @@ def test_expert_gemm_full_workload_sampled():
                f"{name} sampled rows")
 
 
-def test_layer_forward_with_gemm_replays_from_a_hip_graph():
+def test_layer_with_gemm_and_its_gradients_replays_from_a_hip_graph():
     """gate -> layout -> fused GEMM with the route weights in its epilogue -> unweighted
-    combine, captured once; every replay (with eager work between) equals the eager run."""
+    combine, then the GEMM's input-row gradient and its weight gradient (float32 and bf16),
+    captured once; every replay (with eager work between) equals the eager run."""
     announce("gemm hip graph")
     s, m, n, e, k = 2048, 96, 136, 8, 4  # 1024 rows per expert on average: 256-row tiles
     rng = np.random.default_rng(21)
@@ -222,14 +223,21 @@ def test_layer_forward_with_gemm_replays_from_a_hip_graph():
     wt = torch.empty((s, k), dtype=torch.float32, device="cuda")
     h = torch.empty((s * k, n), dtype=torch.bfloat16, device="cuda")
     y = torch.empty((s, n), dtype=torch.bfloat16, device="cuda")
+    ga = torch.empty((s * k, m), dtype=torch.bfloat16, device="cuda")
+    gW = torch.empty((e, n, m), dtype=torch.float32, device="cuda")
+    gWn = torch.empty((e, n, m), dtype=torch.bfloat16, device="cuda")
 
     def step():
         M.moe_gate_topk(logits, k, idx_out=idx, w_out=wt)
         L = M.moe_dispatch_layout(idx, e, 0, workspace=ws)
         M.moe_expert_gemm(L, x, wts, gather=True, w=wt, out=h)
         M.moe_combine(L, h, None, out=y)
+        # h stands in for the gradient arriving at the GEMM's output
+        M.moe_expert_gemm_dgrad(L, h, wts, out=ga)
+        M.moe_expert_gemm_wgrad(L, x, h, gather=True, out=gW)
+        M.moe_expert_gemm_wgrad(L, x, h, gather=True, out=gWn)
 
-    outs = (idx, wt, h, y)
+    outs = (idx, wt, h, y, ga, gW, gWn)
     step()
     torch.cuda.synchronize()
     eager = [o.clone() for o in outs]
@@ -242,7 +250,8 @@ def test_layer_forward_with_gemm_replays_from_a_hip_graph():
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         step()
-    bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+    bits = lambda t: (t.view(torch.int16) if t.dtype == torch.bfloat16 else
+                      t.view(torch.int32) if t.dtype == torch.float32 else t)
     for rep in range(3):
         for o in outs:
             o.zero_()

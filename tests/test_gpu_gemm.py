@@ -489,3 +489,44 @@ def test_expert_gemm_dgrad_full_workload_sampled():
     got = to_host(ga.index_select(0, torch.from_numpy(rows).cuda()))
     check_dgrad(got, sub, np.ascontiguousarray(g[rows]), np.ascontiguousarray(wts[experts]), w.dtype,
                 f"{name} sampled rows")
+
+
+# ----------------------------------------------------------------------------
+# seeded random configurations: forward and both gradients
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_gemm_random_configurations(seed):
+    """Sizes, routing mode and dtype drawn from one seeded generator; the forward (with
+    route weights half the time), the input-row gradient and the weight gradient (float32
+    and the element type) each within their bounds of the oracle."""
+    rng = np.random.default_rng(7000 + seed)
+    s = int(rng.integers(1, 1500))
+    e = int(rng.integers(1, 40))
+    k = int(rng.integers(1, min(e, 8) + 1))
+    m = 8 * int(rng.integers(1, 70))
+    n = 8 * int(rng.integers(1, 70))
+    dtype = ["bf16", "f16"][int(rng.integers(0, 2))]
+    cap = 0 if rng.random() < 0.5 else int(rng.integers(1, max(2, 2 * s * k // e)))
+    rm = bool(rng.random() < 0.3) and cap > 0
+    pad = int([1, 1, 16, 128][int(rng.integers(0, 4))]) if cap == 0 else 1
+    announce("gemm random config", seed, s, e, k, m, n, dtype, cap, rm, pad)
+    idx = W.random_idx(rng, s, e, k)
+    x = W.cast_input(rng.standard_normal((s, m)).astype(np.float32), dtype)
+    wts = W.expert_weights(seed, e, n, m, dtype)
+    rw = W.random_weights(rng, s, k) if rng.random() < 0.5 else None
+    Lo = oracle.dispatch_layout(idx, e, cap, route_major=rm, pad_multiple=pad)
+    g = W.cast_input(rng.standard_normal((Lo.rows, n)).astype(np.float32), dtype)
+    Lg = M.moe_dispatch_layout(to_dev(idx), e, cap, route_major=rm, pad_multiple=pad)
+    xd, wd, gd = to_dev(x, dtype), to_dev(wts, dtype), to_dev(g, dtype)
+
+    out = M.moe_expert_gemm(Lg, xd, wd, gather=True, w=None if rw is None else to_dev(rw))
+    check_gemm(to_host(out), Lo, x, wts, dtype, True, rw, "forward")
+    ga = M.moe_expert_gemm_dgrad(Lg, gd, wd)
+    check_dgrad(to_host(ga), Lo, g, wts, dtype, "input-row gradient")
+    gw = M.moe_expert_gemm_wgrad(Lg, xd, gd, gather=True)
+    check_wgrad(to_host(gw), Lo, x, g, dtype, True, "weight gradient")
+    gwn = M.moe_expert_gemm_wgrad(Lg, xd, gd, gather=True, out_dtype=TORCH_DTYPE[dtype])
+    assert torch.equal(gwn.view(torch.int16), gw.to(TORCH_DTYPE[dtype]).view(torch.int16)), \
+        "narrowed weight gradient is not the rounding of the float32 one"
+    check_wgrad_narrowed(to_host(gwn), Lo, x, g, dtype, "weight gradient, element type")

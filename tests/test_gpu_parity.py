@@ -465,3 +465,50 @@ def test_whole_step_replays_correctly_from_a_hip_graph():
         # eager work between replays
         M.moe_gate_topk(logits.flip(0), k)
         torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------------
+# seeded random configurations through the whole row path
+
+
+def random_config(seed: int):
+    """Sizes, routing mode and dtype drawn from one seeded generator (rows of whole 16-byte
+    chunks, k distinct experts per token)."""
+    rng = np.random.default_rng(9000 + seed)
+    s = int(rng.integers(1, 2500))
+    e = int(rng.integers(1, 300))
+    k = int(rng.integers(1, min(e, 16) + 1))
+    dtype = ["f32", "bf16", "f16"][int(rng.integers(0, 3))]
+    m = int(rng.integers(1, 80)) * (4 if dtype == "f32" else 8)
+    cap = 0 if rng.random() < 0.5 else int(rng.integers(1, max(2, 2 * s * k // e)))
+    route_major = bool(rng.random() < 0.3) and cap > 0
+    pad = int([1, 1, 8, 128][int(rng.integers(0, 4))]) if cap == 0 else 1
+    skew = bool(rng.random() < 0.3)
+    return rng, s, e, k, dtype, m, cap, route_major, pad, skew
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_configurations_bit_exact(seed):
+    rng, s, e, k, dtype, m, cap, rm, pad, skew = random_config(seed)
+    announce("random config", seed, s, e, k, dtype, m, cap, rm, pad, skew)
+    idx = W.skewed_idx(rng, s, e, k) if skew else W.random_idx(rng, s, e, k)
+    x = W.cast_input(rng.standard_normal((s, m)).astype(np.float32), dtype)
+    w = W.random_weights(rng, s, k)
+    Lo = oracle.dispatch_layout(idx, e, cap, route_major=rm, pad_multiple=pad)
+    E = W.cast_input(rng.standard_normal((Lo.rows, m)).astype(np.float32), dtype)
+    gy = W.cast_input(rng.standard_normal((s, m)).astype(np.float32), dtype)
+
+    Lg = M.moe_dispatch_layout(to_dev(idx), e, cap, route_major=rm, pad_multiple=pad)
+    check_layout(Lg, Lo, f"seed {seed}")
+    buf = M.moe_dispatch(Lg, to_dev(x, dtype))
+    assert_bits_equal(to_host(buf), oracle.dispatch(Lo, x), "dispatch")
+    y = M.moe_combine(Lg, to_dev(E, dtype), to_dev(w))
+    assert_bits_equal(to_host(y), oracle.combine(Lo, E, w, dtype), "combine")
+    gE, gw = M.moe_combine_backward(Lg, to_dev(gy, dtype), to_dev(E, dtype), to_dev(w))
+    gE_o, gw_o = oracle.combine_backward(Lo, gy, E, w, dtype)
+    assert_bits_equal(to_host(gE), gE_o, "grad_E")
+    bound = weight_grad_bound(oracle.to_f32(gy, dtype), oracle.to_f32(E, dtype), Lo.dst)
+    err = np.abs(to_host(gw).astype(np.float64) - gw_o)
+    assert np.all(err <= 1e-6 * bound), f"grad_w err {err.max()}"
+    gx = M.moe_dispatch_backward(Lg, gE)
+    assert_bits_equal(to_host(gx), oracle.dispatch_backward(Lo, gE_o, dtype), "dispatch backward")

@@ -43,7 +43,9 @@
  *   - Activation rows of m elements must start on 16-byte boundaries and be a multiple
  *     of 16 bytes long (m * element size % 16 == 0); otherwise MOE_ERR_MISALIGNED.
  *   - Element types: MOE_F32, MOE_BF16 (bfloat16), MOE_F16 (IEEE half). Narrowing to
- *     bf16/f16 rounds to nearest even. Weights, weight gradients and logits are float32.
+ *     bf16/f16 rounds to nearest even. Route weights, their gradients and logits are
+ *     float32; expert projection weights are of the element type and their gradient
+ *     float32 or the element type (moe_expert_gemm_wgrad).
  *   - Results are deterministic: no floating-point atomics; integer atomics only where
  *     the result does not depend on their order.
  */

@@ -469,7 +469,7 @@ moe_status_t moe_expert_gemm_dgrad(const moe_layout_t* layout, const void* grad_
   int64_t rc_in = 0, rc_out = 0;
   MOE_TRY(check_rows(m, dtype, &rc_in));
   MOE_TRY(check_rows(n, dtype, &rc_out));
-  if (v.s > 0 && moe::expert_gemm_dgrad_grid(v, m) > INT32_MAX)
+  if (v.s > 0 && moe::expert_gemm_kn_grid(v, m) > INT32_MAX)
     return fail(MOE_ERR_UNSUPPORTED, "rows x m too large for one input-gradient launch");
   MOE_TRY(check_array(grad_out, v.s > 0 ? v.rows : 0, "grad_out", true));
   MOE_TRY(check_array(weights, v.s > 0 ? v.e : 0, "weights", true));
@@ -481,9 +481,9 @@ moe_status_t moe_expert_gemm_dgrad(const moe_layout_t* layout, const void* grad_
     if (ob < gb + v.rows * n * eb && gb < ob + v.rows * m * eb)
       return fail(MOE_ERR_INVALID_ARG, "grad_out and grad_a may not overlap");
   }
-  return hip_status(moe::launch_expert_gemm_dgrad(v, grad_out, weights, m, n,
-                                                  static_cast<int>(dtype), grad_a,
-                                                  static_cast<hipStream_t>(stream)),
+  // grad_a = grad_out @ W[x]: the grouped GEMM with K = n, N = m, the weights read [K][N]
+  return hip_status(moe::launch_expert_gemm_kn(v, grad_out, weights, n, m, static_cast<int>(dtype), grad_a,
+                                               static_cast<hipStream_t>(stream)),
                     "moe_expert_gemm_dgrad");
 }
 

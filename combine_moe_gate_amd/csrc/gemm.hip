@@ -21,6 +21,17 @@
 // l%32, K elements 8*(l/32)..+7 of each operand (one ds_read_b128) and holds output rows
 // 8*(v/4) + 4*(l/32) + v%4, column l%32 for v = 0..15.
 //
+// The input-row gradient, grad_A[r] = grad_out[r] @ W[x], is the same product with K = n
+// and N = m and the weights read as [K][N] (BKN): that operand is staged K row by K row,
+// each row's 256-column segment (512 bytes) filling half of a direct-to-LDS load, with
+// 16-byte chunk positions XOR-swizzled by 4 (row % 4), and its MFMA fragments are read with
+// gfx950's transposing LDS read ds_read_b64_tr_b16 (two per fragment, four K rows each).
+// Within each 16-lane group that read hands lane i column i % 4 of the 4-element pieces
+// the lanes i / 4 + 4 t (t = 0..3) point at; with lane j pointing at K row k0 + j / 4,
+// columns c0 + 4 (j % 4) .. + 3, lane i receives K rows k0 .. k0 + 3 of column c0 + i. The
+// 32 lanes served together touch 4 K rows x 4 chunks, which the swizzle spreads over 16
+// distinct chunk positions of the 256-byte bank row.
+//
 // Schedule: the expert weights dominate the traffic (e * n * m elements, far above the
 // L2), so tiles are ordered to read each weight tile few times. The tiles of all experts
 // are numbered expert by expert; inside an expert, in bands of kBandRows row-blocks,
@@ -79,6 +90,31 @@ __device__ __forceinline__ void stage_rows(const chunk_t* const (&row)[LOADS], c
   }
 }
 
+// Stage one K step of an operand stored [K][N] (each K row contiguous along N) with
+// direct-to-LDS loads: instruction q of wave w fills the two staged K rows
+// (w * LOADS + q) * 2 + {0, 1}, 512 bytes each; lane l writes row l / 32, slot l % 32, and
+// so loads chunk (l % 32) ^ (4 (row % 4)) of that row's N segment (colp[q]). K rows past
+// the end repeat the last one: the matching chunks of the other operand are cleared.
+template <int LOADS>
+__device__ __forceinline__ void stage_rows_kn(const chunk_t* const (&colp)[LOADS], const int (&krow)[LOADS],
+                                              int kt, int K, int n_chunks, char* lds_rows) {
+#pragma unroll
+  for (int q = 0; q < LOADS; ++q) {
+    const int kk = kt * 64 + krow[q];
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(colp[q] + static_cast<size_t>(kk < K ? kk : K - 1) * n_chunks),
+                                     (lds_void_t*)(lds_rows + q * 64 * 16), 16, 0, 0);
+  }
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// gfx950's transposing LDS read: within each 16-lane group, lane i receives column i % 4 of
+// the 4-element pieces at the addresses of lanes i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12.
+__device__ __forceinline__ uint2 read_tr16(const char* p) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
 template <int LOADS, int CH>
 __device__ __forceinline__ void clear_slots(const int (&c)[LOADS], int kt, int kchunks,
                                             char* lds_rows, int lane) {
@@ -91,7 +127,7 @@ __device__ __forceinline__ void clear_slots(const int (&c)[LOADS], int kt, int k
 
 // One workgroup per CU (its LDS stages take most of the CU's 160 KiB), NW / 2 waves per
 // SIMD: the register file is these waves', so the schedule may keep two fragment sets live.
-template <int DT, bool GATHER, bool SCALE, int WM, int WN, int NW, int BK, int STAGES>
+template <int DT, bool GATHER, bool SCALE, bool BKN, int WM, int WN, int NW, int BK, int STAGES>
 __global__ __launch_bounds__(2 * NW * kWave)
 __attribute__((amdgpu_waves_per_eu(NW / 2, NW / 2))) void expert_gemm_kernel(
     const chunk_t* __restrict__ a, const chunk_t* __restrict__ wts,
@@ -100,6 +136,8 @@ __attribute__((amdgpu_waves_per_eu(NW / 2, NW / 2))) void expert_gemm_kernel(
     const int32_t* __restrict__ offsets, int e, int k, int m, int n, int col_blocks,
     int band_rows, uint16_t* __restrict__ out) {
   using S = GemmShape<WM, WN, NW, BK, STAGES>;
+  static_assert(!BKN || (S::BN == 256 && BK == 64 && S::B_LOADS * 2 * S::WAVES == BK),
+                "a [K][N] operand stages 64 K rows of 512 bytes, two per load instruction");
   extern __shared__ __attribute__((aligned(1024))) char lds[];  // [STAGES][BM + BN rows][ROW_BYTES]
   __shared__ int32_t row_src[S::BM];
   __shared__ float row_scale[S::BM];
@@ -159,10 +197,20 @@ __attribute__((amdgpu_waves_per_eu(NW / 2, NW / 2))) void expert_gemm_kernel(
   }
 #pragma unroll
   for (int q = 0; q < S::B_LOADS; ++q) {
-    const int r = (wv * S::B_LOADS + q) * S::ROWS_PER_LOAD + lane / S::CH;
-    const int j = col0 + r;
-    b_rows[q] = wx + static_cast<size_t>(j < n ? j : n - 1) * kchunks;
-    b_chunk[q] = (lane % S::CH) ^ S::swz(r);
+    if constexpr (BKN) {
+      // weights stored [K][N]: this lane's column chunk of its staged K row (chunks past
+      // N repeat the last one: they reach only output columns that are never stored), and
+      // the K row itself
+      const int kr = (wv * S::B_LOADS + q) * 2 + lane / 32;
+      const int c = col0 / 8 + ((lane % 32) ^ (4 * (kr % 4)));
+      b_rows[q] = wx + (c < n / 8 ? c : n / 8 - 1);
+      b_chunk[q] = kr;
+    } else {
+      const int r = (wv * S::B_LOADS + q) * S::ROWS_PER_LOAD + lane / S::CH;
+      const int j = col0 + r;
+      b_rows[q] = wx + static_cast<size_t>(j < n ? j : n - 1) * kchunks;
+      b_chunk[q] = (lane % S::CH) ^ S::swz(r);
+    }
   }
   auto stage_a = [&](int buf) { return lds + buf * S::STAGE_BYTES + wv * S::A_LOADS * 1024; };
   auto stage_b = [&](int buf) {
@@ -171,7 +219,8 @@ __attribute__((amdgpu_waves_per_eu(NW / 2, NW / 2))) void expert_gemm_kernel(
   auto issue = [&](int kt) {
     const int buf = kt % STAGES;
     stage_rows<S::A_LOADS, S::CH>(a_rows, a_chunk, kt, kchunks, stage_a(buf));
-    stage_rows<S::B_LOADS, S::CH>(b_rows, b_chunk, kt, kchunks, stage_b(buf));
+    if constexpr (BKN) stage_rows_kn<S::B_LOADS>(b_rows, b_chunk, kt, m, n / 8, stage_b(buf));
+    else stage_rows<S::B_LOADS, S::CH>(b_rows, b_chunk, kt, kchunks, stage_b(buf));
   };
   // make stage kt visible to the workgroup: this wave's loads for it have landed (at most
   // the loads of the stages issued after it remain), the K-tail slots are cleared, then
@@ -184,7 +233,7 @@ __attribute__((amdgpu_waves_per_eu(NW / 2, NW / 2))) void expert_gemm_kernel(
     if ((kt + 1) * BK > m) {
       const int buf = kt % STAGES;
       clear_slots<S::A_LOADS, S::CH>(a_chunk, kt, kchunks, stage_a(buf), lane);
-      clear_slots<S::B_LOADS, S::CH>(b_chunk, kt, kchunks, stage_b(buf), lane);
+      if constexpr (!BKN) clear_slots<S::B_LOADS, S::CH>(b_chunk, kt, kchunks, stage_b(buf), lane);
     }
     __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);
     stage_barrier();
@@ -204,6 +253,13 @@ __attribute__((amdgpu_waves_per_eu(NW / 2, NW / 2))) void expert_gemm_kernel(
   const int a_frag = (wm * WM + (lane & 31)) * S::ROW_BYTES;
   const int b_frag = S::BM * S::ROW_BYTES + (wn * WN + (lane & 31)) * S::ROW_BYTES;
   const int fswz = S::swz(lane & 31);
+  // [K][N] weights: each fragment is two transposing reads. Lane j of 16-lane group g
+  // points at K row 8 (g / 2) + j / 4 of the k16 step (and 4 rows further for the second
+  // read), N element 16 (g % 2) + 4 (j % 4) of the 32-column MFMA tile, at swizzled chunk
+  // position chunk ^ 4 (row % 4); it receives 4 consecutive K rows of column lane % 32.
+  const int tr_row = 8 * ((lane >> 4) >> 1) + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int tr_swz = 4 * ((lane & 15) >> 2);
   chunk_t fa[2][S::FM], fb[2][S::FN];
   auto read_frags = [&](int kt, int ks, int fbuf) {
     const char* st = lds + (kt % STAGES) * S::STAGE_BYTES;
@@ -212,8 +268,17 @@ __attribute__((amdgpu_waves_per_eu(NW / 2, NW / 2))) void expert_gemm_kernel(
     for (int i = 0; i < S::FM; ++i)
       fa[fbuf][i] = *reinterpret_cast<const chunk_t*>(st + a_frag + i * 32 * S::ROW_BYTES + slot);
 #pragma unroll
-    for (int jj = 0; jj < S::FN; ++jj)
-      fb[fbuf][jj] = *reinterpret_cast<const chunk_t*>(st + b_frag + jj * 32 * S::ROW_BYTES + slot);
+    for (int jj = 0; jj < S::FN; ++jj) {
+      if constexpr (BKN) {
+        const int byte = (wn * WN + jj * 32 + tr_col) * 2;
+        const char* p = st + S::BM * S::ROW_BYTES + (ks * 16 + tr_row) * 512 + (((byte >> 4) ^ tr_swz) << 4) +
+                        (byte & 15);
+        const uint2 lo = read_tr16(p), hi = read_tr16(p + 4 * 512);
+        fb[fbuf][jj] = chunk_t{lo.x, lo.y, hi.x, hi.y};
+      } else {
+        fb[fbuf][jj] = *reinterpret_cast<const chunk_t*>(st + b_frag + jj * 32 * S::ROW_BYTES + slot);
+      }
+    }
   };
   auto mfmas = [&](int fbuf) {
 #pragma unroll
@@ -297,25 +362,32 @@ static int64_t row_block_bound(const LayoutView& L, int BM) {
   return (static_cast<int64_t>(L.s) * L.k + BM - 1) / BM + L.e;
 }
 
-int64_t expert_gemm_grid(const LayoutView& L, int n) {
+static int64_t tile_grid(const LayoutView& L, int BM, int BN, int n) {
   if (L.s == 0) return 0;
-  const int BM = use_tall(L) ? 2 * kTallWM : 2 * kShortWM;
-  const int BN = use_tall(L) ? kTallNW * kTallWN : kShortNW * kShortWN;
   const int64_t col_blocks = (n + BN - 1) / BN;
   const int64_t tiles = row_block_bound(L, BM) * col_blocks;
   return (tiles + kXcds - 1) / kXcds * kXcds;
 }
 
-template <int DT, bool GATHER, bool SCALE, int WM, int WN, int NW, int BK, int STAGES>
+int64_t expert_gemm_grid(const LayoutView& L, int n) {
+  return use_tall(L) ? tile_grid(L, 2 * kTallWM, kTallNW * kTallWN, n)
+                     : tile_grid(L, 2 * kShortWM, kShortNW * kShortWN, n);
+}
+
+int64_t expert_gemm_kn_grid(const LayoutView& L, int N) {
+  return tile_grid(L, 2 * kTallWM, kTallNW * kTallWN, N);
+}
+
+template <int DT, bool GATHER, bool SCALE, bool BKN, int WM, int WN, int NW, int BK, int STAGES>
 static hipError_t gemm_launch(const LayoutView& L, const void* a, const void* w,
                               const float* route_w, int m, int n, void* out, hipStream_t stream) {
   using S = GemmShape<WM, WN, NW, BK, STAGES>;
-  auto kern = expert_gemm_kernel<DT, GATHER, SCALE, WM, WN, NW, BK, STAGES>;
+  auto kern = expert_gemm_kernel<DT, GATHER, SCALE, BKN, WM, WN, NW, BK, STAGES>;
   // dynamic LDS above the 64 KiB default needs the per-kernel limit raised (idempotent)
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS_BYTES);
   if (err != hipSuccess) return err;
-  const int64_t grid = expert_gemm_grid(L, n);
+  const int64_t grid = tile_grid(L, S::BM, S::BN, n);
   if (grid == 0) return hipSuccess;
   const int col_blocks = (n + S::BN - 1) / S::BN;
   kern<<<static_cast<unsigned>(grid), S::THREADS, S::LDS_BYTES, stream>>>(
@@ -324,13 +396,13 @@ static hipError_t gemm_launch(const LayoutView& L, const void* a, const void* w,
   return hipGetLastError();
 }
 
-template <int DT, bool GATHER, bool SCALE>
+template <int DT, bool GATHER, bool SCALE, bool BKN = false>
 static hipError_t gemm_shape(const LayoutView& L, const void* a, const void* w,
                              const float* route_w, int m, int n, void* out, hipStream_t stream) {
   if (use_tall(L))
-    return gemm_launch<DT, GATHER, SCALE, kTallWM, kTallWN, kTallNW, kTallBK, kTallStages>(
+    return gemm_launch<DT, GATHER, SCALE, BKN, kTallWM, kTallWN, kTallNW, kTallBK, kTallStages>(
         L, a, w, route_w, m, n, out, stream);
-  return gemm_launch<DT, GATHER, SCALE, kShortWM, kShortWN, kShortNW, kShortBK, kShortStages>(
+  return gemm_launch<DT, GATHER, SCALE, BKN, kShortWM, kShortWN, kShortNW, kShortBK, kShortStages>(
       L, a, w, route_w, m, n, out, stream);
 }
 
@@ -355,6 +427,20 @@ hipError_t launch_expert_gemm(const LayoutView& L, const void* a, bool gather, c
   }
   // rows no route fills are zero
   return launch_zero_unfilled_rows(L, out, static_cast<int64_t>(n) * 2 / 16, stream);
+}
+
+hipError_t launch_expert_gemm_kn(const LayoutView& L, const void* a, const void* w, int K, int N,
+                                 int dtype, void* out, hipStream_t stream) {
+  if (L.s > 0) {
+    const hipError_t err =
+        dtype == kBF16
+            ? gemm_launch<kBF16, false, false, true, kTallWM, kTallWN, kTallNW, kTallBK, kTallStages>(
+                  L, a, w, nullptr, K, N, out, stream)
+            : gemm_launch<kF16, false, false, true, kTallWM, kTallWN, kTallNW, kTallBK, kTallStages>(
+                  L, a, w, nullptr, K, N, out, stream);
+    if (err != hipSuccess) return err;
+  }
+  return launch_zero_unfilled_rows(L, out, static_cast<int64_t>(N) * 2 / 16, stream);
 }
 
 }  // namespace moe

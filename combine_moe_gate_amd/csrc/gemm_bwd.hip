@@ -433,179 +433,6 @@ void expert_gemm_wgrad_kernel(const chunk_t* __restrict__ a, const chunk_t* __re
   }
 }
 
-// ---------------------------------------------------------------------------------
-// Input-row gradient: grad_A[r] = grad_out[r] @ W[x] for the placed rows r of expert x,
-// [rows, m]; the token gradient is the dispatch backward of it. The rows operand
-// (grad_out, contiguous along the reduction over n) is staged [256 rows][64] with a
-// 144-byte pitch, on which the 16 rows a 16-byte fragment read touches fall on distinct
-// banks; the weights (contiguous along m) are staged [64 n-rows][256 m] with the 576-byte
-// pitch and read with the transposing LDS read, as in the weight gradient. Tiles are the
-// forward's: 256 rows of one expert's segment x 256 columns, in the same banded,
-// XCD-contiguous order.
-
-constexpr int kDgPitchA = 64 * 2 + 16;  // bytes per staged grad_out row
-constexpr int kDgABytes = 256 * kDgPitchA;
-constexpr int kDgStageBytes = kDgABytes + kWgBK * kWgPitch;
-constexpr int kDgLdsBytes = 2 * kDgStageBytes;  // 147456 bytes
-constexpr int kDgBandRows = 16;
-
-template <int DT>
-__global__ __launch_bounds__(kWgThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void expert_gemm_dgrad_kernel(const chunk_t* __restrict__ g, const chunk_t* __restrict__ w,
-                              const int32_t* __restrict__ kept, const int32_t* __restrict__ offsets,
-                              int e, int m, int n, int col_blocks, uint16_t* __restrict__ out) {
-  extern __shared__ __attribute__((aligned(1024))) char lds[];  // [2 stages][grad_out rows | W rows]
-  __shared__ int32_t tile_info[3];
-  const int tid = threadIdx.x;
-  const int lane = lane_id();
-  const int wv = wave_in_block();
-  if (wv == 0) {
-    const TileCoord tc = find_tile<256>(blockIdx.x, e, kept, col_blocks, kDgBandRows);
-    if (lane == 0) {
-      tile_info[0] = tc.expert;
-      tile_info[1] = tc.rb;
-      tile_info[2] = tc.cb;
-    }
-  }
-  __syncthreads();
-  const int x = tile_info[0];
-  if (x < 0) return;  // uniform per workgroup
-  const int row0 = offsets[x] + tile_info[1] * 256;
-  const int rem = kept[x] - tile_info[1] * 256;
-  const int nrows = rem < 256 ? rem : 256;
-  const int m0 = tile_info[2] * 256;
-  const int n_chunks = n / 8, m_chunks = m / 8;
-  const int nk = (n + kWgBK - 1) / kWgBK;
-  const chunk_t* wx = w + static_cast<size_t>(x) * n * m_chunks;
-
-  // staging: grad_out rows a_r + 64 h (chunk a_c of the K step); W rows b_r + 16 h of the
-  // K step (chunk b_c of the tile's columns; past m: the last chunk, never stored)
-  const int a_c = tid % 8, a_r = tid / 8;
-  const int b_c = tid % 32, b_r = tid / 32;
-  const int mc = m0 / 8 + b_c < m_chunks ? m0 / 8 + b_c : m_chunks - 1;
-  const chunk_t* a_row[4];
-#pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    const int r = a_r + 64 * h;  // rows past the segment repeat its first row: never stored
-    a_row[h] = g + static_cast<size_t>(row0 + (r < nrows ? r : 0)) * n_chunks;
-  }
-  chunk_t ra[4], rb[4];
-  auto issue = [&](int kt) {
-    const chunk_t zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const int kq = kt * 8 + a_c;
-      ra[h] = kq < n_chunks ? a_row[h][kq] : zero;
-      const int kr = kt * kWgBK + b_r + 16 * h;
-      rb[h] = kr < n ? wx[static_cast<size_t>(kr) * m_chunks + mc] : zero;
-    }
-  };
-  auto publish = [&](int kt) {
-    char* st = lds + (kt & 1) * kDgStageBytes;
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      *reinterpret_cast<chunk_t*>(st + (a_r + 64 * h) * kDgPitchA + a_c * 16) = ra[h];
-      *reinterpret_cast<chunk_t*>(st + kDgABytes + (b_r + 16 * h) * kWgPitch + b_c * 16) = rb[h];
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);
-    stage_barrier();
-  };
-
-  const int wave_r = wv >> 2, wave_c = wv & 3;  // this wave's 128 rows x 64 columns
-  const int q = lane >> 4, j = lane & 15;
-  const int frag_off = (8 * (q >> 1) + (j >> 2)) * kWgPitch + (16 * (q & 1) + 4 * (j & 3)) * 2;
-  f32x16_t acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.0f;
-  chunk_t fa[2][4], fb[2][2];
-  auto read_frags = [&](int kt, int ks, int fbuf) {
-    const char* st = lds + (kt & 1) * kDgStageBytes;
-    const char* pa = st + (wave_r * 128 + (lane & 31)) * kDgPitchA + (2 * ks + (lane >> 5)) * 16;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa[fbuf][i] = *reinterpret_cast<const chunk_t*>(pa + i * 32 * kDgPitchA);
-    const char* pb = st + kDgABytes + frag_off + ks * 16 * kWgPitch + wave_c * 64 * 2;
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const uint2 lo = read_tr(pb + jj * 64), hi = read_tr(pb + jj * 64 + 4 * kWgPitch);
-      fb[fbuf][jj] = chunk_t{lo.x, lo.y, hi.x, hi.y};
-    }
-  };
-
-  issue(0);
-  publish(0);
-  read_frags(0, 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) issue(kt + 1);
-#pragma unroll
-    for (int ks = 0; ks < kWgBK / 16; ++ks) {
-      __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);
-      __builtin_amdgcn_sched_barrier(0);
-      if (ks + 1 < kWgBK / 16) {
-        read_frags(kt, ks + 1, (ks + 1) & 1);
-      } else if (kt + 1 < nk) {
-        publish(kt + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(kt + 1, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-          acc[i][jj] = mfma_32x32x16<DT>(fa[ks & 1][i], fb[ks & 1][jj], acc[i][jj]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int col = m0 + wave_c * 64 + jj * 32 + (lane & 31);
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = wave_r * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (row < nrows && col < m) out[static_cast<size_t>(row0 + row) * m + col] = narrow<DT>(acc[i][jj][v]);
-      }
-    }
-  }
-}
-
-int64_t expert_gemm_dgrad_grid(const LayoutView& L, int m) {
-  if (L.s == 0) return 0;
-  const int64_t rb = L.capacity > 0 ? static_cast<int64_t>(L.e) * ((L.capacity + 255) / 256)
-                                    : (static_cast<int64_t>(L.s) * L.k + 255) / 256 + L.e;
-  const int64_t tiles = rb * ((m + 255) / 256);
-  return (tiles + kXcds - 1) / kXcds * kXcds;
-}
-
-template <int DT>
-static hipError_t dgrad_launch(const LayoutView& L, const void* grad_out, const void* w, int m,
-                               int n, void* out, hipStream_t stream) {
-  auto kern = expert_gemm_dgrad_kernel<DT>;
-  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kDgLdsBytes);
-  if (err != hipSuccess) return err;
-  const int64_t grid = expert_gemm_dgrad_grid(L, m);
-  if (grid == 0) return hipSuccess;
-  kern<<<static_cast<unsigned>(grid), kWgThreads, kDgLdsBytes, stream>>>(
-      static_cast<const chunk_t*>(grad_out), static_cast<const chunk_t*>(w), L.kept, L.offsets, L.e,
-      m, n, static_cast<int>((m + 255) / 256), static_cast<uint16_t*>(out));
-  return hipGetLastError();
-}
-
-hipError_t launch_expert_gemm_dgrad(const LayoutView& L, const void* grad_out, const void* w,
-                                    int m, int n, int dtype, void* out, hipStream_t stream) {
-  const hipError_t err = dtype == kBF16 ? dgrad_launch<kBF16>(L, grad_out, w, m, n, out, stream)
-                                        : dgrad_launch<kF16>(L, grad_out, w, m, n, out, stream);
-  if (err != hipSuccess) return err;
-  return launch_zero_unfilled_rows(L, out, static_cast<int64_t>(m) * 2 / 16, stream);
-}
-
 // Workgroups of the weight-gradient kernel: one per CU, a multiple of the XCD count.
 static int wgrad_grid() {
   int dev = 0, cus = 0;

@@ -78,11 +78,12 @@ hipError_t launch_expert_gemm(const LayoutView& L, const void* a, bool gather, c
 hipError_t launch_expert_gemm_wgrad(const LayoutView& L, const void* a, bool gather,
                                     const void* grad_out, int m, int n, int dtype, bool out_f32,
                                     void* grad_w, hipStream_t stream);
-// Input-row gradient of the grouped expert GEMM: grad_A[r] = grad_out[r] @ w[x] for the
-// placed rows of expert x, [rows, m] of dtype; unfilled rows zeroed.
-hipError_t launch_expert_gemm_dgrad(const LayoutView& L, const void* grad_out, const void* w,
-                                    int m, int n, int dtype, void* out, hipStream_t stream);
-int64_t expert_gemm_dgrad_grid(const LayoutView& L, int m);
+// The grouped expert GEMM with weights stored [K][N] per expert (each K row contiguous
+// along N), on placed rows a[r] (no gather, no route weight): out[r] = a[r] @ w[x], [rows,
+// N] of dtype; unfilled rows zeroed. dtype bf16 or f16; K, N multiples of 8.
+hipError_t launch_expert_gemm_kn(const LayoutView& L, const void* a, const void* w, int K, int N,
+                                 int dtype, void* out, hipStream_t stream);
+int64_t expert_gemm_kn_grid(const LayoutView& L, int N);  // its workgroups (0 if none)
 // Workgroups the grouped expert GEMM launches for these sizes (0 if none).
 int64_t expert_gemm_grid(const LayoutView& L, int n);
 

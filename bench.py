@@ -321,6 +321,22 @@ def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None, 
         if i >= 2:
             per_op["_copy_reference"].append(a.elapsed_time(b) * 1e3)
     del csrc, cdst
+    if variant == "expert_gemm":
+        # library reference: torch.matmul (hipBLASLt) on one dense bf16/f16 product with the
+        # same FLOPs ([placed rows, m] x [m, n]), timed the same way
+        da = torch.randn((kept, m), device=dev, dtype=torch.float32).to(tdt)
+        db = torch.randn((W.EXPERT_WIDTH, m), device=dev, dtype=torch.float32).to(tdt)
+        dc = torch.empty((kept, W.EXPERT_WIDTH), device=dev, dtype=tdt)
+        per_op["_dense_gemm_reference"] = []
+        for i in range(min(steps, 10) + 2):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            torch.mm(da, db.t(), out=dc)
+            b.record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                per_op["_dense_gemm_reference"].append(a.elapsed_time(b) * 1e3)
+        del da, db, dc
     flags, _ = M.moe_layout_read(L)
     if flags != 0:
         raise RuntimeError(f"layout flags {flags} on a valid workload")
@@ -443,6 +459,7 @@ def main():
     abytes = algorithmic_bytes(w, kept, rows, args.variant)
     copy_us = per_op.pop("_copy_reference")
     layer_us = per_op.pop("layer_train_step", None)
+    dense_us = per_op.pop("_dense_gemm_reference", None)
     ops = list(per_op)
     kernels = {}
     for op in ops:
@@ -515,6 +532,11 @@ def main():
                            "bytes": copy_moved, "us": round(float(np.mean(copy_us)), 2),
                            "GBps": round(copy_gbps, 1), "frac_of_hbm_peak": round(copy_gbps / HBM_PEAK_GBPS, 4)},
         "roofline": roofline,
+        "dense_gemm_reference": None if dense_us is None else {
+            "what": "torch.mm (hipBLASLt) on one dense [placed rows, m] x [m, n] product of the same "
+                    "FLOPs and dtype, no grouping or gather",
+            "us": round(float(np.mean(dense_us)), 2),
+            "TFLOPs": round(2 * kept * W.EXPERT_WIDTH * w.m / float(np.mean(dense_us)) / 1e6, 1)},
         "layer_train_step": None if layer_us is None else {
             "what": "autograd forward + backward of the layer: gate, layout, fused expert GEMM, weighted "
                     "combine; gradients of tokens, expert weights (element type) and router logits",

@@ -337,6 +337,38 @@ def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None, 
             if i >= 2:
                 per_op["_dense_gemm_reference"].append(a.elapsed_time(b) * 1e3)
         del da, db, dc
+        # the usual PyTorch ways to run the same grouped product on the dispatched buffer
+        # (the dispatch itself not counted): torch.mm per expert, and torch._grouped_mm
+        M.moe_dispatch(L, x, out=buf)
+        kept_h, offs_h = L.kept.cpu().numpy(), L.offsets.cpu().numpy()
+        H3 = torch.empty((rows, W.EXPERT_WIDTH), dtype=tdt, device=dev)
+        wd = wts.detach()
+
+        def per_expert_loop():
+            for xe in range(e):
+                if kept_h[xe] > 0:
+                    r0, r1 = int(offs_h[xe]), int(offs_h[xe] + kept_h[xe])
+                    torch.mm(buf[r0:r1], wd[xe].t(), out=H3[r0:r1])
+
+        refs = [("_torch_mm_per_expert", per_expert_loop)]
+        if hasattr(torch, "_grouped_mm") and cap <= 0 and opts["pad_multiple"] == 1:
+            ends = torch.from_numpy(offs_h[1:].astype(np.int32)).to(dev)
+            wT = wd.transpose(1, 2)
+            refs.append(("_torch_grouped_mm", lambda: torch._grouped_mm(buf, wT, offs=ends)))
+        for op, fn in refs:
+            try:
+                fn()
+            except RuntimeError:  # not supported by this torch build
+                continue
+            per_op[op] = []
+            for i in range(min(steps, 10)):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                torch.cuda.synchronize()
+                per_op[op].append(a.elapsed_time(b) * 1e3)
+        del H3
     flags, _ = M.moe_layout_read(L)
     if flags != 0:
         raise RuntimeError(f"layout flags {flags} on a valid workload")
@@ -460,6 +492,8 @@ def main():
     copy_us = per_op.pop("_copy_reference")
     layer_us = per_op.pop("layer_train_step", None)
     dense_us = per_op.pop("_dense_gemm_reference", None)
+    grouped_refs = {name[1:]: per_op.pop(name) for name in ("_torch_mm_per_expert", "_torch_grouped_mm")
+                    if name in per_op}
     ops = list(per_op)
     kernels = {}
     for op in ops:
@@ -537,6 +571,11 @@ def main():
                     "FLOPs and dtype, no grouping or gather",
             "us": round(float(np.mean(dense_us)), 2),
             "TFLOPs": round(2 * kept * W.EXPERT_WIDTH * w.m / float(np.mean(dense_us)) / 1e6, 1)},
+        "grouped_gemm_references": None if not grouped_refs else {
+            "what": "the same grouped product in PyTorch on the dispatched buffer (dispatch not counted)",
+            **{name: {"us": round(float(np.mean(v)), 2),
+                      "TFLOPs": round(2 * kept * W.EXPERT_WIDTH * w.m / float(np.mean(v)) / 1e6, 1)}
+               for name, v in grouped_refs.items()}},
         "layer_train_step": None if layer_us is None else {
             "what": "autograd forward + backward of the layer: gate, layout, fused expert GEMM, weighted "
                     "combine; gradients of tokens, expert weights (element type) and router logits",

@@ -355,6 +355,10 @@ def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None, 
             ends = torch.from_numpy(offs_h[1:].astype(np.int32)).to(dev)
             wT = wd.transpose(1, 2)
             refs.append(("_torch_grouped_mm", lambda: torch._grouped_mm(buf, wT, offs=ends)))
+            # and the two gradients (the forward's output standing in for the incoming
+            # gradient, as above): rows @ W[x], and per expert grad^T @ rows into [e, n, m]
+            refs.append(("_torch_grouped_mm_input_grad", lambda: torch._grouped_mm(H, wd, offs=ends)))
+            refs.append(("_torch_grouped_mm_weight_grad", lambda: torch._grouped_mm(H.t(), buf, offs=ends)))
         for op, fn in refs:
             try:
                 fn()
@@ -492,7 +496,9 @@ def main():
     copy_us = per_op.pop("_copy_reference")
     layer_us = per_op.pop("layer_train_step", None)
     dense_us = per_op.pop("_dense_gemm_reference", None)
-    grouped_refs = {name[1:]: per_op.pop(name) for name in ("_torch_mm_per_expert", "_torch_grouped_mm")
+    grouped_refs = {name[1:]: per_op.pop(name) for name in ("_torch_mm_per_expert", "_torch_grouped_mm",
+                                                            "_torch_grouped_mm_input_grad",
+                                                            "_torch_grouped_mm_weight_grad")
                     if name in per_op}
     ops = list(per_op)
     kernels = {}
@@ -572,7 +578,8 @@ def main():
             "us": round(float(np.mean(dense_us)), 2),
             "TFLOPs": round(2 * kept * W.EXPERT_WIDTH * w.m / float(np.mean(dense_us)) / 1e6, 1)},
         "grouped_gemm_references": None if not grouped_refs else {
-            "what": "the same grouped product in PyTorch on the dispatched buffer (dispatch not counted)",
+            "what": "the same grouped products in PyTorch on the dispatched buffer (dispatch not counted); "
+                    "the gradients' references in the element type",
             **{name: {"us": round(float(np.mean(v)), 2),
                       "TFLOPs": round(2 * kept * W.EXPERT_WIDTH * w.m / float(np.mean(v)) / 1e6, 1)}
                for name, v in grouped_refs.items()}},

@@ -30,13 +30,18 @@ Readings where the pages are silent (each one is also listed in the design notes
   * Routing checksum: sum over routes of (idx + 1) * (t*k + j + 1) modulo 2**64,
     with idx read as a signed 32-bit integer. The checksum compared in the
     checkpoint-recompute page has no published definition; this one is ours.
+  * Grouped expert GEMM: one projection per expert, weights [e, n, m]; its sums
+    are exact (float64) and rounded once to the element type (forward, input-row
+    gradient) or to float32 (weight gradient), the latter optionally rounded once
+    more, to nearest even, to the element type.
 
 Parity status: every function here is pinned by the `not gpu` tests (brute
 force on tiny inputs, the dense one-hot einsum the index path replaced, closed
 forms, finite differences and adjoint identities; the grouped expert GEMM and its
-weight gradient by loops, scaled identities, the forward/backward adjoint identity
-and exact integer derivatives). The routing checksum is our own definition and is
-pinned only by a hand-worked fixture.
+two gradients by loops, scaled identities, the forward/backward adjoint identities
+and exact integer derivatives, the weight gradient kept in the element type by
+ties-to-even sums). The routing checksum is our own definition and is pinned only
+by a hand-worked fixture.
 """
 from __future__ import annotations
 

@@ -8,7 +8,7 @@
 namespace moe {
 
 constexpr int kWave = 64;           // CDNA wavefront width
-constexpr int kBlock = 256;         // threads per workgroup in the row kernels
+constexpr int kBlock = 256;         // threads per workgroup of the gate kernels
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kTileTokens = 256;    // tokens per layout tile (one workgroup)
 

@@ -165,6 +165,9 @@ ROW_CASES = [
     (64, 8, "bf16", 1024, 16, 0),
     (2000, 1032, "bf16", 128, 8, 0),
     (129, 520, "f16", 3, 1, 20),
+    # rows longer than one group per wave (more than 8 KiB): waves take several groups
+    (300, 8200, "bf16", 16, 4, 0),
+    (200, 2052, "f32", 8, 2, 30),
 ]
 
 

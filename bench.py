@@ -293,6 +293,29 @@ def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None, 
     for ev in events:
         for j, op in enumerate(names):
             per_op[op].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)  # microseconds
+    if flush_mib == 0:
+        # the same step captured once in a HIP graph and replayed, outside the timed region:
+        # the host then launches one graph instead of each kernel (the path has no memsets,
+        # allocations or host syncs, so it captures as it is)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        gev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        gev[0].record()
+        for i in range(steps):
+            graph.replay()
+            gev[i + 1].record()
+        torch.cuda.synchronize()
+        per_op["_graph_step"] = [gev[i].elapsed_time(gev[i + 1]) * 1e3 for i in range(steps)]
+        del graph
     for op, fn in extra.get("unfused", []) + extra.get("layer", []):  # outside the timed step
         per_op[op] = []
         fn()  # the first call sets up the autograd graph and allocator
@@ -495,6 +518,7 @@ def main():
     abytes = algorithmic_bytes(w, kept, rows, args.variant)
     copy_us = per_op.pop("_copy_reference")
     layer_us = per_op.pop("layer_train_step", None)
+    graph_us = per_op.pop("_graph_step", None)
     dense_us = per_op.pop("_dense_gemm_reference", None)
     grouped_refs = {name[1:]: per_op.pop(name) for name in ("_torch_mm_per_expert", "_torch_grouped_mm",
                                                             "_torch_grouped_mm_input_grad",
@@ -583,6 +607,11 @@ def main():
             **{name: {"us": round(float(np.mean(v)), 2),
                       "TFLOPs": round(2 * kept * W.EXPERT_WIDTH * w.m / float(np.mean(v)) / 1e6, 1)}
                for name, v in grouped_refs.items()}},
+        "graph_step": None if graph_us is None else {
+            "what": "the same step captured once in a HIP graph and replayed (HIP events per replay)",
+            "us": round(float(np.mean(graph_us)), 2), "us_median": round(float(np.median(graph_us)), 2),
+            "tokens_per_s": round(w.s / (float(np.mean(graph_us)) / 1e6), 1),
+            "speedup_vs_eager": round(ms_per_step * 1e3 / float(np.mean(graph_us)), 3)},
         "layer_train_step": None if layer_us is None else {
             "what": "autograd forward + backward of the layer: gate, layout, fused expert GEMM, weighted "
                     "combine; gradients of tokens, expert weights (element type) and router logits",

@@ -1,0 +1,75 @@
+"""Host-side logic of bench.py (no GPU): the algorithmic byte counts it reports against,
+the gating of counter-measured traffic by the kernel sources' digest, and the refusal of
+more than one GPU.
+
+The byte counts are pinned to figures worked out independently of bench.py from the
+per-call formulas (x read once, every placed row written or read once, 4 bytes of slot
+map per route, 8 with the route weight): the dispatch + combine bytes and bytes per token
+of the three dropless workloads, and the backward bytes of the Zipf workload.
+"""
+import subprocess
+import sys
+
+import pytest
+
+import bench
+import workloads as W
+
+
+@pytest.mark.parametrize("name,total,per_token", [
+    ("dropless_top8_h2816", 415_629_312, 101_472),
+    ("zipf_skew_h4096", 1_208_745_984, 147_552),
+    ("checkpoint_replay_h2816", 3_325_034_496, 101_472),
+])
+def test_dispatch_combine_bytes_of_the_dropless_workloads(name, total, per_token):
+    w = W.WORKLOADS[name]
+    ab = bench.algorithmic_bytes(w, kept_routes=w.s * w.k)  # dropless: every route placed
+    assert ab["dispatch"] + ab["combine"] == total
+    assert total // w.s == per_token
+
+
+def test_backward_bytes_of_the_zipf_workload():
+    w = W.WORKLOADS["zipf_skew_h4096"]
+    ab = bench.algorithmic_bytes(w, kept_routes=w.s * w.k)
+    # combine backward: grad_y once, every expert row read, every buffer row written, and
+    # per route its slot, weight and weight gradient
+    assert ab["combine_bwd"] == 1_141_637_120
+    assert ab["dispatch_bwd"] == 604_241_920
+
+
+def test_dropped_routes_are_not_counted_as_read():
+    w = W.WORKLOADS["gshard_capacity_drop"]
+    full = bench.algorithmic_bytes(w, kept_routes=w.s * w.k)
+    part = bench.algorithmic_bytes(w, kept_routes=w.s * w.k - 100)
+    row = w.m * W.ELEM_BYTES[w.dtype]
+    assert full["combine"] - part["combine"] == 100 * row
+    assert full["dispatch"] == part["dispatch"]  # the [e, c, m] buffer is written whole
+
+
+def _write_traffic(root, digest):
+    prof = root / "profiles"
+    prof.mkdir()
+    (prof / "traffic_zipf_skew_h4096.txt").write_text(
+        "# summary\n\ntraffic dispatch 606666937\ntraffic combine 606132834\n"
+        f"source_digest {digest}\n")
+
+
+def test_traffic_is_reported_only_for_the_sources_it_was_taken_on(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    _write_traffic(tmp_path, bench.kernel_source_digest())
+    assert bench.measured_traffic("zipf_skew_h4096") == {"dispatch": 606666937, "combine": 606132834}
+    assert bench.measured_traffic("zipf_skew_h4096", "expert_gemm") == {}  # no such summary
+
+
+def test_traffic_of_other_sources_is_dropped(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    _write_traffic(tmp_path, "0123456789abcdef")
+    assert bench.measured_traffic("zipf_skew_h4096") == {}
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    res = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
+    assert res.stdout == ""

@@ -41,6 +41,10 @@ HBM_PEAK_GBPS = 8000.0
 # GEMM with the dispatch fused into its operand loads, weighted combine.
 VARIANTS = ("route_major", "pad128", "weights_before", "renorm_kept", "expert_gemm")
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+# cold-cache headline pair: a read of this much scratch before each of COLD_PAIRS
+# dispatch + combine pairs (more than L2 and the 256 MB Infinity Cache together)
+COLD_FLUSH_MIB = 1024
+COLD_PAIRS = 20
 
 
 def kernel_source_digest() -> str:
@@ -121,6 +125,20 @@ def algorithmic_bytes(w: W.Workload, kept_routes: int, rows: int | None = None,
 
 
 _WEIGHTS = {}
+
+
+def cold_pair_summary(s: int, disp_us, comb_us, nbytes: int) -> dict:
+    """Per-pair statistics of the cold-cache dispatch + combine (event microseconds)."""
+    pair = np.asarray(disp_us, dtype=np.float64) + np.asarray(comb_us, dtype=np.float64)
+    us = float(np.mean(pair))
+    gbps = nbytes / us / 1e3
+    return {"what": f"dispatch + combine with a {COLD_FLUSH_MIB} MiB read of scratch before each pair, "
+                    "outside its events (neither L2 nor the Infinity Cache holds the pair's data)",
+            "pairs": int(pair.size), "tokens_per_s": round(s / (us / 1e6), 1), "GBps": round(gbps, 1),
+            "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "us": round(us, 2),
+            "us_median": round(float(np.median(pair)), 2), "us_min": round(float(np.min(pair)), 2),
+            "dispatch_us": round(float(np.mean(disp_us)), 2), "combine_us": round(float(np.mean(comb_us)), 2),
+            "bytes": int(nbytes)}
 
 
 def expert_weights(w: W.Workload):
@@ -316,6 +334,27 @@ def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None, 
         torch.cuda.synchronize()
         per_op["_graph_step"] = [gev[i].elapsed_time(gev[i + 1]) * 1e3 for i in range(steps)]
         del graph
+    if flush_mib == 0 and variant != "expert_gemm":
+        # the headline pair with cold caches, outside the timed step: before each
+        # dispatch + combine, outside its events, read 1 GiB of scratch so that neither L2
+        # nor the Infinity Cache holds x or the buffer (a read leaves only clean lines)
+        flush = torch.zeros((COLD_FLUSH_MIB << 20) // 4, dtype=torch.float32, device=dev)
+        dsp = next(fn for op, fn in ops if op == "dispatch")
+        cmb = next(fn for op, fn in ops if op == "combine")
+        per_op["_cold_dispatch"], per_op["_cold_combine"] = [], []
+        for i in range(COLD_PAIRS + 1):
+            a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            flush.sum()
+            a.record()
+            dsp()
+            b.record()
+            cmb()
+            c.record()
+            torch.cuda.synchronize()
+            if i > 0:  # the first pair sets up the flush's reduction
+                per_op["_cold_dispatch"].append(a.elapsed_time(b) * 1e3)
+                per_op["_cold_combine"].append(b.elapsed_time(c) * 1e3)
+        del flush
     for op, fn in extra.get("unfused", []) + extra.get("layer", []):  # outside the timed step
         per_op[op] = []
         fn()  # the first call sets up the autograd graph and allocator
@@ -519,6 +558,7 @@ def main():
     copy_us = per_op.pop("_copy_reference")
     layer_us = per_op.pop("layer_train_step", None)
     graph_us = per_op.pop("_graph_step", None)
+    cold_d, cold_c = per_op.pop("_cold_dispatch", None), per_op.pop("_cold_combine", None)
     dense_us = per_op.pop("_dense_gemm_reference", None)
     grouped_refs = {name[1:]: per_op.pop(name) for name in ("_torch_mm_per_expert", "_torch_grouped_mm",
                                                             "_torch_grouped_mm_input_grad",
@@ -592,6 +632,8 @@ def main():
             "us_p90": round(float(np.percentile(dc_steps, 90)), 2),
             "us_min": round(float(np.min(dc_steps)), 2),
             "bytes": dc_bytes, "frac_of_copy": round(dc_gbps / copy_gbps, 4)},
+        "dispatch_combine_cold": None if cold_d is None else cold_pair_summary(
+            w.s, np.array(cold_d), np.array(cold_c), abytes["dispatch"] + abytes["combine"]),
         "copy_reference": {"what": "device-to-device copy of the dispatch+combine byte count (read + write)",
                            "bytes": copy_moved, "us": round(float(np.mean(copy_us)), 2),
                            "GBps": round(copy_gbps, 1), "frac_of_hbm_peak": round(copy_gbps / HBM_PEAK_GBPS, 4)},

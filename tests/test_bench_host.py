@@ -73,3 +73,14 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert res.returncode == 2
     assert "one GPU" in res.stderr
     assert res.stdout == ""
+
+
+def test_cold_pair_summary_adds_dispatch_and_combine_per_pair():
+    # three pairs of 100 + 110, 120 + 130 and 140 + 150 microseconds over 1.2e9 bytes:
+    # pairs of 210, 250 and 290 us, mean 250 us, so 4800 GB/s and 0.6 of 8 TB/s
+    s = bench.cold_pair_summary(8192, [100.0, 120.0, 140.0], [110.0, 130.0, 150.0], 1_200_000_000)
+    assert s["pairs"] == 3
+    assert s["us"] == 250.0 and s["us_median"] == 250.0 and s["us_min"] == 210.0
+    assert s["dispatch_us"] == 120.0 and s["combine_us"] == 130.0
+    assert s["GBps"] == 4800.0 and s["frac_of_hbm_peak"] == 0.6
+    assert s["tokens_per_s"] == round(8192 / 250e-6, 1)

@@ -2,7 +2,8 @@
 
     python -m combine_moe_gate_amd._build
 
-hipcc cross-compiles for gfx950 without a GPU present.
+hipcc cross-compiles for gfx950 without a GPU present. The same build compiles
+tests/c_abi_check, a C++ program that drives the library through its C ABI alone.
 """
 from __future__ import annotations
 
@@ -43,6 +44,23 @@ def hipcc() -> str:
     return path
 
 
+C_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi_check.cpp")
+C_CHECK_BIN = os.path.join(ROOT, "tests", "c_abi_check")
+
+
+def build_c_check(verbose: bool = False) -> str:
+    """Compile the C++ program that drives the library through its C ABI alone (a GPU
+    test runs it). It links LIB_PATH, found next to the binary through its run path."""
+    cmd = [hipcc(), "-O2", "-std=c++17", "-Wall", "-I", os.path.join(ROOT, "include"), C_CHECK_SRC,
+           "-L", HERE, "-lmoe_gate", "-Wl,-rpath,$ORIGIN/../combine_moe_gate_amd", "-o", C_CHECK_BIN]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
+    return C_CHECK_BIN
+
+
 def build(verbose: bool = False) -> str:
     """Compile every HIP source into LIB_PATH (always recompiles). Returns the path."""
     tmp = LIB_PATH + ".tmp"
@@ -55,6 +73,7 @@ def build(verbose: bool = False) -> str:
     if verbose and res.stderr.strip():
         print(res.stderr, file=sys.stderr)
     os.replace(tmp, LIB_PATH)
+    build_c_check(verbose)
     return LIB_PATH
 
 

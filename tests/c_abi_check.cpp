@@ -1,0 +1,338 @@
+// The library driven through its C ABI alone: no Python, no PyTorch. Device buffers come
+// from hipMalloc, work goes on one hipStream_t, and every result is checked on the host
+// against properties and closed forms that need no reference implementation:
+//   gate      ids distinct and in range, in descending logit order with ties to the lower
+//             id, no unselected logit above a selected one; weights sum to 1;
+//   layout    counts are the histogram of the ids; a placed route's slot is the number of
+//             earlier tokens that chose its expert (the column cumsum minus one, counted by
+//             brute force); a route is dropped exactly when that number reaches the
+//             capacity; src inverts dst; offsets are the exclusive scan of the segments;
+//   dispatch  every buffer row is its token's row bit for bit, unfilled rows are zero;
+//   combine   with unit weights over integer-valued rows, token t comes back as exactly
+//             (placed routes of t) * x[t]; the dispatch backward of the buffer likewise;
+//   backward  grad_E[dst] is the float32 product w * grad_y; with the buffer as expert
+//             output, grad_w[t,j] is exactly sum_m x[t,m]^2 (integers); the gate gradient
+//             is zero off the selection and sums to zero over it (softmax Jacobian);
+//   replay    byte-identical to the dispatch; a changed route sets the mismatch flag;
+//   errors    bad arguments return their status and a message, enqueueing nothing.
+// Prints "c_abi_check: ok" and exits 0, or lists the failures and exits 1.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "moe_gate.h"
+
+static int g_failures = 0;
+
+#define CHECK(cond, ...)                                               \
+  do {                                                                 \
+    if (!(cond)) {                                                     \
+      if (++g_failures <= 20) {                                        \
+        std::fprintf(stderr, "FAIL line %d: ", __LINE__);              \
+        std::fprintf(stderr, __VA_ARGS__);                             \
+        std::fputc('\n', stderr);                                      \
+      }                                                                \
+    }                                                                  \
+  } while (0)
+
+#define HIP_OK(call)                                                                   \
+  do {                                                                                 \
+    const hipError_t e_ = (call);                                                      \
+    if (e_ != hipSuccess) {                                                            \
+      std::fprintf(stderr, "%s: %s (line %d)\n", #call, hipGetErrorString(e_), __LINE__); \
+      std::exit(2);                                                                    \
+    }                                                                                  \
+  } while (0)
+
+#define MOE_OK_(call)                                                                  \
+  do {                                                                                 \
+    const moe_status_t s_ = (call);                                                    \
+    if (s_ != MOE_OK) {                                                                \
+      std::fprintf(stderr, "%s: %s: %s (line %d)\n", #call, moe_status_string(s_),     \
+                   moe_last_error(), __LINE__);                                        \
+      std::exit(3);                                                                    \
+    }                                                                                  \
+  } while (0)
+
+// A device array of n elements (at least one byte is allocated, so pointers are never
+// NULL even for empty arrays).
+template <class T>
+struct Dev {
+  T* p = nullptr;
+  size_t n = 0;
+  explicit Dev(size_t count) : n(count) { HIP_OK(hipMalloc(&p, std::max<size_t>(n, 1) * sizeof(T))); }
+  ~Dev() { (void)hipFree(p); }
+  Dev(const Dev&) = delete;
+  Dev& operator=(const Dev&) = delete;
+  void put(const std::vector<T>& h) {
+    if (n) HIP_OK(hipMemcpy(p, h.data(), n * sizeof(T), hipMemcpyHostToDevice));
+  }
+  std::vector<T> get() const {
+    std::vector<T> h(n);
+    if (n) HIP_OK(hipMemcpy(h.data(), p, n * sizeof(T), hipMemcpyDeviceToHost));
+    return h;
+  }
+};
+
+// splitmix64: a small counter-based generator for the inputs
+struct Rng {
+  uint64_t state;
+  uint64_t next() {
+    uint64_t z = (state += 0x9e3779b97f4a7c15ull);
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
+  }
+  int below(int n) { return static_cast<int>(next() % static_cast<uint64_t>(n)); }
+};
+
+static bool same_bits(float a, float b) { return std::memcmp(&a, &b, sizeof(float)) == 0; }
+
+static void run_case(int s, int e, int k, int m, int cap, uint64_t seed, hipStream_t st) {
+  std::printf("case s=%d e=%d k=%d m=%d capacity=%d\n", s, e, k, m, cap);
+  std::fflush(stdout);
+  Rng rng{seed};
+  // logits on a coarse grid (multiples of 1/8 in [-4, 4)) so that ties occur
+  std::vector<float> logits(static_cast<size_t>(s) * e);
+  for (auto& v : logits) v = static_cast<float>(rng.below(64) - 32) / 8.0f;
+  // integer-valued rows: every sum below is exact in float32
+  std::vector<float> x(static_cast<size_t>(s) * m);
+  for (auto& v : x) v = static_cast<float>(rng.below(17) - 8);
+
+  Dev<float> d_logits(logits.size()), d_x(x.size()), d_w(static_cast<size_t>(s) * k),
+      d_ones(static_cast<size_t>(s) * k), d_y(x.size()), d_gx(x.size()),
+      d_gw(static_cast<size_t>(s) * k), d_gl(static_cast<size_t>(s) * e);
+  Dev<int32_t> d_idx(static_cast<size_t>(s) * k);
+  d_logits.put(logits);
+  d_x.put(x);
+  d_ones.put(std::vector<float>(static_cast<size_t>(s) * k, 1.0f));
+
+  // (1) gate
+  MOE_OK_(moe_gate_topk(d_logits.p, s, e, k, d_idx.p, d_w.p, st));
+  HIP_OK(hipStreamSynchronize(st));
+  const std::vector<int32_t> idx = d_idx.get();
+  const std::vector<float> w = d_w.get();
+  for (int t = 0; t < s; ++t) {
+    const float* l = &logits[static_cast<size_t>(t) * e];
+    const int32_t* id = &idx[static_cast<size_t>(t) * k];
+    std::vector<char> chosen(e, 0);
+    double wsum = 0.0;
+    for (int j = 0; j < k; ++j) {
+      CHECK(id[j] >= 0 && id[j] < e, "t=%d j=%d id %d out of range", t, j, id[j]);
+      if (id[j] < 0 || id[j] >= e) continue;
+      CHECK(!chosen[id[j]], "t=%d expert %d chosen twice", t, id[j]);
+      chosen[id[j]] = 1;
+      if (j > 0 && id[j - 1] >= 0 && id[j - 1] < e) {
+        const float a = l[id[j - 1]], b = l[id[j]];
+        CHECK(a > b || (a == b && id[j - 1] < id[j]), "t=%d routes %d,%d out of order", t, j - 1, j);
+        CHECK(w[static_cast<size_t>(t) * k + j - 1] >= w[static_cast<size_t>(t) * k + j],
+              "t=%d weights not descending", t);
+      }
+      wsum += w[static_cast<size_t>(t) * k + j];
+    }
+    CHECK(std::fabs(wsum - 1.0) <= 1e-6, "t=%d weights sum to %.9f", t, wsum);
+    const int last = id[k - 1];
+    if (last >= 0 && last < e)
+      for (int x2 = 0; x2 < e; ++x2)
+        if (!chosen[x2])
+          CHECK(l[x2] < l[last] || (l[x2] == l[last] && x2 > last),
+                "t=%d unselected expert %d beats selected %d", t, x2, last);
+  }
+
+  // (2) layout
+  const size_t ws_bytes = moe_layout_workspace_bytes(s, e, k, cap);
+  CHECK(ws_bytes > 0, "workspace size 0");
+  Dev<unsigned char> ws(ws_bytes);
+  moe_layout_t L;
+  MOE_OK_(moe_dispatch_layout(d_idx.p, s, e, k, cap, ws.p, ws_bytes, &L, st));
+  const int64_t rows = L.rows;
+  CHECK(rows == (cap > 0 ? static_cast<int64_t>(e) * cap : static_cast<int64_t>(s) * k),
+        "rows %lld", static_cast<long long>(rows));
+  std::vector<int32_t> counts(e), kept(e), offsets(e + 1), dst(static_cast<size_t>(s) * k),
+      src(static_cast<size_t>(rows));
+  HIP_OK(hipStreamSynchronize(st));
+  HIP_OK(hipMemcpy(counts.data(), L.counts, sizeof(int32_t) * e, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(kept.data(), L.kept, sizeof(int32_t) * e, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(offsets.data(), L.offsets, sizeof(int32_t) * (e + 1), hipMemcpyDeviceToHost));
+  if (!dst.empty())
+    HIP_OK(hipMemcpy(dst.data(), L.dst, sizeof(int32_t) * dst.size(), hipMemcpyDeviceToHost));
+  if (!src.empty())
+    HIP_OK(hipMemcpy(src.data(), L.src, sizeof(int32_t) * src.size(), hipMemcpyDeviceToHost));
+  int32_t flags = -1;
+  MOE_OK_(moe_layout_read(&L, &flags, nullptr, st));
+  CHECK(flags == 0, "flags %d on valid routing", flags);
+
+  std::vector<int32_t> seen(e, 0), placed_of_token(s, 0);
+  std::vector<int> row_refs(static_cast<size_t>(rows), 0);
+  int32_t expect_off = 0;
+  for (int x2 = 0; x2 < e; ++x2) {
+    CHECK(offsets[x2] == expect_off, "offsets[%d] = %d, want %d", x2, offsets[x2], expect_off);
+    expect_off += cap > 0 ? cap : counts[x2];
+  }
+  CHECK(offsets[e] == (cap > 0 ? e * cap : s * k), "offsets[e] = %d", offsets[e]);
+  for (int t = 0; t < s; ++t)
+    for (int j = 0; j < k; ++j) {
+      const int x2 = idx[static_cast<size_t>(t) * k + j];
+      const int slot = seen[x2]++;  // earlier tokens that chose x2
+      const int32_t d = dst[static_cast<size_t>(t) * k + j];
+      if (cap > 0 && slot >= cap) {
+        CHECK(d == -1, "t=%d j=%d slot %d past capacity but placed at %d", t, j, slot, d);
+        continue;
+      }
+      CHECK(d == offsets[x2] + slot, "t=%d j=%d dst %d, want %d", t, j, d, offsets[x2] + slot);
+      if (d >= 0 && d < rows) {
+        ++row_refs[d];
+        CHECK(src[d] == t, "src[%d] = %d, want %d", d, src[d], t);
+      }
+      ++placed_of_token[t];
+    }
+  for (int x2 = 0; x2 < e; ++x2) {
+    CHECK(counts[x2] == seen[x2], "counts[%d] = %d, want %d", x2, counts[x2], seen[x2]);
+    CHECK(kept[x2] == (cap > 0 ? std::min(seen[x2], cap) : seen[x2]), "kept[%d] = %d", x2, kept[x2]);
+  }
+  for (int64_t r = 0; r < rows; ++r)
+    CHECK((row_refs[r] == 1) == (src[r] >= 0) && row_refs[r] <= 1, "row %lld referenced %d times, src %d",
+          static_cast<long long>(r), row_refs[r], src[r]);
+
+  // (3) dispatch, and its replay
+  Dev<float> d_buf(static_cast<size_t>(rows) * m), d_rep(static_cast<size_t>(rows) * m),
+      d_gE(static_cast<size_t>(rows) * m);
+  MOE_OK_(moe_dispatch(&L, d_x.p, m, MOE_F32, d_buf.p, st));
+  MOE_OK_(moe_dispatch_replay(&L, d_idx.p, d_x.p, m, MOE_F32, d_rep.p, st));
+  HIP_OK(hipStreamSynchronize(st));
+  const std::vector<float> buf = d_buf.get();
+  const std::vector<float> rep = d_rep.get();
+  for (int64_t r = 0; r < rows; ++r)
+    for (int i = 0; i < m; ++i) {
+      const float got = buf[static_cast<size_t>(r) * m + i];
+      const float want = src[r] >= 0 ? x[static_cast<size_t>(src[r]) * m + i] : 0.0f;
+      CHECK(same_bits(got, want), "buffer row %lld col %d: %g, want %g", static_cast<long long>(r), i, got, want);
+    }
+  CHECK(buf.empty() || std::memcmp(buf.data(), rep.data(), buf.size() * sizeof(float)) == 0,
+        "replay differs from dispatch");
+  MOE_OK_(moe_layout_read(&L, &flags, nullptr, st));
+  CHECK(flags == 0, "flags %d after a faithful replay", flags);
+
+  // (4) unit-weight combine and the dispatch backward of the buffer: kept_t * x[t]
+  MOE_OK_(moe_combine(&L, d_buf.p, d_ones.p, m, MOE_F32, d_y.p, st));
+  MOE_OK_(moe_dispatch_backward(&L, d_buf.p, m, MOE_F32, d_gx.p, st));
+  HIP_OK(hipStreamSynchronize(st));
+  const std::vector<float> y = d_y.get();
+  const std::vector<float> gx = d_gx.get();
+  for (int t = 0; t < s; ++t)
+    for (int i = 0; i < m; ++i) {
+      const float want = static_cast<float>(placed_of_token[t]) * x[static_cast<size_t>(t) * m + i];
+      CHECK(y[static_cast<size_t>(t) * m + i] == want, "combine t=%d col %d: %g, want %g", t, i,
+            y[static_cast<size_t>(t) * m + i], want);
+      CHECK(gx[static_cast<size_t>(t) * m + i] == want, "dispatch backward t=%d col %d", t, i);
+    }
+
+  // (5) combine backward with grad_y = x over the buffer as expert output, and the gate
+  // backward of the resulting weight gradient
+  MOE_OK_(moe_combine_backward(&L, d_x.p, d_buf.p, d_w.p, m, MOE_F32, d_gE.p, d_gw.p, st));
+  MOE_OK_(moe_gate_topk_backward(d_idx.p, d_w.p, d_gw.p, s, e, k, d_gl.p, st));
+  HIP_OK(hipStreamSynchronize(st));
+  const std::vector<float> gE = d_gE.get();
+  const std::vector<float> gw = d_gw.get();
+  const std::vector<float> gl = d_gl.get();
+  for (int t = 0; t < s; ++t) {
+    double sq = 0.0;
+    for (int i = 0; i < m; ++i) sq += static_cast<double>(x[static_cast<size_t>(t) * m + i]) * x[static_cast<size_t>(t) * m + i];
+    double gsum = 0.0, gabs = 0.0;
+    for (int j = 0; j < k; ++j) {
+      const size_t o = static_cast<size_t>(t) * k + j;
+      const int32_t d = dst[o];
+      CHECK(gw[o] == (d >= 0 ? static_cast<float>(sq) : 0.0f), "grad_w t=%d j=%d: %g, want %g", t, j, gw[o],
+            d >= 0 ? sq : 0.0);
+      if (d >= 0)
+        for (int i = 0; i < m; ++i) {
+          const float want = w[o] * x[static_cast<size_t>(t) * m + i];  // one float32 product
+          CHECK(same_bits(gE[static_cast<size_t>(d) * m + i], want), "grad_E row %d col %d", d, i);
+        }
+      const float g = gl[static_cast<size_t>(t) * e + idx[o]];
+      gsum += g;
+      gabs += std::fabs(static_cast<double>(w[o]) * gw[o]);
+    }
+    CHECK(std::fabs(gsum) <= 1e-6 * gabs + 1e-30, "t=%d gate gradient sums to %g over the selection", t, gsum);
+    std::vector<char> chosen(e, 0);
+    for (int j = 0; j < k; ++j) chosen[idx[static_cast<size_t>(t) * k + j]] = 1;
+    for (int x2 = 0; x2 < e; ++x2)
+      if (!chosen[x2]) CHECK(gl[static_cast<size_t>(t) * e + x2] == 0.0f, "t=%d gate gradient off the selection", t);
+  }
+  for (int64_t r = 0; r < rows; ++r)
+    if (src[r] < 0)
+      for (int i = 0; i < m; ++i) CHECK(gE[static_cast<size_t>(r) * m + i] == 0.0f, "grad_E unfilled row %lld", static_cast<long long>(r));
+
+  // replay against changed routing: the copy still follows the layout, the flag is set
+  if (s > 0 && k < e) {
+    std::vector<int32_t> idx2 = idx;
+    for (int x2 = 0; x2 < e; ++x2)
+      if (std::find(idx2.begin(), idx2.begin() + k, x2) == idx2.begin() + k) {
+        idx2[0] = x2;
+        break;
+      }
+    Dev<int32_t> d_idx2(idx2.size());
+    d_idx2.put(idx2);
+    MOE_OK_(moe_dispatch_replay(&L, d_idx2.p, d_x.p, m, MOE_F32, d_rep.p, st));
+    MOE_OK_(moe_layout_read(&L, &flags, nullptr, st));
+    CHECK((flags & MOE_FLAG_REPLAY_MISMATCH) != 0, "changed routing not flagged (flags %d)", flags);
+    const std::vector<float> rep2 = d_rep.get();
+    CHECK(std::memcmp(buf.data(), rep2.data(), buf.size() * sizeof(float)) == 0, "flagged replay differs");
+  }
+}
+
+static void check_errors(hipStream_t st) {
+  std::printf("case argument errors\n");
+  std::fflush(stdout);
+  Dev<float> d_logits(64), d_w(8), d_x(64);
+  Dev<int32_t> d_idx(8);
+  CHECK(moe_gate_topk(d_logits.p, 8, 8, 9, d_idx.p, d_w.p, st) == MOE_ERR_INVALID_ARG, "k > e accepted");
+  CHECK(std::strlen(moe_last_error()) > 0, "no message for k > e");
+  CHECK(moe_gate_topk(nullptr, 8, 8, 1, d_idx.p, d_w.p, st) == MOE_ERR_INVALID_ARG, "NULL logits accepted");
+  const size_t ws_bytes = moe_layout_workspace_bytes(8, 8, 1, 0);
+  Dev<unsigned char> ws(ws_bytes);
+  moe_layout_t L;
+  CHECK(moe_dispatch_layout(d_idx.p, 8, 8, 1, 0, ws.p, ws_bytes - 1, &L, st) == MOE_ERR_WORKSPACE,
+        "short workspace accepted");
+  std::vector<int32_t> idx(8);
+  for (int t = 0; t < 8; ++t) idx[t] = t;
+  d_idx.put(idx);
+  MOE_OK_(moe_dispatch_layout(d_idx.p, 8, 8, 1, 0, ws.p, ws_bytes, &L, st));
+  Dev<float> d_out(64);
+  // rows of 3 float32 are 12 bytes: not a multiple of 16
+  CHECK(moe_dispatch(&L, d_x.p, 3, MOE_F32, d_out.p, st) == MOE_ERR_MISALIGNED, "12-byte rows accepted");
+  moe_layout_t bad = L;
+  bad.magic ^= 1u;
+  CHECK(moe_dispatch(&bad, d_x.p, 8, MOE_F32, d_out.p, st) == MOE_ERR_HANDLE_MISMATCH, "foreign handle accepted");
+  HIP_OK(hipStreamSynchronize(st));
+}
+
+int main() {
+  std::printf("c_abi_check: library ABI version %d (header %d)\n", moe_abi_version(), MOE_ABI_VERSION);
+  if (moe_abi_version() != MOE_ABI_VERSION) {
+    std::fprintf(stderr, "library and header ABI versions differ\n");
+    return 1;
+  }
+  hipStream_t st;
+  HIP_OK(hipStreamCreate(&st));
+  run_case(300, 16, 4, 40, 0, 1, st);      // dropless, ragged against every tile size
+  run_case(300, 16, 4, 40, 60, 2, st);     // capacity drop
+  run_case(1000, 64, 8, 64, 0, 3, st);
+  run_case(97, 8, 2, 8, 5, 4, st);         // heavy drop, 32-byte rows
+  run_case(513, 128, 16, 1028, 0, 5, st);  // rows of more than one 1 KiB group
+  run_case(0, 8, 2, 16, 4, 6, st);         // empty batch: the buffer is all padding
+  check_errors(st);
+  HIP_OK(hipStreamDestroy(st));
+  if (g_failures != 0) {
+    std::fprintf(stderr, "c_abi_check: %d failed checks\n", g_failures);
+    return 1;
+  }
+  std::printf("c_abi_check: ok\n");
+  return 0;
+}

@@ -495,7 +495,7 @@ def test_expert_gemm_dgrad_full_workload_sampled():
 # seeded random configurations: forward and both gradients
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_gemm_random_configurations(seed):
     """Sizes, routing mode and dtype drawn from one seeded generator; the forward (with
     route weights half the time), the input-row gradient and the weight gradient (float32

@@ -490,7 +490,7 @@ def random_config(seed: int):
     return rng, s, e, k, dtype, m, cap, route_major, pad, skew
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(64))
 def test_random_configurations_bit_exact(seed):
     rng, s, e, k, dtype, m, cap, rm, pad, skew = random_config(seed)
     announce("random config", seed, s, e, k, dtype, m, cap, rm, pad, skew)

@@ -141,3 +141,50 @@ def test_autograd_weights_before_experts_and_renormalized():
     gl = to_host(logits.grad)
     assert np.all(gl[gl_o == 0] == 0)
     assert np.abs(gl - gl_o).max() <= 1e-5 * max(1e-30, np.abs(gl_o).max())
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_variant_random_configurations(seed):
+    """Seeded random sizes, routing modes and dtypes (the row path's random configurations,
+    other seeds) through the variants: weighted dispatch and its backward, the unweighted
+    combine, renormalisation over kept routes and its backward, and the replay with its
+    routing check, each to the bars above."""
+    from tests.test_gpu_parity import random_config
+
+    rng, s, e, k, dtype, m, cap, rm, pad, skew = random_config(1000 + seed)
+    announce("variant random config", seed, s, e, k, dtype, m, cap, rm, pad, skew)
+    idx = W.skewed_idx(rng, s, e, k) if skew else W.random_idx(rng, s, e, k)
+    x = W.cast_input(rng.standard_normal((s, m)).astype(np.float32), dtype)
+    w = W.random_weights(rng, s, k)
+    Lo = oracle.dispatch_layout(idx, e, cap, route_major=rm, pad_multiple=pad)
+    G = W.cast_input(rng.standard_normal((Lo.rows, m)).astype(np.float32), dtype)
+    g = rng.standard_normal((s, k)).astype(np.float32)
+    Lg = M.moe_dispatch_layout(to_dev(idx), e, cap, route_major=rm, pad_multiple=pad)
+
+    out = M.moe_dispatch_weighted(Lg, to_dev(x, dtype), to_dev(w))
+    assert_bits_equal(to_host(out), oracle.dispatch_weighted(Lo, x, w, dtype), "weighted dispatch")
+    y = M.moe_combine(Lg, to_dev(G, dtype), None)
+    assert_bits_equal(to_host(y), oracle.dispatch_backward(Lo, G, dtype), "unweighted combine")
+    gx, gw = M.moe_dispatch_weighted_backward(Lg, to_dev(G, dtype), to_dev(x, dtype), to_dev(w))
+    gx_o, gw_o = oracle.dispatch_weighted_backward(Lo, G, x, w, dtype)
+    assert_bits_equal(to_host(gx), gx_o, "weighted dispatch backward: grad_x")
+    bound = weight_grad_bound(oracle.to_f32(x, dtype), oracle.to_f32(G, dtype), Lo.dst)
+    err = np.abs(to_host(gw).astype(np.float64) - gw_o)
+    assert np.all(err <= 1e-6 * bound), f"grad_w err {err.max()}"
+
+    wr = M.moe_renormalize_kept(Lg, to_dev(w))
+    assert_bits_equal(to_host(wr), oracle.renormalize_kept(Lo, w), "renormalized weights")
+    gwr = M.moe_renormalize_kept_backward(Lg, to_dev(w), to_dev(g))
+    assert_bits_equal(to_host(gwr), oracle.renormalize_kept_backward(Lo, w, g), "renormalize backward")
+
+    xd = to_dev(x, dtype)
+    buf = M.moe_dispatch(Lg, xd)
+    rep = M.moe_dispatch_replay(Lg, xd, to_dev(idx))
+    assert_bits_equal(to_host(rep), to_host(buf), "replay")
+    assert M.moe_layout_read(Lg)[0] == Lo.flags, "flags after a faithful replay"
+    if s > 0 and k < e:  # one route of the last token moved to an expert it did not pick
+        idx2 = idx.copy()
+        idx2[-1, 0] = next(q for q in range(e) if q not in set(idx[-1].tolist()))
+        rep2 = M.moe_dispatch_replay(Lg, xd, to_dev(idx2))
+        assert M.moe_layout_read(Lg)[0] & M.FLAG_REPLAY_MISMATCH, "changed routing not flagged"
+        assert_bits_equal(to_host(rep2), to_host(buf), "flagged replay still follows the layout")

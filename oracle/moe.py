@@ -40,8 +40,9 @@ force on tiny inputs, the dense one-hot einsum the index path replaced, closed
 forms, finite differences and adjoint identities; the grouped expert GEMM and its
 two gradients by loops, scaled identities, the forward/backward adjoint identities
 and exact integer derivatives, the weight gradient kept in the element type by
-ties-to-even sums). The routing checksum is our own definition and is pinned only
-by a hand-worked fixture.
+ties-to-even sums). Parity unpinned: the routing checksum's definition. The pages
+print no definition for it, so it is our own, pinned to that definition only by a
+hand-worked fixture.
 """
 from __future__ import annotations
 

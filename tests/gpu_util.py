@@ -68,3 +68,21 @@ def weight_grad_bound(gy32: np.ndarray, E32: np.ndarray, dst: np.ndarray) -> np.
         sel = dst[:, j] >= 0
         out[sel, j] = np.abs(gy32[sel].astype(np.float64) * E32[dst[sel, j]].astype(np.float64)).sum(1)
     return out
+
+
+def tagged_rows(x: np.ndarray, src: np.ndarray, expert_of_row: np.ndarray, dt: str) -> np.ndarray:
+    """Expert rows E[r] = 2^q * x[src[r]], q = expert(r) mod Q (zero rows where src < 0).
+
+    With the identity expert every route of a token reads an equal row, so reading one
+    route's row in place of another's goes unseen; scaling by a power of two per expert
+    makes the rows differ while staying exact (Q = 8 for f16, whose range is narrow;
+    32 otherwise)."""
+    Q = 8 if dt == "f16" else 32
+    used = src >= 0
+    scale = np.where(used, np.ldexp(1.0, (expert_of_row % Q).astype(np.int64)), 0.0).astype(np.float32)
+    if dt == "bf16":
+        f = (x[np.maximum(src, 0)].astype(np.uint32) << np.uint32(16)).view(np.float32) * scale[:, None]
+        tagged = (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    else:
+        tagged = x[np.maximum(src, 0)] * scale[:, None].astype(x.dtype)
+    return np.where(used[:, None], tagged, np.zeros((), x.dtype)).astype(x.dtype)  # +0.0 rows

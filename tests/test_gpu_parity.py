@@ -16,8 +16,8 @@ import torch
 import combine_moe_gate_amd as M
 import oracle
 import workloads as W
-from tests.gpu_util import (assert_bits_equal, f32_ulps, sample_tokens, sub_layout, to_dev,
-                            to_host, weight_grad_bound)
+from tests.gpu_util import (assert_bits_equal, f32_ulps, sample_tokens, sub_layout, tagged_rows,
+                            to_dev, to_host, weight_grad_bound)
 
 pytestmark = pytest.mark.gpu
 
@@ -302,6 +302,40 @@ def test_workload_path_matches_oracle(name):
     dotmag = np.abs(w64 * g64).sum(1, keepdims=True)
     np.put_along_axis(scale, idx_o[toks].astype(np.int64), np.abs(w64) * (np.abs(g64) + dotmag), axis=1)
     assert np.all(np.abs(gl_g.astype(np.float64) - gl_o) <= 8 * 2.0 ** -24 * scale + 1e-38)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_tagged_expert_rows_at_full_size(name):
+    """Combine and its backward at full size, in the bench's launch configuration, over
+    expert rows tagged by a power of two per expert, against the oracle on sampled
+    tokens: bit-exact combine and grad_E, grad_w within its bound."""
+    announce("tagged expert", name)
+    inp = W.make_inputs(name)
+    w = inp.workload
+    dt = w.dtype
+    idx_o, wt_o = oracle.gate_topk(inp.logits, w.k)
+    Lo = oracle.dispatch_layout(idx_o, w.e, w.capacity)
+    toks = np.arange(w.s) if name in SMALL else sample_tokens(w.s, 512)
+    S = sub_layout(Lo, toks)
+    # expert of every buffer row, from the segments
+    expert_of_row = np.repeat(np.arange(w.e), np.diff(Lo.offsets))
+    expert_of_row = np.concatenate([expert_of_row, np.zeros(Lo.rows - len(expert_of_row), np.int64)])
+    src = np.full(Lo.rows, -1, dtype=np.int64)
+    rows = S.dst[S.dst >= 0]
+    src[rows] = Lo.src[rows]
+    E = tagged_rows(inp.x, src, expert_of_row, dt)
+    assert E.shape == (Lo.rows, w.m)
+
+    Lg = M.moe_dispatch_layout(to_dev(idx_o), w.e, w.capacity)
+    E_dev, wt_dev, gy_dev = to_dev(E, dt), to_dev(wt_o), to_dev(inp.grad_y, dt)
+    y = to_host(M.moe_combine(Lg, E_dev, wt_dev))[toks]
+    assert_bits_equal(y, oracle.combine(S, E, wt_o[toks], dt), "combine over tagged rows")
+    gE, gw = M.moe_combine_backward(Lg, gy_dev, E_dev, wt_dev)
+    gE_o, gw_o = oracle.combine_backward(S, inp.grad_y[toks], E, wt_o[toks], dt)
+    assert_bits_equal(to_host(gE[torch.from_numpy(rows).cuda()]), gE_o[rows], "grad_E")
+    bound = weight_grad_bound(oracle.to_f32(inp.grad_y[toks], dt), oracle.to_f32(E, dt), S.dst)
+    err = np.abs(to_host(gw)[toks].astype(np.float64) - gw_o)
+    assert np.all(err <= 1e-6 * bound), f"grad_w err {err.max()}"
 
 
 def dtype_ulp(mag: np.ndarray, dt: str) -> np.ndarray:

@@ -267,3 +267,28 @@ def test_planted_mistake_is_caught(name, monkeypatch):
 def test_unmutated_oracle_passes_every_pin():
     for pin in PINS:
         pin()
+
+
+def test_tagged_rows_expose_a_route_swap_that_identity_rows_hide():
+    """The full-size GPU tests feed combine expert rows tagged by a power of two per
+    expert: with the identity expert (every route of a token reads an equal row) a kernel
+    that read one route's row in place of another's would pass; with tagged rows it
+    cannot. Planted on the oracle: two routes of one token swapped."""
+    import dataclasses
+
+    import workloads as W
+    from tests.gpu_util import tagged_rows
+
+    rng = np.random.default_rng(5)
+    s, m, e, k = 40, 16, 8, 4
+    idx = W.random_idx(rng, s, e, k)
+    x = W.cast_input(rng.standard_normal((s, m)).astype(np.float32), "bf16")
+    w = W.random_weights(rng, s, k)
+    L = oracle.dispatch_layout(idx, e, 0)
+    swapped = dataclasses.replace(L, dst=L.dst.copy())
+    swapped.dst[7, [0, 1]] = swapped.dst[7, [1, 0]]
+    ident = oracle.dispatch(L, x)
+    assert np.array_equal(oracle.combine(L, ident, w, "bf16"), oracle.combine(swapped, ident, w, "bf16"))
+    expert_of_row = np.repeat(np.arange(e), np.diff(L.offsets))
+    tagged = tagged_rows(x, L.src.astype(np.int64), expert_of_row, "bf16")
+    assert not np.array_equal(oracle.combine(L, tagged, w, "bf16"), oracle.combine(swapped, tagged, w, "bf16"))

@@ -549,3 +549,65 @@ def test_random_configurations_bit_exact(seed):
     assert np.all(err <= 1e-6 * bound), f"grad_w err {err.max()}"
     gx = M.moe_dispatch_backward(Lg, gE)
     assert_bits_equal(to_host(gx), oracle.dispatch_backward(Lo, gE_o, dtype), "dispatch backward")
+
+
+# ----------------------------------------------------------------------------
+# many tiny seeded cases end to end, gate included
+
+
+@pytest.mark.parametrize("seed", range(200))
+def test_tiny_random_end_to_end(seed):
+    """Tiny sizes (s <= 64, e <= 16) with logits on a coarse grid, so that ties between
+    experts are common, through gate, layout, dispatch, combine, replay and every backward
+    pass. Ids, maps, buffers, combine, grad_E and grad_x bit-exact (the rows steps fed the
+    oracle's weights); weights and the gate gradient within one float32 ulp; grad_w within
+    its bound."""
+    rng = np.random.default_rng(20000 + seed)
+    s = int(rng.integers(1, 65))
+    e = int(rng.integers(1, 17))
+    k = int(rng.integers(1, e + 1))
+    dt = ["f32", "bf16", "f16"][int(rng.integers(0, 3))]
+    m = int(rng.integers(1, 9)) * (4 if dt == "f32" else 8)
+    cap = 0 if rng.random() < 0.4 else int(rng.integers(1, max(2, s * k // e + 2)))
+    announce("tiny", seed, s, e, k, dt, m, cap)
+    logits = (rng.integers(-3, 4, size=(s, e)) / 2).astype(np.float32)
+    x = W.cast_input(rng.standard_normal((s, m)).astype(np.float32), dt)
+    gy = W.cast_input(rng.standard_normal((s, m)).astype(np.float32), dt)
+
+    idx, wt = M.moe_gate_topk(to_dev(logits), k)
+    idx_o, wt_o = oracle.gate_topk(logits, k)
+    assert_bits_equal(to_host(idx), idx_o, "idx")
+    assert f32_ulps(to_host(wt), wt_o).max() <= 1, "weights"
+
+    Lg = M.moe_dispatch_layout(idx, e, cap)
+    Lo = oracle.dispatch_layout(idx_o, e, cap)
+    check_layout(Lg, Lo, f"tiny seed {seed}")
+    xd = to_dev(x, dt)
+    buf = M.moe_dispatch(Lg, xd)
+    E_o = oracle.dispatch(Lo, x)
+    assert_bits_equal(to_host(buf), E_o, "dispatch")
+    assert_bits_equal(to_host(M.moe_dispatch_replay(Lg, xd, idx)), E_o, "replay")
+    w_dev = to_dev(wt_o)
+    assert_bits_equal(to_host(M.moe_combine(Lg, buf, w_dev)), oracle.combine(Lo, E_o, wt_o, dt), "combine")
+    gE, gw = M.moe_combine_backward(Lg, to_dev(gy, dt), buf, w_dev)
+    gE_o, gw_o = oracle.combine_backward(Lo, gy, E_o, wt_o, dt)
+    assert_bits_equal(to_host(gE), gE_o, "grad_E")
+    bound = weight_grad_bound(oracle.to_f32(gy, dt), oracle.to_f32(E_o, dt), Lo.dst)
+    assert np.all(np.abs(to_host(gw).astype(np.float64) - gw_o) <= 1e-6 * bound), "grad_w"
+    assert_bits_equal(to_host(M.moe_dispatch_backward(Lg, gE)), oracle.dispatch_backward(Lo, gE_o, dt), "grad_x")
+    g32 = gw_o.astype(np.float32)
+    gl = to_host(M.moe_gate_topk_backward(idx, w_dev, to_dev(g32), e))
+    gl_o = oracle.gate_topk_backward(idx_o, wt_o, g32, e)
+    assert np.all(gl[gl_o == 0] == 0)
+    # w_j (g_j - sum_q w_q g_q) in float64 on both sides, summed in different orders:
+    # apart from each side's rounding to float32 (one ulp together) they differ by at most
+    # about k * 2^-53 of |w_j| (|g_j| + sum_q |w_q g_q|), which matters where g_j cancels
+    # the sum (e.g. every kept route of a token with the same gradient)
+    w64, g64 = wt_o.astype(np.float64), g32.astype(np.float64)
+    scale = np.zeros((s, e))
+    np.put_along_axis(scale, idx_o.astype(np.int64),
+                      np.abs(w64) * (np.abs(g64) + np.abs(w64 * g64).sum(1, keepdims=True)), axis=1)
+    big = np.maximum(np.abs(gl.astype(np.float64)), np.abs(gl_o))
+    ulp = np.ldexp(1.0, np.frexp(np.maximum(big, 2.0 ** -126))[1] - 24)
+    assert np.all(np.abs(gl.astype(np.float64) - gl_o) <= ulp + 2.0 ** -45 * scale), "gate gradient"
+    assert M.moe_layout_read(Lg)[0] == 0

@@ -14,6 +14,7 @@
 //             output, grad_w[t,j] is exactly sum_m x[t,m]^2 (integers); the gate gradient
 //             is zero off the selection and sums to zero over it (softmax Jacobian);
 //   replay    byte-identical to the dispatch; a changed route sets the mismatch flag;
+//   options, variants and the grouped expert GEMM: see run_variants_case;
 //   errors    bad arguments return their status and a message, enqueueing nothing.
 // Prints "c_abi_check: ok" and exits 0, or lists the failures and exits 1.
 #include <hip/hip_runtime_api.h>
@@ -287,6 +288,248 @@ static void run_case(int s, int e, int k, int m, int cap, uint64_t seed, hipStre
   }
 }
 
+static uint16_t bf16_of(float v) {  // exact for the small integers used here
+  uint32_t u;
+  std::memcpy(&u, &v, sizeof(u));
+  return static_cast<uint16_t>(u >> 16);
+}
+
+static float float_of_bf16(uint16_t h) {
+  const uint32_t u = static_cast<uint32_t>(h) << 16;
+  float v;
+  std::memcpy(&v, &u, sizeof(v));
+  return v;
+}
+
+static std::vector<int32_t> read_i32(const int32_t* p, size_t n) {
+  std::vector<int32_t> h(n);
+  if (n) HIP_OK(hipMemcpy(h.data(), p, n * sizeof(int32_t), hipMemcpyDeviceToHost));
+  return h;
+}
+
+// The layout options, the variants and the grouped expert GEMM through the ABI:
+//   pad_multiple  segments rounded up to the multiple, pad rows never referenced;
+//   route_major   with a capacity, a route's slot counts the earlier routes of lower rank
+//                 j' < j (any token) and of the same rank from earlier tokens;
+//   weighted dispatch out[dst] = w * x (one float32 product), its unweighted combine and
+//                 its backward, with power-of-two weights over integer rows (exact sums);
+//   renormalisation the kept weights of a token sum to one, and the backward of a
+//                 gradient along the weights themselves is zero;
+//   expert GEMM   forward (gathered and on the dispatched buffer, with and without route
+//                 weights), input-row and weight gradients: small-integer bf16 operands,
+//                 so every sum is an exact integer.
+static void run_variants_case(hipStream_t st) {
+  const int s = 200, e = 12, k = 3, m = 64, n = 32, cap = 40;
+  std::printf("case variants and expert GEMM s=%d e=%d k=%d m=%d n=%d\n", s, e, k, m, n);
+  std::fflush(stdout);
+  Rng rng{77};
+  std::vector<int32_t> idx(static_cast<size_t>(s) * k);
+  for (int t = 0; t < s; ++t) {  // k distinct experts per token
+    for (int j = 0; j < k; ++j) {
+      int x;
+      bool again;
+      do {
+        x = rng.below(e);
+        again = false;
+        for (int q = 0; q < j; ++q) again |= idx[static_cast<size_t>(t) * k + q] == x;
+      } while (again);
+      idx[static_cast<size_t>(t) * k + j] = x;
+    }
+  }
+  const float wchoice[4] = {0.25f, 0.5f, 1.0f, 2.0f};
+  std::vector<float> w(static_cast<size_t>(s) * k), x(static_cast<size_t>(s) * m);
+  for (auto& v : w) v = wchoice[rng.below(4)];
+  for (auto& v : x) v = static_cast<float>(rng.below(3) - 1);  // -1, 0, 1
+  Dev<int32_t> d_idx(idx.size());
+  Dev<float> d_w(w.size()), d_x(x.size());
+  d_idx.put(idx);
+  d_w.put(w);
+  d_x.put(x);
+
+  // pad_multiple = 8, dropless
+  {
+    moe_layout_options_t o{0, 8};
+    const size_t wsb = moe_layout_workspace_bytes_ex(s, e, k, 0, &o);
+    Dev<unsigned char> ws(wsb);
+    moe_layout_t L;
+    MOE_OK_(moe_dispatch_layout_ex(d_idx.p, s, e, k, 0, &o, ws.p, wsb, &L, st));
+    HIP_OK(hipStreamSynchronize(st));
+    CHECK(L.rows == static_cast<int64_t>(s) * k + e * 7, "padded rows %lld", static_cast<long long>(L.rows));
+    const auto offsets = read_i32(L.offsets, e + 1);
+    const auto dst = read_i32(L.dst, idx.size());
+    const auto src = read_i32(L.src, static_cast<size_t>(L.rows));
+    std::vector<int> seen(e, 0);
+    for (int t = 0; t < s; ++t)
+      for (int j = 0; j < k; ++j) {
+        const int xe = idx[static_cast<size_t>(t) * k + j];
+        const int d = dst[static_cast<size_t>(t) * k + j];
+        CHECK(d == offsets[xe] + seen[xe], "padded dst t=%d j=%d", t, j);
+        if (d >= 0 && d < L.rows) CHECK(src[d] == t, "padded src");
+        ++seen[xe];
+      }
+    int32_t off = 0;
+    for (int xe = 0; xe < e; ++xe) {
+      CHECK(offsets[xe] == off && off % 8 == 0, "padded offsets[%d]", xe);
+      for (int32_t r = off + seen[xe]; r < off + (seen[xe] + 7) / 8 * 8; ++r) CHECK(src[r] == -1, "pad row %d", r);
+      off += (seen[xe] + 7) / 8 * 8;
+    }
+  }
+
+  // route-major slots with a capacity
+  {
+    moe_layout_options_t o{1, 1};
+    const size_t wsb = moe_layout_workspace_bytes_ex(s, e, k, cap, &o);
+    Dev<unsigned char> ws(wsb);
+    moe_layout_t L;
+    MOE_OK_(moe_dispatch_layout_ex(d_idx.p, s, e, k, cap, &o, ws.p, wsb, &L, st));
+    HIP_OK(hipStreamSynchronize(st));
+    const auto dst = read_i32(L.dst, idx.size());
+    std::vector<int> seen(e, 0);
+    for (int j = 0; j < k; ++j)
+      for (int t = 0; t < s; ++t) {
+        const int xe = idx[static_cast<size_t>(t) * k + j];
+        const int slot = seen[xe]++;
+        const int want = slot < cap ? xe * cap + slot : -1;
+        CHECK(dst[static_cast<size_t>(t) * k + j] == want, "route-major dst t=%d j=%d: %d, want %d", t, j,
+              dst[static_cast<size_t>(t) * k + j], want);
+      }
+  }
+
+  // capacity layout for the weighted dispatch, renormalisation and the GEMMs
+  const size_t wsb = moe_layout_workspace_bytes(s, e, k, cap);
+  Dev<unsigned char> ws(wsb);
+  moe_layout_t L;
+  MOE_OK_(moe_dispatch_layout(d_idx.p, s, e, k, cap, ws.p, wsb, &L, st));
+  HIP_OK(hipStreamSynchronize(st));
+  const int64_t rows = L.rows;
+  const auto dst = read_i32(L.dst, idx.size());
+  const auto src = read_i32(L.src, static_cast<size_t>(rows));
+
+  Dev<float> d_out(static_cast<size_t>(rows) * m), d_y(x.size()), d_gx(x.size()), d_gw(w.size());
+  MOE_OK_(moe_dispatch_weighted(&L, d_x.p, d_w.p, m, MOE_F32, d_out.p, st));
+  MOE_OK_(moe_combine(&L, d_out.p, nullptr, m, MOE_F32, d_y.p, st));
+  MOE_OK_(moe_dispatch_weighted_backward(&L, d_out.p, d_x.p, d_w.p, m, MOE_F32, d_gx.p, d_gw.p, st));
+  HIP_OK(hipStreamSynchronize(st));
+  const auto out = d_out.get();
+  const auto y = d_y.get();
+  const auto gx = d_gx.get();
+  const auto gw = d_gw.get();
+  for (int t = 0; t < s; ++t) {
+    float sw = 0.0f, sw2 = 0.0f, sq = 0.0f;
+    for (int i = 0; i < m; ++i) sq += x[static_cast<size_t>(t) * m + i] * x[static_cast<size_t>(t) * m + i];
+    for (int j = 0; j < k; ++j) {
+      const size_t o = static_cast<size_t>(t) * k + j;
+      if (dst[o] < 0) {
+        CHECK(gw[o] == 0.0f, "weighted dispatch grad_w of a dropped route");
+        continue;
+      }
+      sw += w[o];
+      sw2 += w[o] * w[o];
+      for (int i = 0; i < m; ++i)
+        CHECK(same_bits(out[static_cast<size_t>(dst[o]) * m + i], w[o] * x[static_cast<size_t>(t) * m + i]),
+              "weighted dispatch row %d", dst[o]);
+      CHECK(gw[o] == w[o] * sq, "weighted dispatch grad_w t=%d j=%d", t, j);
+    }
+    for (int i = 0; i < m; ++i) {
+      const float xv = x[static_cast<size_t>(t) * m + i];
+      CHECK(y[static_cast<size_t>(t) * m + i] == sw * xv, "unweighted combine t=%d", t);
+      CHECK(gx[static_cast<size_t>(t) * m + i] == sw2 * xv, "weighted dispatch grad_x t=%d", t);
+    }
+  }
+  for (int64_t r = 0; r < rows; ++r)
+    if (src[r] < 0)
+      for (int i = 0; i < m; ++i) CHECK(out[static_cast<size_t>(r) * m + i] == 0.0f, "unfilled weighted row");
+
+  // renormalisation over kept routes
+  Dev<float> d_wr(w.size()), d_g(w.size()), d_gr(w.size());
+  std::vector<float> g(w.size());
+  for (size_t o = 0; o < g.size(); ++o) g[o] = w[o];  // a gradient along the weights
+  d_g.put(g);
+  MOE_OK_(moe_renormalize_kept(&L, d_w.p, d_wr.p, st));
+  MOE_OK_(moe_renormalize_kept_backward(&L, d_w.p, d_g.p, d_gr.p, st));
+  HIP_OK(hipStreamSynchronize(st));
+  const auto wr = d_wr.get();
+  const auto gr = d_gr.get();
+  for (int t = 0; t < s; ++t) {
+    double sum = 0.0, dotw = 0.0, mag = 0.0;
+    int kept = 0;
+    for (int j = 0; j < k; ++j) {
+      const size_t o = static_cast<size_t>(t) * k + j;
+      if (dst[o] < 0) {
+        CHECK(wr[o] == 0.0f && gr[o] == 0.0f, "renormalised dropped route t=%d", t);
+        continue;
+      }
+      ++kept;
+      sum += wr[o];
+      dotw += static_cast<double>(w[o]) * gr[o];
+      mag += std::fabs(static_cast<double>(w[o]) * gr[o]) + std::fabs(static_cast<double>(g[o]));
+    }
+    if (kept) {
+      CHECK(std::fabs(sum - 1.0) <= 1e-6, "renormalised weights of t=%d sum to %.9f", t, sum);
+      CHECK(std::fabs(dotw) <= 1e-6 * mag + 1e-30, "renormalisation backward along w: %g", dotw);
+    }
+  }
+
+  // grouped expert GEMM, bf16 small-integer operands
+  std::vector<uint16_t> xb(x.size()), wb(static_cast<size_t>(e) * n * m), gb(static_cast<size_t>(rows) * n);
+  for (size_t i = 0; i < x.size(); ++i) xb[i] = bf16_of(x[i]);
+  for (auto& v : wb) v = bf16_of(static_cast<float>(rng.below(3) - 1));
+  for (auto& v : gb) v = bf16_of(static_cast<float>(rng.below(3) - 1));
+  Dev<uint16_t> d_xb(xb.size()), d_wb(wb.size()), d_gb(gb.size()), d_buf(static_cast<size_t>(rows) * m),
+      d_h(static_cast<size_t>(rows) * n), d_h2(static_cast<size_t>(rows) * n), d_hs(static_cast<size_t>(rows) * n),
+      d_ga(static_cast<size_t>(rows) * m), d_gwn(wb.size());
+  Dev<float> d_gwf(wb.size());
+  d_xb.put(xb);
+  d_wb.put(wb);
+  d_gb.put(gb);
+  MOE_OK_(moe_dispatch(&L, d_xb.p, m, MOE_BF16, d_buf.p, st));
+  MOE_OK_(moe_expert_gemm(&L, d_xb.p, 1, d_wb.p, m, n, MOE_BF16, nullptr, d_h.p, st));
+  MOE_OK_(moe_expert_gemm(&L, d_buf.p, 0, d_wb.p, m, n, MOE_BF16, nullptr, d_h2.p, st));
+  MOE_OK_(moe_expert_gemm(&L, d_xb.p, 1, d_wb.p, m, n, MOE_BF16, d_w.p, d_hs.p, st));
+  MOE_OK_(moe_expert_gemm_dgrad(&L, d_gb.p, d_wb.p, m, n, MOE_BF16, d_ga.p, st));
+  MOE_OK_(moe_expert_gemm_wgrad(&L, d_xb.p, 1, d_gb.p, m, n, MOE_BF16, MOE_F32, d_gwf.p, st));
+  MOE_OK_(moe_expert_gemm_wgrad(&L, d_xb.p, 1, d_gb.p, m, n, MOE_BF16, MOE_BF16, d_gwn.p, st));
+  HIP_OK(hipStreamSynchronize(st));
+  const auto h = d_h.get(), h2 = d_h2.get(), hs = d_hs.get(), ga = d_ga.get(), gwn = d_gwn.get();
+  const auto gwf = d_gwf.get();
+  CHECK(h == h2, "gathered and buffered expert GEMM differ");
+  std::vector<float> rw(static_cast<size_t>(rows), 0.0f);  // the route weight placed at each row
+  for (size_t o = 0; o < dst.size(); ++o)
+    if (dst[o] >= 0) rw[dst[o]] = w[o];
+  std::vector<double> gwx(wb.size(), 0.0);
+  for (int64_t r = 0; r < rows; ++r) {
+    const int xe = static_cast<int>(r / cap);
+    const bool filled = src[r] >= 0;
+    for (int c = 0; c < n; ++c) {
+      double acc = 0.0;
+      if (filled)
+        for (int i = 0; i < m; ++i)
+          acc += static_cast<double>(x[static_cast<size_t>(src[r]) * m + i]) *
+                 float_of_bf16(wb[(static_cast<size_t>(xe) * n + c) * m + i]);
+      const size_t o = static_cast<size_t>(r) * n + c;
+      CHECK(float_of_bf16(h[o]) == acc, "expert GEMM row %lld col %d", static_cast<long long>(r), c);
+      CHECK(float_of_bf16(hs[o]) == rw[r] * acc, "scaled expert GEMM row %lld col %d", static_cast<long long>(r), c);
+    }
+    for (int i = 0; i < m; ++i) {
+      double acc = 0.0;
+      if (filled)
+        for (int c = 0; c < n; ++c)
+          acc += static_cast<double>(float_of_bf16(gb[static_cast<size_t>(r) * n + c])) *
+                 float_of_bf16(wb[(static_cast<size_t>(xe) * n + c) * m + i]);
+      CHECK(float_of_bf16(ga[static_cast<size_t>(r) * m + i]) == acc, "input-row gradient row %lld", static_cast<long long>(r));
+    }
+    if (filled)
+      for (int c = 0; c < n; ++c)
+        for (int i = 0; i < m; ++i)
+          gwx[(static_cast<size_t>(xe) * n + c) * m + i] +=
+              static_cast<double>(float_of_bf16(gb[static_cast<size_t>(r) * n + c])) * x[static_cast<size_t>(src[r]) * m + i];
+  }
+  for (size_t i = 0; i < gwx.size(); ++i) {
+    CHECK(gwf[i] == gwx[i], "weight gradient (float32) element %zu", i);
+    CHECK(float_of_bf16(gwn[i]) == gwx[i], "weight gradient (bf16) element %zu", i);
+  }
+}
+
 static void check_errors(hipStream_t st) {
   std::printf("case argument errors\n");
   std::fflush(stdout);
@@ -327,6 +570,7 @@ int main() {
   run_case(97, 8, 2, 8, 5, 4, st);         // heavy drop, 32-byte rows
   run_case(513, 128, 16, 1028, 0, 5, st);  // rows of more than one 1 KiB group
   run_case(0, 8, 2, 16, 4, 6, st);         // empty batch: the buffer is all padding
+  run_variants_case(st);
   check_errors(st);
   HIP_OK(hipStreamDestroy(st));
   if (g_failures != 0) {

@@ -1,7 +1,9 @@
 """The library driven from C++ through its C ABI alone (tests/c_abi_check.cpp): hipMalloc'd
-buffers, one HIP stream, no Python or PyTorch in the process. The program checks gate,
-layout, dispatch, replay, combine and the backward passes against properties and closed
-forms (see its header), plus the host-side argument checks, and exits 0 when all hold.
+buffers, one HIP stream, no Python or PyTorch in the process. The program calls every
+entry point (gate, layout and its options, dispatch, replay, combine, the backward passes,
+the variants, the grouped expert GEMM and its gradients), checks the results against
+properties and closed forms (see its header), plus the host-side argument checks, and exits
+0 when all hold.
 It is compiled with the library by the package build."""
 import os
 import subprocess

@@ -13,7 +13,8 @@
 //                mask2, ... of the same review comment, later columns offset by the
 //                counts of earlier ones), so first choices win capacity.
 //
-// No sorting and no order-dependent atomics; two launches over tiles of 256 items:
+// No sorting and no order-dependent atomics; two launches over tiles of 256 items (one
+// when all items fit one tile: the place kernel then counts that tile itself):
 //
 //   count  one workgroup per tile: LDS histogram of the tile's valid routes (integer
 //          atomic adds; the totals do not depend on their order), the tile's share of
@@ -188,26 +189,45 @@ __global__ __launch_bounds__(kTileTokens) void layout_place_kernel(
   const int lane = lane_id(), wv = threadIdx.x >> 6;
   const int tile = blockIdx.x;
   const int my_tile = tile < ntiles ? tile : ntiles;  // workgroups past the tiles: padding only
+  // A single tile has no count launch before it: every workgroup builds that tile's
+  // histogram from the routes itself (workgroup 0 also its checksum and flags).
+  const bool single = ntiles == 1;
 
   // this thread's routes, loaded first so that their latency overlaps the table reads
-  const int item = tile * kTileTokens + threadIdx.x;
+  const int item = (single ? 0 : tile) * kTileTokens + threadIdx.x;
   const int nr = RM ? 1 : k;
   int tok = 0, ids[KMAX];
   bool ok[KMAX];
   int64_t pos[KMAX];
+  int item_flags = 0;
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     ids[j] = -1;
     ok[j] = false;
     pos[j] = 0;
   }
-  if (tile < ntiles && item < items) load_item<KMAX, RM>(idx, item, s, k, e, tok, ids, ok, pos);
+  if ((tile < ntiles || single) && item < items)
+    item_flags = load_item<KMAX, RM>(idx, item, s, k, e, tok, ids, ok, pos);
 
   // per expert: sum over earlier tiles and over all tiles. Row x of the expert-major
   // tile table is read with 16-byte loads; with e <= 128 several threads share a row
   // (P parts of consecutive tiles) and their partial sums meet in LDS.
   __shared__ int32_t part_before[kTileTokens], part_all[kTileTokens];
-  {
+  if (single) {
+    // no earlier tile; the counts are the histogram of this tile's valid routes (LDS
+    // integer adds, whose totals do not depend on their order)
+    for (int x = threadIdx.x; x < e; x += kTileTokens) {
+      base_s[x] = 0;
+      total_s[x] = 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (ok[j]) atomicAdd(&total_s[ids[j]], 1);
+    __syncthreads();
+    for (int x = threadIdx.x; x < e; x += kTileTokens)
+      off_s[x] = capacity > 0 ? capacity : (total_s[x] + pad - 1) / pad * pad;  // segment sizes
+  } else {
     const int P = e <= kTileTokens / 2 ? kTileTokens / e : 1;  // threads per expert
     const int nq = ntp / 4;                                      // int4 groups per row
     const int qlen = (nq + P - 1) / P;
@@ -265,9 +285,18 @@ __global__ __launch_bounds__(kTileTokens) void layout_place_kernel(
     if (threadIdx.x == 0) offsets_out[e] = off_s[e];
     uint64_t cks = 0;
     int f = 0;
-    for (int b = threadIdx.x; b < ntiles; b += kTileTokens) {
-      cks += tile_checksum[b];
-      f |= tile_flags[b];
+    if (single) {  // this workgroup's own routes are the only tile's
+      if (item < items) {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+          if (j < nr) cks += static_cast<uint64_t>(static_cast<int64_t>(ids[j]) + 1) * static_cast<uint64_t>(pos[j] + 1);
+      }
+      f = item_flags;
+    } else {
+      for (int b = threadIdx.x; b < ntiles; b += kTileTokens) {
+        cks += tile_checksum[b];
+        f |= tile_flags[b];
+      }
     }
     cks = wave_sum(cks);
     f = wave_or(f);
@@ -342,7 +371,7 @@ template <int KMAX, bool RM>
 static hipError_t launch_layout_k(const int32_t* idx, const LayoutView& L, hipStream_t stream) {
   const int ntiles = L.ntiles;
   const int items = RM ? L.s * L.k : L.s;
-  if (ntiles > 0) {
+  if (ntiles > 1) {  // one tile: the place kernel counts it itself
     layout_count_kernel<KMAX, RM><<<ntiles, kTileTokens, L.e * sizeof(int32_t), stream>>>(
         idx, L.s, L.e, L.k, items, tile_row_length(ntiles), L.tile_counts, L.tile_checksum,
         L.tile_flags);

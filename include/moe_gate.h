@@ -198,7 +198,8 @@ moe_status_t moe_gate_topk_backward(const int32_t* topk_idx, const float* topk_w
  * The slot of route (t, j) is the number of tokens t' < t whose routes name the same
  * expert (column cumsum of the token x expert mask, minus one). Routes naming an expert
  * outside [0, e), or an expert an earlier route of the same token named, are invalid:
- * not counted, not placed, and flagged. Two kernels, no host synchronisation.
+ * not counted, not placed, and flagged. Two kernels (one when the routes fit a single
+ * 256-item tile), no host synchronisation.
  */
 moe_status_t moe_dispatch_layout(const int32_t* topk_idx, int32_t s, int32_t e, int32_t k,
                                  int32_t capacity, void* workspace, size_t workspace_bytes,

@@ -132,16 +132,17 @@ def test_layout_random_cases(s, e, k, cap, routing):
     check_layout(Lg, oracle.dispatch_layout(idx, e, cap), f"s={s} e={e} k={k} c={cap}")
 
 
+@pytest.mark.parametrize("s", [600, 200])  # several tiles; one tile (no count launch)
 @pytest.mark.parametrize("cap", [0, 3])
-def test_layout_invalid_routes_are_flagged_and_skipped(cap):
-    announce("layout invalid", cap)
+def test_layout_invalid_routes_are_flagged_and_skipped(cap, s):
+    announce("layout invalid", cap, s)
     rng = np.random.default_rng(77 + cap)
-    s, e, k = 600, 12, 4
+    e, k = 12, 4
     idx = W.random_idx(rng, s, e, k)
     idx[5, 2] = e          # out of range
     idx[17, 0] = -3        # out of range
-    idx[300, 3] = idx[300, 1]  # duplicate
-    idx[599, 1] = idx[599, 0]
+    idx[s // 2, 3] = idx[s // 2, 1]  # duplicate
+    idx[s - 1, 1] = idx[s - 1, 0]
     Lg = M.moe_dispatch_layout(to_dev(idx), e, cap)
     Lo = oracle.dispatch_layout(idx, e, cap)
     assert Lo.flags == 3

@@ -46,18 +46,28 @@ def f32_ulps(got: np.ndarray, want: np.ndarray) -> np.ndarray:
     return np.abs(key(got) - key(want))
 
 
-def sub_layout(L: oracle.Layout, tokens: np.ndarray) -> oracle.Layout:
-    """The oracle layout restricted to some tokens (combine is per token)."""
-    return oracle.Layout(s=len(tokens), e=L.e, k=L.k, capacity=L.capacity, rows=L.rows,
-                         idx=L.idx[tokens], counts=L.counts, kept=L.kept, offsets=L.offsets,
-                         dst=L.dst[tokens], src=L.src, flags=L.flags, checksum=L.checksum)
+def compact_layout(L: oracle.Layout, tokens: np.ndarray) -> tuple[oracle.Layout, np.ndarray]:
+    """The oracle layout restricted to some tokens, the buffer rows their routes point at
+    renumbered 0..n-1 (combine and its backward are per token, so a chunk of tokens can be
+    checked against a compact copy of just its rows).
+
+    Returns (layout, used): `used` holds the original row of each compact row, ascending;
+    layout.src is the token of each compact row."""
+    dst = L.dst[tokens]
+    placed = dst >= 0
+    used = np.unique(dst[placed]).astype(np.int64)
+    cdst = np.full(dst.shape, -1, dtype=np.int32)
+    cdst[placed] = np.searchsorted(used, dst[placed]).astype(np.int32)
+    sub = oracle.Layout(s=len(tokens), e=L.e, k=L.k, capacity=L.capacity, rows=len(used),
+                        idx=L.idx[tokens], counts=L.counts, kept=L.kept, offsets=L.offsets,
+                        dst=cdst, src=L.src[used], flags=L.flags, checksum=L.checksum)
+    return sub, used
 
 
-def sample_tokens(s: int, n: int, seed: int = 0) -> np.ndarray:
-    rng = np.random.default_rng(seed)
-    pick = set(rng.choice(s, size=min(n, s), replace=False).tolist())
-    pick.update({0, s - 1, min(255, s - 1), min(256, s - 1)})
-    return np.array(sorted(pick), dtype=np.int64)
+def token_chunks(s: int, chunk: int):
+    """Consecutive token ranges covering all s tokens."""
+    for t0 in range(0, s, chunk):
+        yield np.arange(t0, min(s, t0 + chunk), dtype=np.int64)
 
 
 def weight_grad_bound(gy32: np.ndarray, E32: np.ndarray, dst: np.ndarray) -> np.ndarray:

@@ -16,12 +16,11 @@ import torch
 import combine_moe_gate_amd as M
 import oracle
 import workloads as W
-from tests.gpu_util import (assert_bits_equal, f32_ulps, sample_tokens, sub_layout, tagged_rows,
-                            to_dev, to_host, weight_grad_bound)
+from tests.gpu_util import (TORCH_DTYPE, assert_bits_equal, compact_layout, f32_ulps, tagged_rows,
+                            to_dev, to_host, token_chunks, weight_grad_bound)
 
 pytestmark = pytest.mark.gpu
 
-SMALL = ["tiny_capacity_top2", "dropless_top8_h2816", "gshard_capacity_drop"]
 ALL = list(W.WORKLOADS)
 
 
@@ -225,8 +224,41 @@ def test_unit_weight_round_trip_closed_form(dtype, cap):
 # whole path on the five workloads, at full size
 
 
+# tokens per chunk of the full-size sweeps below: every token of every workload is
+# compared, a chunk at a time, against the oracle run on just that chunk's rows
+CHUNK_TOKENS = 1024
+
+
+def check_end_to_end_chunk(toks, S, E_c, wt_o, idx_o, dt, e, y_o, gw_o, bound, y_g, gw_g, gl_g, what):
+    """One chunk of tokens end to end, each side with its own gate weights: combine within
+    1e-6 relative (float32) or one ulp of the element type of the oracle's y_o; grad_w
+    (which does not depend on the weights) within 1e-6 of sum_m |grad_y * E| (`bound`) of
+    the oracle's gw_o; the gate gradient within its bound."""
+    if dt == "f32":
+        mag = np.zeros(y_o.shape)
+        for j in range(S.k):
+            sel = S.dst[:, j] >= 0
+            mag[sel] += np.abs(wt_o[toks][sel, j, None].astype(np.float64) * E_c[S.dst[sel, j]])
+        assert np.all(np.abs(y_g.astype(np.float64) - y_o) <= 1e-6 * mag + 1e-30), f"{what} combine"
+    else:
+        yg, yo = oracle.to_f32(y_g, dt).astype(np.float64), oracle.to_f32(y_o, dt).astype(np.float64)
+        assert np.all(np.abs(yg - yo) <= dtype_ulp(np.maximum(np.abs(yg), np.abs(yo)), dt)), f"{what} combine"
+    assert np.all(np.abs(gw_g.astype(np.float64) - gw_o) <= 1e-6 * bound), f"{what} grad_w"
+    gl_o = oracle.gate_topk_backward(idx_o[toks], wt_o[toks], gw_o, e)
+    assert np.all(gl_g[gl_o == 0] == 0), f"{what} gate gradient off the selection"
+    w64, g64 = wt_o[toks].astype(np.float64), gw_o.astype(np.float64)
+    scale = np.zeros((len(toks), e))
+    dotmag = np.abs(w64 * g64).sum(1, keepdims=True)
+    np.put_along_axis(scale, idx_o[toks].astype(np.int64), np.abs(w64) * (np.abs(g64) + dotmag), axis=1)
+    assert np.all(np.abs(gl_g.astype(np.float64) - gl_o) <= 8 * 2.0 ** -24 * scale + 1e-38), \
+        f"{what} gate gradient"
+
+
 @pytest.mark.parametrize("name", ALL)
 def test_workload_path_matches_oracle(name):
+    """The whole path at full size, every token compared: gate, layout, dispatch and
+    replay bit-exact; combine, grad_E and grad_x bit-exact given the oracle's weights,
+    grad_w within its bound; end to end with the GPU's own weights within tolerance."""
     announce("workload", name)
     inp = W.make_inputs(name)
     w = inp.workload
@@ -249,94 +281,77 @@ def test_workload_path_matches_oracle(name):
     torch.cuda.synchronize()
 
     assert_bits_equal(to_host(idx), idx_o, "idx")
+    assert f32_ulps(to_host(wt), wt_o).max() <= 1
     check_layout(Lg, Lo, name)
     check_buffer_chunked(buf, inp.x, Lo.src, "dispatch")
     assert torch.equal(replay.view(torch.uint8), buf.view(torch.uint8)), "replay differs"
+    del replay, gE
 
-    # op level, bit exact: the oracle's weights fed to the GPU combine
+    # op level, bit exact: the oracle's weights fed to the GPU combine and its backward
     wt_o_dev = to_dev(wt_o)
-    toks = np.arange(w.s) if name in SMALL else sample_tokens(w.s, 512)
-    S = sub_layout(Lo, toks)
-    E_o = oracle.dispatch(Lo, inp.x) if name in SMALL else None
-    if E_o is None:
-        E_o = np.zeros((Lo.rows, w.m), dtype=inp.x.dtype)
-        rows = S.dst[S.dst >= 0]
-        E_o[rows] = inp.x[Lo.src[rows]]
-    y_same_w = to_host(M.moe_combine(Lg, buf, wt_o_dev))[toks]
-    assert_bits_equal(y_same_w, oracle.combine(S, E_o, wt_o[toks], dt), "combine (same weights)")
-
+    y_same_w = to_host(M.moe_combine(Lg, buf, wt_o_dev))
     gE_s, gw_s = M.moe_combine_backward(Lg, gy, buf, wt_o_dev)
-    gE_o, gw_o = oracle.combine_backward(S, inp.grad_y[toks], E_o, wt_o[toks], dt)
-    rows = S.dst[S.dst >= 0]
-    assert_bits_equal(to_host(gE_s)[rows] if name in SMALL else to_host(gE_s[torch.from_numpy(rows).cuda()]),
-                      gE_o[rows], "grad_E (same weights)")
-    bound = weight_grad_bound(oracle.to_f32(inp.grad_y[toks], dt), oracle.to_f32(E_o, dt), S.dst)
-    err = np.abs(to_host(gw_s)[toks].astype(np.float64) - gw_o)
-    assert np.all(err <= 1e-6 * bound)
-
-    gx_s = to_host(M.moe_dispatch_backward(Lg, gE_s))[toks]
-    # oracle dispatch backward over the same grad_E rows (the oracle's own grad_E)
-    assert_bits_equal(gx_s, oracle.dispatch_backward(S, gE_o, dt), "dispatch backward (same weights)")
-
-    # end to end with each side's own weights: within the stated tolerance
-    assert f32_ulps(to_host(wt), wt_o).max() <= 1
-    y_o = oracle.combine(S, E_o, wt_o[toks], dt)
-    y_g = to_host(y)[toks]
-    if dt == "f32":
-        mag = np.zeros((len(toks), w.m))
-        for j in range(w.k):
-            sel = S.dst[:, j] >= 0
-            mag[sel] += np.abs(wt_o[toks][sel, j, None].astype(np.float64) * E_o[S.dst[sel, j]])
-        assert np.all(np.abs(y_g.astype(np.float64) - y_o) <= 1e-6 * mag + 1e-30)
-    else:
-        yg, yo = oracle.to_f32(y_g, dt).astype(np.float64), oracle.to_f32(y_o, dt).astype(np.float64)
-        assert np.all(np.abs(yg - yo) <= dtype_ulp(np.maximum(np.abs(yg), np.abs(yo)), dt))
-    # grad_w does not depend on the weights, so the GPU's end-to-end grad_w meets the
-    # oracle's directly; the gate gradient then differs only through last-ulp weights
-    gw_g = to_host(gw)[toks]
-    assert np.all(np.abs(gw_g.astype(np.float64) - gw_o) <= 1e-6 * bound)
-    gl_o = oracle.gate_topk_backward(idx_o[toks], wt_o[toks], gw_o, w.e)
-    gl_g = to_host(gl)[toks]
-    assert np.all(gl_g[gl_o == 0] == 0)
-    w64, g64 = wt_o[toks].astype(np.float64), gw_o.astype(np.float64)
-    scale = np.zeros((len(toks), w.e))
-    dotmag = np.abs(w64 * g64).sum(1, keepdims=True)
-    np.put_along_axis(scale, idx_o[toks].astype(np.int64), np.abs(w64) * (np.abs(g64) + dotmag), axis=1)
-    assert np.all(np.abs(gl_g.astype(np.float64) - gl_o) <= 8 * 2.0 ** -24 * scale + 1e-38)
+    gx_s = to_host(M.moe_dispatch_backward(Lg, gE_s))
+    gw_s = to_host(gw_s)
+    y_g, gw_g, gl_g = to_host(y), to_host(gw), to_host(gl)
+    n_checked = 0
+    for toks in token_chunks(w.s, CHUNK_TOKENS):
+        what = f"{name} tokens {toks[0]}:{toks[-1] + 1}"
+        S, used = compact_layout(Lo, toks)
+        E_c = inp.x[S.src]  # the identity expert: each row is its token's row
+        y_o = oracle.combine(S, E_c, wt_o[toks], dt)
+        assert_bits_equal(y_same_w[toks], y_o, f"{what} combine (same weights)")
+        gE_o, gw_o = oracle.combine_backward(S, inp.grad_y[toks], E_c, wt_o[toks], dt)
+        assert_bits_equal(to_host(gE_s[torch.from_numpy(used).cuda()]), gE_o, f"{what} grad_E (same weights)")
+        bound = weight_grad_bound(oracle.to_f32(inp.grad_y[toks], dt), oracle.to_f32(E_c, dt), S.dst)
+        assert np.all(np.abs(gw_s[toks].astype(np.float64) - gw_o) <= 1e-6 * bound), f"{what} grad_w"
+        assert_bits_equal(gx_s[toks], oracle.dispatch_backward(S, gE_o, dt), f"{what} dispatch backward")
+        check_end_to_end_chunk(toks, S, E_c, wt_o, idx_o, dt, w.e, y_o, gw_o, bound, y_g[toks],
+                               gw_g[toks], gl_g[toks], what)
+        n_checked += len(toks)
+    assert n_checked == w.s
 
 
 @pytest.mark.parametrize("name", ALL)
 def test_tagged_expert_rows_at_full_size(name):
     """Combine and its backward at full size, in the bench's launch configuration, over
-    expert rows tagged by a power of two per expert, against the oracle on sampled
-    tokens: bit-exact combine and grad_E, grad_w within its bound."""
+    expert rows tagged by a power of two per expert, against the oracle on every token:
+    bit-exact combine and grad_E, grad_w within its bound."""
     announce("tagged expert", name)
     inp = W.make_inputs(name)
     w = inp.workload
     dt = w.dtype
     idx_o, wt_o = oracle.gate_topk(inp.logits, w.k)
     Lo = oracle.dispatch_layout(idx_o, w.e, w.capacity)
-    toks = np.arange(w.s) if name in SMALL else sample_tokens(w.s, 512)
-    S = sub_layout(Lo, toks)
     # expert of every buffer row, from the segments
     expert_of_row = np.repeat(np.arange(w.e), np.diff(Lo.offsets))
     expert_of_row = np.concatenate([expert_of_row, np.zeros(Lo.rows - len(expert_of_row), np.int64)])
-    src = np.full(Lo.rows, -1, dtype=np.int64)
-    rows = S.dst[S.dst >= 0]
-    src[rows] = Lo.src[rows]
-    E = tagged_rows(inp.x, src, expert_of_row, dt)
-    assert E.shape == (Lo.rows, w.m)
-
     Lg = M.moe_dispatch_layout(to_dev(idx_o), w.e, w.capacity)
-    E_dev, wt_dev, gy_dev = to_dev(E, dt), to_dev(wt_o), to_dev(inp.grad_y, dt)
-    y = to_host(M.moe_combine(Lg, E_dev, wt_dev))[toks]
-    assert_bits_equal(y, oracle.combine(S, E, wt_o[toks], dt), "combine over tagged rows")
+    E_dev = torch.empty((Lo.rows, w.m), dtype=TORCH_DTYPE[dt], device="cuda")
+    for r0 in range(0, Lo.rows, 32768):  # the tagged rows, built and uploaded in pieces
+        r1 = min(Lo.rows, r0 + 32768)
+        E_dev[r0:r1] = to_dev(tagged_rows(inp.x, Lo.src[r0:r1], expert_of_row[r0:r1], dt), dt)
+    wt_dev, gy_dev = to_dev(wt_o), to_dev(inp.grad_y, dt)
+    y = to_host(M.moe_combine(Lg, E_dev, wt_dev))
     gE, gw = M.moe_combine_backward(Lg, gy_dev, E_dev, wt_dev)
-    gE_o, gw_o = oracle.combine_backward(S, inp.grad_y[toks], E, wt_o[toks], dt)
-    assert_bits_equal(to_host(gE[torch.from_numpy(rows).cuda()]), gE_o[rows], "grad_E")
-    bound = weight_grad_bound(oracle.to_f32(inp.grad_y[toks], dt), oracle.to_f32(E, dt), S.dst)
-    err = np.abs(to_host(gw)[toks].astype(np.float64) - gw_o)
-    assert np.all(err <= 1e-6 * bound), f"grad_w err {err.max()}"
+    gw = to_host(gw)
+    n_checked = 0
+    for toks in token_chunks(w.s, CHUNK_TOKENS):
+        what = f"{name} tokens {toks[0]}:{toks[-1] + 1}"
+        S, used = compact_layout(Lo, toks)
+        E_c = tagged_rows(inp.x, S.src, expert_of_row[used], dt)
+        assert_bits_equal(y[toks], oracle.combine(S, E_c, wt_o[toks], dt), f"{what} combine over tagged rows")
+        gE_o, gw_o = oracle.combine_backward(S, inp.grad_y[toks], E_c, wt_o[toks], dt)
+        assert_bits_equal(to_host(gE[torch.from_numpy(used).cuda()]), gE_o, f"{what} grad_E")
+        bound = weight_grad_bound(oracle.to_f32(inp.grad_y[toks], dt), oracle.to_f32(E_c, dt), S.dst)
+        err = np.abs(gw[toks].astype(np.float64) - gw_o)
+        assert np.all(err <= 1e-6 * bound), f"{what} grad_w err {err.max()}"
+        n_checked += len(toks)
+    assert n_checked == w.s
+    # rows no route fills come back zero in grad_E
+    unfilled = np.nonzero(Lo.src < 0)[0]
+    if len(unfilled):
+        assert not bool(gE[torch.from_numpy(unfilled).cuda()].ne(0).any()), "grad_E unfilled rows"
 
 
 def dtype_ulp(mag: np.ndarray, dt: str) -> np.ndarray:

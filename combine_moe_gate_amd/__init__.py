@@ -154,6 +154,35 @@ def _require_gpu(*tensors):
             raise ValueError("all tensors must be contiguous")
 
 
+def _expect(t, name: str, shape, dtype=None):
+    """Check a tensor argument before any pointer reaches the library: its shape (None
+    matches any size in that place) and element type. The C ABI receives bare pointers
+    and cannot tell a short or mistyped buffer from a right one."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dim() != len(shape) or any(want is not None and got != want for got, want in zip(t.shape, shape)):
+        want = "[" + ", ".join("*" if d is None else str(d) for d in shape) + "]"
+        raise ValueError(f"{name} must have shape {want}, got {list(t.shape)}")
+    if dtype is not None:
+        allowed = dtype if isinstance(dtype, tuple) else (dtype,)
+        if t.dtype not in allowed:
+            raise ValueError(f"{name} must be {' or '.join(str(d) for d in allowed)}, got {t.dtype}")
+
+
+_ROW_DTYPES = tuple(_DTYPE_CODE)
+
+
+def _same_device(layout, *tensors):
+    """Every tensor on the layout's device (its workspace's), contiguous."""
+    _require_gpu(*tensors)
+    dev = layout.workspace.device
+    for t in tensors:
+        if t is not None and t.device != dev:
+            raise ValueError(f"tensor on {t.device}, the layout lives on {dev}")
+
+
 def workspace_bytes(s: int, e: int, k: int, capacity: int, route_major: bool = False,
                     pad_multiple: int = 1) -> int:
     opts = LayoutOptions(int(route_major), pad_multiple)
@@ -209,10 +238,11 @@ class Layout:
 
 
 def moe_gate_topk(logits: torch.Tensor, k: int, idx_out=None, w_out=None):
-    _require_gpu(logits)
+    _expect(logits, "logits", (None, None), torch.float32)
     s, e = logits.shape
-    if logits.dtype != torch.float32:
-        raise ValueError("logits must be float32")
+    _expect(idx_out, "idx_out", (s, k), torch.int32)
+    _expect(w_out, "w_out", (s, k), torch.float32)
+    _require_gpu(logits, idx_out, w_out)
     idx = idx_out if idx_out is not None else torch.empty((s, k), dtype=torch.int32, device=logits.device)
     w = w_out if w_out is not None else torch.empty((s, k), dtype=torch.float32, device=logits.device)
     _check(lib().moe_gate_topk(_ptr(logits), s, e, k, _ptr(idx), _ptr(w), _stream(logits)))
@@ -220,8 +250,12 @@ def moe_gate_topk(logits: torch.Tensor, k: int, idx_out=None, w_out=None):
 
 
 def moe_gate_topk_backward(idx: torch.Tensor, w: torch.Tensor, grad_w: torch.Tensor, e: int, out=None):
-    _require_gpu(idx, w, grad_w)
+    _expect(idx, "idx", (None, None), torch.int32)
     s, k = idx.shape
+    _expect(w, "w", (s, k), torch.float32)
+    _expect(grad_w, "grad_w", (s, k), torch.float32)
+    _expect(out, "out", (s, e), torch.float32)
+    _require_gpu(idx, w, grad_w, out)
     gl = out if out is not None else torch.empty((s, e), dtype=torch.float32, device=idx.device)
     _check(lib().moe_gate_topk_backward(_ptr(idx), _ptr(w), _ptr(grad_w), s, e, k, _ptr(gl), _stream(idx)))
     return gl
@@ -229,9 +263,9 @@ def moe_gate_topk_backward(idx: torch.Tensor, w: torch.Tensor, grad_w: torch.Ten
 
 def moe_dispatch_layout(idx: torch.Tensor, e: int, capacity: int = 0, workspace=None,
                         route_major: bool = False, pad_multiple: int = 1) -> Layout:
-    _require_gpu(idx)
-    if idx.dtype != torch.int32:
-        raise ValueError("expert ids must be int32")
+    _expect(idx, "expert ids", (None, None), torch.int32)
+    _expect(workspace, "workspace", (None,), torch.uint8)
+    _require_gpu(idx, workspace)
     s, k = idx.shape
     opts = LayoutOptions(int(route_major), pad_multiple)
     nbytes = workspace_bytes(s, e, k, capacity, route_major, pad_multiple)
@@ -242,6 +276,8 @@ def moe_dispatch_layout(idx: torch.Tensor, e: int, capacity: int = 0, workspace=
                                             _stream(idx)))
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=idx.device)
+    elif workspace.device != idx.device:
+        raise ValueError(f"workspace on {workspace.device}, the expert ids on {idx.device}")
     st = LayoutStruct()
     _check(lib().moe_dispatch_layout_ex(_ptr(idx), s, e, k, capacity, ctypes.byref(opts),
                                         _ptr(workspace), workspace.numel(), ctypes.byref(st),
@@ -257,16 +293,21 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def moe_dispatch(layout: Layout, x: torch.Tensor, out=None):
-    _require_gpu(x)
+    _expect(x, "x", (layout.s, None), _ROW_DTYPES)
     m = x.shape[1]
+    _expect(out, "out", (layout.rows, m), x.dtype)
+    _same_device(layout, x, out)
     out = out if out is not None else torch.empty((layout.rows, m), dtype=x.dtype, device=x.device)
     _check(lib().moe_dispatch(layout.byref(), _ptr(x), m, _dtype_code(x), _ptr(out), _stream(x)))
     return out
 
 
 def moe_dispatch_replay(layout: Layout, x: torch.Tensor, idx=None, out=None):
-    _require_gpu(x, idx)
+    _expect(x, "x", (layout.s, None), _ROW_DTYPES)
     m = x.shape[1]
+    _expect(idx, "idx", (layout.s, layout.k), torch.int32)
+    _expect(out, "out", (layout.rows, m), x.dtype)
+    _same_device(layout, x, idx, out)
     out = out if out is not None else torch.empty((layout.rows, m), dtype=x.dtype, device=x.device)
     _check(lib().moe_dispatch_replay(layout.byref(), _ptr(idx), _ptr(x), m, _dtype_code(x),
                                      _ptr(out), _stream(x)))
@@ -275,8 +316,11 @@ def moe_dispatch_replay(layout: Layout, x: torch.Tensor, idx=None, out=None):
 
 def moe_combine(layout: Layout, expert_out: torch.Tensor, w, out=None):
     """Weighted combine; w=None gives the unweighted sum (after moe_dispatch_weighted)."""
-    _require_gpu(expert_out, w)
+    _expect(expert_out, "expert_out", (layout.rows, None), _ROW_DTYPES)
     m = expert_out.shape[1]
+    _expect(w, "w", (layout.s, layout.k), torch.float32)
+    _expect(out, "out", (layout.s, m), expert_out.dtype)
+    _same_device(layout, expert_out, w, out)
     y = out if out is not None else torch.empty((layout.s, m), dtype=expert_out.dtype, device=expert_out.device)
     _check(lib().moe_combine(layout.byref(), _ptr(expert_out), _ptr(w), m, _dtype_code(expert_out),
                              _ptr(y), _stream(expert_out)))
@@ -285,8 +329,15 @@ def moe_combine(layout: Layout, expert_out: torch.Tensor, w, out=None):
 
 def moe_combine_backward(layout: Layout, grad_y: torch.Tensor, expert_out: torch.Tensor,
                          w: torch.Tensor, grad_expert_out=None, grad_w=None):
-    _require_gpu(grad_y, expert_out, w)
+    _expect(grad_y, "grad_y", (layout.s, None), _ROW_DTYPES)
     m = grad_y.shape[1]
+    _expect(expert_out, "expert_out", (layout.rows, m), grad_y.dtype)
+    if w is None:
+        raise ValueError("w is required (the combine's route weights)")
+    _expect(w, "w", (layout.s, layout.k), torch.float32)
+    _expect(grad_expert_out, "grad_expert_out", (layout.rows, m), grad_y.dtype)
+    _expect(grad_w, "grad_w", (layout.s, layout.k), torch.float32)
+    _same_device(layout, grad_y, expert_out, w, grad_expert_out, grad_w)
     gE = grad_expert_out if grad_expert_out is not None else torch.empty(
         (layout.rows, m), dtype=grad_y.dtype, device=grad_y.device)
     gw = grad_w if grad_w is not None else torch.empty((layout.s, layout.k), dtype=torch.float32,
@@ -297,8 +348,10 @@ def moe_combine_backward(layout: Layout, grad_y: torch.Tensor, expert_out: torch
 
 
 def moe_dispatch_backward(layout: Layout, grad_out: torch.Tensor, out=None):
-    _require_gpu(grad_out)
+    _expect(grad_out, "grad_out", (layout.rows, None), _ROW_DTYPES)
     m = grad_out.shape[1]
+    _expect(out, "out", (layout.s, m), grad_out.dtype)
+    _same_device(layout, grad_out, out)
     gx = out if out is not None else torch.empty((layout.s, m), dtype=grad_out.dtype, device=grad_out.device)
     _check(lib().moe_dispatch_backward(layout.byref(), _ptr(grad_out), m, _dtype_code(grad_out),
                                        _ptr(gx), _stream(grad_out)))
@@ -306,8 +359,13 @@ def moe_dispatch_backward(layout: Layout, grad_out: torch.Tensor, out=None):
 
 
 def moe_dispatch_weighted(layout: Layout, x: torch.Tensor, w: torch.Tensor, out=None):
-    _require_gpu(x, w)
+    _expect(x, "x", (layout.s, None), _ROW_DTYPES)
     m = x.shape[1]
+    if w is None:
+        raise ValueError("w is required (the route weights applied at dispatch)")
+    _expect(w, "w", (layout.s, layout.k), torch.float32)
+    _expect(out, "out", (layout.rows, m), x.dtype)
+    _same_device(layout, x, w, out)
     out = out if out is not None else torch.empty((layout.rows, m), dtype=x.dtype, device=x.device)
     _check(lib().moe_dispatch_weighted(layout.byref(), _ptr(x), _ptr(w), m, _dtype_code(x), _ptr(out),
                                        _stream(x)))
@@ -316,8 +374,15 @@ def moe_dispatch_weighted(layout: Layout, x: torch.Tensor, w: torch.Tensor, out=
 
 def moe_dispatch_weighted_backward(layout: Layout, grad_out: torch.Tensor, x: torch.Tensor,
                                    w: torch.Tensor, grad_x=None, grad_w=None):
-    _require_gpu(grad_out, x, w)
+    _expect(x, "x", (layout.s, None), _ROW_DTYPES)
     m = x.shape[1]
+    _expect(grad_out, "grad_out", (layout.rows, m), x.dtype)
+    if w is None:
+        raise ValueError("w is required (the route weights applied at dispatch)")
+    _expect(w, "w", (layout.s, layout.k), torch.float32)
+    _expect(grad_x, "grad_x", (layout.s, m), x.dtype)
+    _expect(grad_w, "grad_w", (layout.s, layout.k), torch.float32)
+    _same_device(layout, grad_out, x, w, grad_x, grad_w)
     gx = grad_x if grad_x is not None else torch.empty_like(x)
     gw = grad_w if grad_w is not None else torch.empty((layout.s, layout.k), dtype=torch.float32,
                                                       device=x.device)
@@ -334,13 +399,13 @@ def moe_expert_gemm(layout: Layout, a: torch.Tensor, weights: torch.Tensor, gath
     loads), else a dispatched buffer [rows, m]; weights [e, n, m]; w [s, k] float32 scales
     each row by its route's weight, or None. Returns out [rows, n].
     """
-    _require_gpu(a, weights, w)
+    _expect(a, "a", (layout.s if gather else layout.rows, None), _ROW_DTYPES)
     m = a.shape[1]
+    _expect(weights, "weights", (layout.e, None, m), a.dtype)
     n = weights.shape[1]
-    if weights.dim() != 3 or weights.shape[0] != layout.e or weights.shape[2] != m:
-        raise ValueError(f"weights must be [e={layout.e}, n, m={m}], got {tuple(weights.shape)}")
-    if weights.dtype != a.dtype:
-        raise ValueError("a and weights must have the same dtype")
+    _expect(w, "w", (layout.s, layout.k), torch.float32)
+    _expect(out, "out", (layout.rows, n), a.dtype)
+    _same_device(layout, a, weights, w, out)
     out = out if out is not None else torch.empty((layout.rows, n), dtype=a.dtype, device=a.device)
     _check(lib().moe_expert_gemm(layout.byref(), _ptr(a), int(bool(gather)), _ptr(weights), m, n,
                                  _dtype_code(a), _ptr(w), _ptr(out), _stream(a)))
@@ -357,15 +422,16 @@ def moe_expert_gemm_wgrad(layout: Layout, a: torch.Tensor, grad_out: torch.Tenso
     a is x [s, m] when gather (rows gathered through the layout), else a dispatched
     buffer [rows, m]; grad_out [rows, n] in a's dtype.
     """
-    _require_gpu(a, grad_out)
+    _expect(a, "a", (layout.s if gather else layout.rows, None), _ROW_DTYPES)
     m = a.shape[1]
+    _expect(grad_out, "grad_out", (layout.rows, None), a.dtype)
     n = grad_out.shape[1]
-    if grad_out.dtype != a.dtype:
-        raise ValueError("a and grad_out must have the same dtype")
+    _expect(out, "out", (layout.e, n, m), (torch.float32, a.dtype))
+    _same_device(layout, a, grad_out, out)
     if out is None:
+        if out_dtype not in (torch.float32, a.dtype):
+            raise ValueError(f"out_dtype must be float32 or {a.dtype}, got {out_dtype}")
         out = torch.empty((layout.e, n, m), dtype=out_dtype, device=a.device)
-    elif tuple(out.shape) != (layout.e, n, m) or not out.is_contiguous():
-        raise ValueError(f"out must be a contiguous [{layout.e}, {n}, {m}] tensor")
     _check(lib().moe_expert_gemm_wgrad(layout.byref(), _ptr(a), int(bool(gather)), _ptr(grad_out), m, n,
                                        _dtype_code(a), _dtype_code(out), _ptr(out), _stream(a)))
     return out
@@ -375,13 +441,12 @@ def moe_expert_gemm_dgrad(layout: Layout, grad_out: torch.Tensor, weights: torch
     """Input-row gradient of moe_expert_gemm: grad_a[r] = grad_out[r] @ weights[x] for the
     placed rows of expert x, [rows, m] (zero rows where no route is placed). The token
     gradient of the gathered forward is moe_dispatch_backward(layout, grad_a)."""
-    _require_gpu(grad_out, weights)
+    _expect(grad_out, "grad_out", (layout.rows, None), _ROW_DTYPES)
     n = grad_out.shape[1]
-    if weights.dim() != 3 or weights.shape[0] != layout.e or weights.shape[1] != n:
-        raise ValueError(f"weights must be [e={layout.e}, n={n}, m], got {tuple(weights.shape)}")
-    if weights.dtype != grad_out.dtype:
-        raise ValueError("grad_out and weights must have the same dtype")
+    _expect(weights, "weights", (layout.e, n, None), grad_out.dtype)
     m = weights.shape[2]
+    _expect(out, "out", (layout.rows, m), grad_out.dtype)
+    _same_device(layout, grad_out, weights, out)
     out = out if out is not None else torch.empty((layout.rows, m), dtype=grad_out.dtype, device=grad_out.device)
     _check(lib().moe_expert_gemm_dgrad(layout.byref(), _ptr(grad_out), _ptr(weights), m, n,
                                        _dtype_code(grad_out), _ptr(out), _stream(grad_out)))
@@ -389,14 +454,19 @@ def moe_expert_gemm_dgrad(layout: Layout, grad_out: torch.Tensor, weights: torch
 
 
 def moe_renormalize_kept(layout: Layout, w: torch.Tensor, out=None):
-    _require_gpu(w)
+    _expect(w, "w", (layout.s, layout.k), torch.float32)
+    _expect(out, "out", (layout.s, layout.k), torch.float32)
+    _same_device(layout, w, out)
     w_out = out if out is not None else torch.empty_like(w)
     _check(lib().moe_renormalize_kept(layout.byref(), _ptr(w), _ptr(w_out), _stream(w)))
     return w_out
 
 
 def moe_renormalize_kept_backward(layout: Layout, w: torch.Tensor, grad_out: torch.Tensor, out=None):
-    _require_gpu(w, grad_out)
+    _expect(w, "w", (layout.s, layout.k), torch.float32)
+    _expect(grad_out, "grad_out", (layout.s, layout.k), torch.float32)
+    _expect(out, "out", (layout.s, layout.k), torch.float32)
+    _same_device(layout, w, grad_out, out)
     gw = out if out is not None else torch.empty_like(w)
     _check(lib().moe_renormalize_kept_backward(layout.byref(), _ptr(w), _ptr(grad_out), _ptr(gw),
                                                _stream(w)))

@@ -233,3 +233,91 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(4, 8)
     with pytest.raises((ValueError, RuntimeError)):
         M.moe_gate_topk(x, 2)
+
+
+# ----------------------------------------------------------------------------
+# the binding checks tensors against the layout before any pointer reaches the library
+# (the C ABI gets bare pointers and could not tell a short or mistyped buffer)
+
+
+def fake_layout(s=6, e=4, k=2, rows=12):
+    st = M.LayoutStruct()
+    st.s, st.e, st.k, st.rows = s, e, k, rows
+    return M.Layout(st, torch.empty(0, dtype=torch.uint8))
+
+
+@pytest.fixture
+def no_library(monkeypatch):
+    def refuse():
+        raise AssertionError("the library was called with arguments the binding should have refused")
+    monkeypatch.setattr(M, "lib", refuse)
+
+
+BAD_CALLS = [
+    # (call, message fragment): shapes against the layout s=6, e=4, k=2, rows=12, m=8
+    (lambda L: M.moe_dispatch(L, torch.zeros(5, 8)), "x must have shape [6, *]"),
+    (lambda L: M.moe_dispatch(L, torch.zeros(6, 8, dtype=torch.int32)), "x must be"),
+    (lambda L: M.moe_dispatch(L, torch.zeros(6, 8), out=torch.zeros(11, 8)), "out must have shape [12, 8]"),
+    (lambda L: M.moe_dispatch(L, torch.zeros(6, 8), out=torch.zeros(12, 8, dtype=torch.float16)), "out must be"),
+    (lambda L: M.moe_dispatch_replay(L, torch.zeros(6, 8), torch.zeros(6, 3, dtype=torch.int32)), "idx must have"),
+    (lambda L: M.moe_dispatch_replay(L, torch.zeros(6, 8), torch.zeros(6, 2, dtype=torch.int64)), "idx must be"),
+    (lambda L: M.moe_combine(L, torch.zeros(11, 8), torch.zeros(6, 2)), "expert_out must have shape [12, *]"),
+    (lambda L: M.moe_combine(L, torch.zeros(12, 8), torch.zeros(6, 2, dtype=torch.bfloat16)), "w must be"),
+    (lambda L: M.moe_combine(L, torch.zeros(12, 8), torch.zeros(5, 2)), "w must have shape [6, 2]"),
+    (lambda L: M.moe_combine(L, torch.zeros(12, 8), None, out=torch.zeros(6, 4)), "out must have shape [6, 8]"),
+    (lambda L: M.moe_combine_backward(L, torch.zeros(6, 8), torch.zeros(12, 8), None), "w is required"),
+    (lambda L: M.moe_combine_backward(L, torch.zeros(6, 8), torch.zeros(12, 4), torch.zeros(6, 2)),
+     "expert_out must have shape [12, 8]"),
+    (lambda L: M.moe_combine_backward(L, torch.zeros(6, 8), torch.zeros(12, 8, dtype=torch.float16),
+                                      torch.zeros(6, 2)), "expert_out must be"),
+    (lambda L: M.moe_combine_backward(L, torch.zeros(6, 8), torch.zeros(12, 8), torch.zeros(6, 2),
+                                      grad_w=torch.zeros(6, 2, dtype=torch.float64)), "grad_w must be"),
+    (lambda L: M.moe_dispatch_backward(L, torch.zeros(6, 8)), "grad_out must have shape [12, *]"),
+    (lambda L: M.moe_dispatch_weighted(L, torch.zeros(6, 8), torch.zeros(6, 1)), "w must have shape [6, 2]"),
+    (lambda L: M.moe_dispatch_weighted_backward(L, torch.zeros(12, 8), torch.zeros(6, 8), torch.zeros(6, 2),
+                                                grad_x=torch.zeros(6, 9)), "grad_x must have shape [6, 8]"),
+    (lambda L: M.moe_renormalize_kept(L, torch.zeros(6, 3)), "w must have shape [6, 2]"),
+    (lambda L: M.moe_renormalize_kept_backward(L, torch.zeros(6, 2), torch.zeros(6, 2, dtype=torch.float16)),
+     "grad_out must be"),
+    (lambda L: M.moe_expert_gemm(L, torch.zeros(12, 8, dtype=torch.bfloat16),
+                                 torch.zeros(4, 16, 8, dtype=torch.bfloat16)), "a must have shape [6, *]"),
+    (lambda L: M.moe_expert_gemm(L, torch.zeros(6, 8, dtype=torch.bfloat16),
+                                 torch.zeros(3, 16, 8, dtype=torch.bfloat16)), "weights must have shape [4, *, 8]"),
+    (lambda L: M.moe_expert_gemm(L, torch.zeros(6, 8, dtype=torch.bfloat16),
+                                 torch.zeros(4, 16, 8, dtype=torch.float16)), "weights must be"),
+    (lambda L: M.moe_expert_gemm_wgrad(L, torch.zeros(6, 8, dtype=torch.bfloat16),
+                                       torch.zeros(12, 16, dtype=torch.bfloat16), out=torch.zeros(4, 16, 9)),
+     "out must have shape [4, 16, 8]"),
+    (lambda L: M.moe_expert_gemm_dgrad(L, torch.zeros(12, 16, dtype=torch.bfloat16),
+                                       torch.zeros(4, 15, 8, dtype=torch.bfloat16)), "weights must have shape [4, 16, *]"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(BAD_CALLS)))
+def test_binding_refuses_mismatched_tensors_before_the_library(case, no_library):
+    call, fragment = BAD_CALLS[case]
+    with pytest.raises(ValueError) as err:
+        call(fake_layout())
+    assert fragment in str(err.value)
+
+
+def test_binding_refuses_wrong_gate_and_layout_arguments(no_library):
+    with pytest.raises(ValueError, match="logits must be"):
+        M.moe_gate_topk(torch.zeros(4, 8, dtype=torch.float16), 2)
+    with pytest.raises(ValueError, match=r"idx_out must have shape \[4, 2\]"):
+        M.moe_gate_topk(torch.zeros(4, 8), 2, idx_out=torch.zeros(4, 3, dtype=torch.int32))
+    with pytest.raises(ValueError, match="grad_w must be"):
+        M.moe_gate_topk_backward(torch.zeros(4, 2, dtype=torch.int32), torch.zeros(4, 2),
+                                 torch.zeros(4, 2, dtype=torch.float64), 8)
+    with pytest.raises(ValueError, match="expert ids must be"):
+        M.moe_dispatch_layout(torch.zeros(4, 2, dtype=torch.int64), 8)
+    with pytest.raises(ValueError, match="workspace must be"):
+        M.moe_dispatch_layout(torch.zeros(4, 2, dtype=torch.int32), 8, workspace=torch.zeros(64))
+
+
+def test_binding_refuses_well_shaped_cpu_tensors(no_library):
+    """Right shapes and types on the host still stop before the library: no CPU path."""
+    with pytest.raises(ValueError, match="on the GPU"):
+        M.moe_dispatch(fake_layout(), torch.zeros(6, 8))
+    with pytest.raises(ValueError, match="on the GPU"):
+        M.moe_combine(fake_layout(), torch.zeros(12, 8), torch.zeros(6, 2))

@@ -4,26 +4,29 @@ activation-checkpoint layout recorder.
 Every forward and backward step calls the library's HIP kernels; these classes
 only wire them into autograd:
 
-    idx, w  = route(logits, k)                    # w carries a gradient to the logits
+    idx, w  = route(logits, k, rec)               # w carries a gradient to the logits
     buf, L  = dispatch(x, idx, e, capacity, rec)  # buf [L.rows, m]; grad -> x
     y       = combine(expert_out, w, L)           # grads -> expert_out and w
 
-The gradient of a combine is a dispatch and the gradient of a dispatch is a
-combine, both on the forward's layout (DeepSpeed PR "Add an opt-in DeepEP
-transport for the AutoEP expert all-to-all", first commit). The routing
-weights are an autograd output of the gate and an input of the combine, so
-their gradient reaches the router (same page, review-fix commit: returning no
-gradient for them silently stopped the gate from learning).
+Dispatch and combine are each other's adjoint, so the backward of one runs the
+other's kernel on the layout the forward built (DeepSpeed PR "Add an opt-in
+DeepEP transport for the AutoEP expert all-to-all", first commit). The routing
+weights are an autograd output of the gate and an input of the combine, so the
+router receives their gradient (same page, review-fix commit).
 
 LayoutRecorder follows NeMo Automodel PR "perf(moe): reuse the DeepEP dispatch
 layout on activation-checkpoint recompute", section 1 and its "How" part: one
-recorder per checkpointed call; the forward logs each dispatch's layout (and
-its routing) in call order; the recompute consumes them in the same order and
-replays the dispatch without rebuilding the layout; a recompute that outruns
-its log falls back to a full layout; the dispatched rows themselves are not
-kept, only routing metadata. With verify=True a replay compares the routing it
-is handed with the recorded one on the GPU, and check() raises if any differed
-(fail loudly rather than mis-route silently).
+recorder per checkpointed call. The forward logs, in call order, each gate's
+routing (expert ids and weights) and each dispatch's layout; only this routing
+metadata is kept, never the dispatched rows. The recompute consumes the log in
+the same order: the gate hands back the recorded routing instead of running
+top-k again (the router is bypassed, and the weights' gradient still reaches the
+logits through the recorded selection), and the dispatch replays the recorded
+layout without rebuilding it. The replayed layout therefore always meets the
+routing it was built from. A layout replayed for routing that did not come from
+the recorder's gate is verified on the GPU against the recorded routing, and the
+backward of that dispatch raises if they differ: a mis-route fails loudly
+instead of silently. A recompute that outruns its log builds afresh.
 """
 from __future__ import annotations
 
@@ -55,12 +58,51 @@ class _Gate(torch.autograd.Function):
         return moe_gate_topk_backward(idx, w, g_w.float().contiguous(), ctx.e), None
 
 
+class _GateReplay(torch.autograd.Function):
+    """The gate on a recompute, pinned to the forward's record: the recorded weights come
+    back as they are (top-k is not run again on the recomputed logits), and their
+    gradient reaches the logits through the recorded selection (the gate backward needs
+    only the ids and weights)."""
+
+    @staticmethod
+    def forward(ctx, logits, idx, w):
+        ctx.save_for_backward(idx, w)
+        ctx.e = logits.shape[1]
+        return w.clone()
+
+    @staticmethod
+    def backward(ctx, g_w):
+        idx, w = ctx.saved_tensors
+        return moe_gate_topk_backward(idx, w, g_w.float().contiguous(), ctx.e), None, None
+
+
+def _raise_on_replay_mismatch(layout: Layout) -> None:
+    """Raise if a replay of `layout` was handed routing that differs from the recorded one.
+
+    Inside a backward pass (where a checkpoint's recompute runs) the check is queued to
+    run when that pass ends, costing one synchronisation per backward; outside one it
+    runs at once."""
+
+    def check():
+        flags, _ = moe_layout_read(layout)  # synchronises
+        if flags & FLAG_REPLAY_MISMATCH:
+            raise RuntimeError("a checkpoint recompute replayed a dispatch layout for routing that "
+                               "differs from the forward's (route through the recorder to pin it)")
+
+    try:
+        torch.autograd.Variable._execution_engine.queue_callback(check)
+    except RuntimeError:  # not inside a backward pass
+        check()
+
+
 class _Dispatch(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x, layout, verify_idx):
         ctx.layout = layout
         if verify_idx is not None:
-            return moe_dispatch_replay(layout, x.contiguous(), verify_idx)
+            out = moe_dispatch_replay(layout, x.contiguous(), verify_idx)
+            _raise_on_replay_mismatch(layout)
+            return out
         return moe_dispatch(layout, x.contiguous())
 
     @staticmethod
@@ -153,31 +195,64 @@ class _ExpertLinear(torch.autograd.Function):
 
 
 class LayoutRecorder:
-    """Layouts of one checkpointed call, recorded on its forward, replayed on its recompute.
+    """Routing and layouts of one checkpointed call, recorded on its forward, replayed on
+    its recompute.
 
-    Enter it (``with rec:``) around each pass of the checkpointed function. The
-    first pass records; every later pass replays from the start of the log.
+    Enter it (``with rec:``) around each pass of the checkpointed function. The first
+    pass records; every later pass replays from the start of the log. `verify` (on by
+    default) checks a replayed layout against the routing the recompute hands it when
+    that routing did not come from this recorder's gate; the dispatch's backward then
+    raises on a mismatch.
     """
 
-    def __init__(self, verify: bool = False):
+    def __init__(self, verify: bool = True):
         self.verify = verify
         self.log: list[tuple[Layout, tuple]] = []
+        self.routes: list[tuple[torch.Tensor, torch.Tensor, int, int]] = []
         self.passes = 0
         self._cursor = 0
+        self._route_cursor = 0
         self._recording = True
         self.layouts_built = 0
         self.replays = 0
         self.fallbacks = 0
+        self.routes_replayed = 0
+        self.route_fallbacks = 0
         self._replayed: list[Layout] = []
 
     def __enter__(self):
         self._recording = self.passes == 0
         self._cursor = 0
+        self._route_cursor = 0
         return self
 
     def __exit__(self, *exc):
         self.passes += 1
         return False
+
+    def route_for(self, logits: torch.Tensor, k: int):
+        """Top-k ids and weights: computed and logged on the forward, the logged ones on a
+        recompute (with the weights' gradient routed to the recomputed logits)."""
+        s, e = logits.shape
+        if self._recording:
+            idx, w = _Gate.apply(logits, k)
+            self.routes.append((idx, w.detach(), e, k))
+            return idx, w
+        if self._route_cursor < len(self.routes):
+            idx, w, e_rec, k_rec = self.routes[self._route_cursor]
+            self._route_cursor += 1
+            if (s, e, k) != (idx.shape[0], e_rec, k_rec):
+                raise RuntimeError(f"recompute asked to route {(s, e, k)}, the forward recorded "
+                                   f"{(idx.shape[0], e_rec, k_rec)}")
+            self.routes_replayed += 1
+            return idx, _GateReplay.apply(logits, idx, w)
+        self.route_fallbacks += 1  # the recompute outran its log: route afresh
+        return _Gate.apply(logits, k)
+
+    def _pinned(self, idx: torch.Tensor) -> bool:
+        """Whether idx is routing this recorder's gate logged (and so the routing the
+        recorded layouts were built from)."""
+        return any(idx is r[0] for r in self.routes)
 
     def layout_for(self, idx: torch.Tensor, e: int, capacity: int, **options):
         """The layout to dispatch with, and the routing to verify a replay against."""
@@ -194,7 +269,8 @@ class LayoutRecorder:
                 raise RuntimeError(f"recompute asked for a layout of {key}, the forward recorded {rec_key}")
             self.replays += 1
             self._replayed.append(layout)
-            return layout, (idx.contiguous() if self.verify else None)
+            verify = self.verify and not self._pinned(idx)
+            return layout, (idx.contiguous() if verify else None)
         self.fallbacks += 1  # the recompute outran its log: build the layout afresh
         layout = moe_dispatch_layout(idx, e, capacity, **options)
         self.layouts_built += 1
@@ -208,8 +284,11 @@ class LayoutRecorder:
                 raise RuntimeError("a recompute replayed a layout with routing that differs from the forward's")
 
 
-def route(logits: torch.Tensor, k: int):
-    """Top-k expert ids (no gradient) and renormalised weights (gradient to the logits)."""
+def route(logits: torch.Tensor, k: int, recorder: LayoutRecorder | None = None):
+    """Top-k expert ids (no gradient) and renormalised weights (gradient to the logits);
+    with a recorder, logged on the forward and handed back unchanged on the recompute."""
+    if recorder is not None:
+        return recorder.route_for(logits, k)
     return _Gate.apply(logits, k)
 
 
@@ -263,7 +342,7 @@ def renormalize(w: torch.Tensor, layout: Layout):
     return _Renormalize.apply(w, layout)
 
 
-def checkpoint(fn, *args, verify: bool = False, **kwargs):
+def checkpoint(fn, *args, verify: bool = True, **kwargs):
     """torch.utils.checkpoint of fn(recorder, *args), with layouts replayed on recompute."""
     rec = LayoutRecorder(verify=verify)
 

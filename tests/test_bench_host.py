@@ -75,12 +75,28 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert res.stdout == ""
 
 
-def test_cold_pair_summary_adds_dispatch_and_combine_per_pair():
-    # three pairs of 100 + 110, 120 + 130 and 140 + 150 microseconds over 1.2e9 bytes:
-    # pairs of 210, 250 and 290 us, mean 250 us, so 4800 GB/s and 0.6 of 8 TB/s
-    s = bench.cold_pair_summary(8192, [100.0, 120.0, 140.0], [110.0, 130.0, 150.0], 1_200_000_000)
+def test_cold_pair_summary_quotes_the_median_pair():
+    # three pairs of 100 + 110, 120 + 130 and 200 + 200 microseconds over 1.2e9 bytes:
+    # pairs of 210, 250 and 400 us, median 250 us (the mean, 286.7, is not quoted), so
+    # 4800 GB/s and 0.6 of 8 TB/s; p10 = 210 + 0.2 * 40, p90 = 250 + 0.8 * 150
+    s = bench.cold_pair_summary(8192, [100.0, 120.0, 200.0], [110.0, 130.0, 200.0], 1_200_000_000)
     assert s["pairs"] == 3
-    assert s["us"] == 250.0 and s["us_median"] == 250.0 and s["us_min"] == 210.0
-    assert s["dispatch_us"] == 120.0 and s["combine_us"] == 130.0
+    assert s["us_median"] == 250.0 and s["us_min"] == 210.0 and s["us_mean"] == 286.67
+    assert s["us_p10"] == 218.0 and s["us_p90"] == 370.0
+    assert s["dispatch_us_median"] == 120.0 and s["combine_us_median"] == 130.0
     assert s["GBps"] == 4800.0 and s["frac_of_hbm_peak"] == 0.6
     assert s["tokens_per_s"] == round(8192 / 250e-6, 1)
+
+
+def test_expert_gemm_bytes_count_only_the_experts_that_receive_rows():
+    w = W.WORKLOADS["zipf_skew_h4096"]
+    K = w.s * w.k
+    row, wrow = w.m * 2, W.EXPERT_WIDTH * w.m * 2  # bf16: one token row, one expert's weights
+    all_e = bench.algorithmic_bytes(w, K, variant="expert_gemm")
+    some = bench.algorithmic_bytes(w, K, variant="expert_gemm", active_experts=43)
+    assert all_e["expert_gemm"] - some["expert_gemm"] == (w.e - 43) * wrow
+    assert all_e["expert_gemm_dgrad"] - some["expert_gemm_dgrad"] == (w.e - 43) * wrow
+    # x once, 43 experts' weights once, [rows, n] output and its row map
+    assert some["expert_gemm"] == w.s * row + 43 * wrow + K * W.EXPERT_WIDTH * 2 + K * 4
+    # the weight gradient writes every expert's (zeros for the idle ones)
+    assert all_e["expert_gemm_wgrad"] == some["expert_gemm_wgrad"]

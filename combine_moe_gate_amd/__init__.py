@@ -104,11 +104,13 @@ _SIGNATURES = {
     "moe_dispatch_backward": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _I, ctypes.c_int,
                                              _P, _P]),
     "moe_layout_read": (ctypes.c_int, [ctypes.POINTER(LayoutStruct), _P, _P, _P]),
+    "moe_dispatch_layout_static_scratch": (ctypes.c_int, [_P, _I, _I, _I, _I, ctypes.POINTER(LayoutOptions), _P,
+                                                          ctypes.c_size_t, ctypes.POINTER(LayoutStruct), _P]),
 }
 EXPORTS = tuple(_SIGNATURES)
 
 
-ABI_VERSION = 5  # MOE_ABI_VERSION of include/moe_gate.h that _SIGNATURES follows
+ABI_VERSION = 6  # MOE_ABI_VERSION of include/moe_gate.h that _SIGNATURES follows
 
 
 def lib() -> ctypes.CDLL:

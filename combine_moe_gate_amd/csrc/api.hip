@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/moe_gate.h"
@@ -45,12 +46,14 @@ size_t elem_bytes(moe_dtype_t dt) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Sizes of a layout, and where each of its arrays sits in the workspace.
+// The handle's arrays come first; the tile tables, which only the layout build itself
+// uses, last, so that `handle_bytes` is the share a handle needs once it is built.
 struct Plan {
   int64_t rows = 0;
   int32_t ntiles = 0;
   size_t off_counts = 0, off_kept = 0, off_offsets = 0, off_dst = 0, off_src = 0,
          off_route = 0, off_checksum = 0, off_flags = 0, off_tile_counts = 0,
-         off_tile_checksum = 0, off_tile_flags = 0, bytes = 0;
+         off_tile_checksum = 0, off_tile_flags = 0, handle_bytes = 0, bytes = 0;
 };
 
 size_t take(size_t& cursor, size_t nbytes) {
@@ -119,6 +122,7 @@ Plan make_plan(int32_t s, int32_t e, int32_t k, int32_t capacity, const Options&
   p.off_route = take(cur, sizeof(int32_t) * routes);
   p.off_checksum = take(cur, sizeof(uint64_t));
   p.off_flags = take(cur, sizeof(int32_t));
+  p.handle_bytes = (cur + kAlign - 1) / kAlign * kAlign;
   p.off_tile_counts = take(cur, sizeof(int32_t) * static_cast<size_t>(moe::tile_row_length(p.ntiles)) * e);
   p.off_tile_checksum = take(cur, sizeof(uint64_t) * static_cast<size_t>(p.ntiles));
   p.off_tile_flags = take(cur, sizeof(int32_t) * static_cast<size_t>(p.ntiles));
@@ -138,7 +142,7 @@ moe_status_t view_of(const moe_layout_t* h, moe::LayoutView* v) {
   st = read_options(&o, h->s, h->e, h->k, h->capacity, &opt);
   if (st != MOE_OK) return fail(MOE_ERR_HANDLE_MISMATCH, "layout options invalid: %s", g_last_error.c_str());
   const Plan p = make_plan(h->s, h->e, h->k, h->capacity, opt);
-  if (h->rows != p.rows || h->workspace == nullptr || h->workspace_bytes < p.bytes)
+  if (h->rows != p.rows || h->workspace == nullptr || h->workspace_bytes < p.handle_bytes)
     return fail(MOE_ERR_HANDLE_MISMATCH, "layout fields are inconsistent with its sizes");
   char* ws = static_cast<char*>(h->workspace);
   if (reinterpret_cast<char*>(h->dst) != ws + p.off_dst ||
@@ -161,9 +165,12 @@ moe_status_t view_of(const moe_layout_t* h, moe::LayoutView* v) {
   v->route_idx = reinterpret_cast<int32_t*>(ws + p.off_route);
   v->checksum = reinterpret_cast<uint64_t*>(ws + p.off_checksum);
   v->flags = reinterpret_cast<int32_t*>(ws + p.off_flags);
-  v->tile_counts = reinterpret_cast<int32_t*>(ws + p.off_tile_counts);
-  v->tile_checksum = reinterpret_cast<uint64_t*>(ws + p.off_tile_checksum);
-  v->tile_flags = reinterpret_cast<int32_t*>(ws + p.off_tile_flags);
+  // the tile tables are in the workspace only if it was sized for them (a layout built
+  // with moe_dispatch_layout_static_scratch had them elsewhere); only a build uses them
+  const bool tables = h->workspace_bytes >= p.bytes;
+  v->tile_counts = tables ? reinterpret_cast<int32_t*>(ws + p.off_tile_counts) : nullptr;
+  v->tile_checksum = tables ? reinterpret_cast<uint64_t*>(ws + p.off_tile_checksum) : nullptr;
+  v->tile_flags = tables ? reinterpret_cast<int32_t*>(ws + p.off_tile_flags) : nullptr;
   return MOE_OK;
 }
 
@@ -193,6 +200,48 @@ moe_status_t check_array(const void* p, int64_t n_rows, const char* name, bool r
     const moe_status_t st_ = (expr);       \
     if (st_ != MOE_OK) return st_;         \
   } while (0)
+
+// ---------------------------------------------------------------------------------
+// Static scratch for moe_dispatch_layout_static_scratch: the layout's tile tables in a
+// device array of the library's own, for callers that cannot allocate.
+
+constexpr size_t kStaticScratchBytes = static_cast<size_t>(2) << 20;  // 2 MiB per GPU
+constexpr int kMaxDevices = 64;
+
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+}  // namespace
+
+// One copy per GPU the library's code is loaded on, held until the process ends. On the
+// host, `scratch` names only a stand-in: host code uses the device address that
+// scratch_address() looks up, never the name.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+// The current device's address of `scratch`, looked up once per device with that device
+// current (each GPU holds its own copy at its own address), then kept.
+moe_status_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return hip_status(err, "moe_dispatch_layout_static_scratch: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "device %d is beyond the %d devices the static scratch tracks",
+                dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess)
+      return hip_status(err, "moe_dispatch_layout_static_scratch: hipGetSymbolAddress(scratch)");
+    if (p == nullptr)
+      return fail(MOE_ERR_HIP, "moe_dispatch_layout_static_scratch: hipGetSymbolAddress gave NULL");
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return MOE_OK;
+}
 
 }  // namespace
 
@@ -263,10 +312,13 @@ moe_status_t moe_dispatch_layout(const int32_t* topk_idx, int32_t s, int32_t e, 
                                 layout, stream);
 }
 
-moe_status_t moe_dispatch_layout_ex(const int32_t* topk_idx, int32_t s, int32_t e, int32_t k,
-                                    int32_t capacity, const moe_layout_options_t* options,
-                                    void* workspace, size_t workspace_bytes,
-                                    moe_layout_t* layout, void* stream) {
+// Checks, fills the handle and launches the layout build. The tile tables go to
+// `tables` if given (the static scratch array: the workspace then needs only the
+// handle's share), else to the workspace's own tile region.
+static moe_status_t build_layout(const int32_t* topk_idx, int32_t s, int32_t e, int32_t k,
+                                 int32_t capacity, const moe_layout_options_t* options,
+                                 void* workspace, size_t workspace_bytes, moe_layout_t* layout,
+                                 void* stream, bool static_tables, const char* what) {
   if (capacity < 0) capacity = 0;
   MOE_TRY(check_sizes(s, e, k, capacity));
   Options opt;
@@ -277,9 +329,21 @@ moe_status_t moe_dispatch_layout_ex(const int32_t* topk_idx, int32_t s, int32_t 
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
     return fail(MOE_ERR_MISALIGNED, "workspace is not %zu-byte aligned", kAlign);
   const Plan p = make_plan(s, e, k, capacity, opt);
-  if (workspace_bytes < p.bytes)
-    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, the layout needs %zu",
-                workspace_bytes, p.bytes);
+  const size_t need = static_tables ? p.handle_bytes : p.bytes;
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, the layout needs %zu", workspace_bytes, need);
+  char* tables = nullptr;
+  if (static_tables) {
+    const size_t table_bytes = p.bytes - p.handle_bytes;
+    if (table_bytes > kStaticScratchBytes)
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "%s: the layout's tile tables need %zu bytes, more than the %zu of the static "
+                  "scratch array (fewer tokens or experts per call, or moe_dispatch_layout_ex)",
+                  what, table_bytes, kStaticScratchBytes);
+    void* base = nullptr;
+    MOE_TRY(scratch_address(&base));
+    tables = static_cast<char*>(base);
+  }
 
   char* ws = static_cast<char*>(workspace);
   moe_layout_t h;
@@ -300,16 +364,38 @@ moe_status_t moe_dispatch_layout_ex(const int32_t* topk_idx, int32_t s, int32_t 
   h.route_idx = reinterpret_cast<int32_t*>(ws + p.off_route);
   h.checksum = reinterpret_cast<uint64_t*>(ws + p.off_checksum);
   h.flags = reinterpret_cast<int32_t*>(ws + p.off_flags);
-  h.scratch = ws + p.off_tile_counts;
+  h.scratch = static_tables ? nullptr : ws + p.off_tile_counts;
   h.workspace = workspace;
   h.workspace_bytes = workspace_bytes;
 
   moe::LayoutView v;
   MOE_TRY(view_of(&h, &v));
-  const moe_status_t st = hip_status(
-      moe::launch_layout(topk_idx, v, static_cast<hipStream_t>(stream)), "moe_dispatch_layout");
+  if (static_tables) {  // same offsets within the tables as in a full workspace
+    v.tile_counts = reinterpret_cast<int32_t*>(tables + (p.off_tile_counts - p.handle_bytes));
+    v.tile_checksum = reinterpret_cast<uint64_t*>(tables + (p.off_tile_checksum - p.handle_bytes));
+    v.tile_flags = reinterpret_cast<int32_t*>(tables + (p.off_tile_flags - p.handle_bytes));
+  }
+  const moe_status_t st =
+      hip_status(moe::launch_layout(topk_idx, v, static_cast<hipStream_t>(stream)), what);
   if (st == MOE_OK) *layout = h;
   return st;
+}
+
+moe_status_t moe_dispatch_layout_ex(const int32_t* topk_idx, int32_t s, int32_t e, int32_t k,
+                                    int32_t capacity, const moe_layout_options_t* options,
+                                    void* workspace, size_t workspace_bytes,
+                                    moe_layout_t* layout, void* stream) {
+  return build_layout(topk_idx, s, e, k, capacity, options, workspace, workspace_bytes, layout,
+                      stream, false, "moe_dispatch_layout");
+}
+
+moe_status_t moe_dispatch_layout_static_scratch(const int32_t* topk_idx, int32_t s, int32_t e,
+                                                int32_t k, int32_t capacity,
+                                                const moe_layout_options_t* options,
+                                                void* workspace, size_t workspace_bytes,
+                                                moe_layout_t* layout, void* stream) {
+  return build_layout(topk_idx, s, e, k, capacity, options, workspace, workspace_bytes, layout,
+                      stream, true, "moe_dispatch_layout_static_scratch");
 }
 
 static moe_status_t dispatch_common(const moe_layout_t* layout, const int32_t* verify_idx,

@@ -30,7 +30,8 @@
  * Conventions for every call:
  *   - All array arguments are DEVICE pointers unless stated otherwise. The caller owns
  *     every buffer, including the layout workspace; the library allocates nothing and
- *     keeps no device state between calls.
+ *     keeps no device state between calls, apart from the static scratch array of
+ *     moe_dispatch_layout_static_scratch (a fixed size per GPU, never allocated).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Every call
  *     that takes a stream only enqueues work on it and returns without waiting, except
  *     moe_layout_read, which synchronises the stream.
@@ -59,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -214,6 +215,42 @@ moe_status_t moe_dispatch_layout_ex(const int32_t* topk_idx, int32_t s, int32_t 
                                     int32_t capacity, const moe_layout_options_t* options,
                                     void* workspace, size_t workspace_bytes,
                                     moe_layout_t* layout, void* stream);
+
+/*
+ * Dispatch layout that allocates nothing and needs no scratch from the caller: for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation). The same contract and results as
+ * moe_dispatch_layout_ex, bit for bit, except where the tile tables live that only the
+ * layout build itself uses (per-tile expert counts, checksums and flags): in a static
+ * device array of the library, MOE_STATIC_SCRATCH_BYTES per GPU, held by each GPU the
+ * library runs on until the process ends.
+ *   workspace  as for moe_dispatch_layout_ex, but only the handle's arrays live in it:
+ *              at least MOE_LAYOUT_HANDLE_BYTES(s, e, k, rows) bytes (the regions
+ *              counts[e], kept[e], offsets[e+1], dst[s*k], src[rows], route copy[s*k]
+ *              int32, checksum u64 and flags i32, each starting on a 256-byte
+ *              boundary; rows = e*capacity, or s*k + e*(pad_multiple-1) dropless);
+ *              moe_layout_workspace_bytes_ex is always enough. The handle it fills is
+ *              used by every other call exactly like one from moe_dispatch_layout_ex.
+ *   MOE_ERR_UNSUPPORTED if the tile tables of (s, e, k, options) exceed the static array
+ *   (about 4 bytes per expert per 256 tokens, 256 routes route-major: e = 128 covers a
+ *   million tokens); MOE_ERR_WORKSPACE if the workspace is below the handle's share.
+ * The first call on a device looks up its copy of the array; later calls reuse it. No
+ * allocation, no memset: every table entry the build reads it wrote earlier in the same
+ * call. All calls on one GPU share its array, so two of these builds enqueued on
+ * different streams of one GPU that overlap in time race; builds on one stream, and
+ * every other entry point, are unaffected. The stream must belong to the current device.
+ */
+#define MOE_STATIC_SCRATCH_BYTES (2u << 20)
+#define MOE_LAYOUT_ALIGN_UP(n) ((((size_t)(n)) + 255u) / 256u * 256u)
+#define MOE_LAYOUT_HANDLE_BYTES(s, e, k, rows)                                               \
+  (2 * MOE_LAYOUT_ALIGN_UP(4 * (size_t)(e)) + MOE_LAYOUT_ALIGN_UP(4 * ((size_t)(e) + 1)) +   \
+   2 * MOE_LAYOUT_ALIGN_UP(4 * (size_t)(s) * (size_t)(k)) + MOE_LAYOUT_ALIGN_UP(4 * (size_t)(rows)) + \
+   MOE_LAYOUT_ALIGN_UP(8) + MOE_LAYOUT_ALIGN_UP(4))
+moe_status_t moe_dispatch_layout_static_scratch(const int32_t* topk_idx, int32_t s, int32_t e,
+                                                int32_t k, int32_t capacity,
+                                                const moe_layout_options_t* options,
+                                                void* workspace, size_t workspace_bytes,
+                                                moe_layout_t* layout, void* stream);
 
 /*
  * (3) Dispatch ([DS-8195] part 3; [DS-8213] first commit): out[dst[t,j]] = x[t] for every

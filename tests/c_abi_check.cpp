@@ -14,6 +14,8 @@
 //             output, grad_w[t,j] is exactly sum_m x[t,m]^2 (integers); the gate gradient
 //             is zero off the selection and sums to zero over it (softmax Jacobian);
 //   replay    byte-identical to the dispatch; a changed route sets the mismatch flag;
+//   static    the layout built with its tile tables in the library's static scratch
+//             array, in a workspace of the handle's share only, equals the other;
 //   options, variants and the grouped expert GEMM: see run_variants_case;
 //   errors    bad arguments return their status and a message, enqueueing nothing.
 // Prints "c_abi_check: ok" and exits 0, or lists the failures and exits 1.
@@ -168,6 +170,34 @@ static void run_case(int s, int e, int k, int m, int cap, uint64_t seed, hipStre
   int32_t flags = -1;
   MOE_OK_(moe_layout_read(&L, &flags, nullptr, st));
   CHECK(flags == 0, "flags %d on valid routing", flags);
+
+  // the same layout with its tile tables in the library's static scratch array, in a
+  // workspace of only the handle's share: the same arrays, flags and checksum
+  {
+    const size_t hb = MOE_LAYOUT_HANDLE_BYTES(s, e, k, rows);
+    CHECK(hb <= ws_bytes, "handle share %zu above the workspace size %zu", hb, ws_bytes);
+    Dev<unsigned char> ws2(hb);
+    moe_layout_t L2;
+    MOE_OK_(moe_dispatch_layout_static_scratch(d_idx.p, s, e, k, cap, nullptr, ws2.p, hb, &L2, st));
+    CHECK(L2.rows == rows, "static-scratch layout rows %lld", static_cast<long long>(L2.rows));
+    HIP_OK(hipStreamSynchronize(st));
+    auto fetch = [](const int32_t* p, size_t n) {
+      std::vector<int32_t> h(n);
+      if (n) HIP_OK(hipMemcpy(h.data(), p, n * sizeof(int32_t), hipMemcpyDeviceToHost));
+      return h;
+    };
+    CHECK(fetch(L2.counts, e) == counts && fetch(L2.kept, e) == kept && fetch(L2.offsets, e + 1) == offsets,
+          "static-scratch layout: counts, kept or offsets differ");
+    CHECK(fetch(L2.dst, dst.size()) == dst && fetch(L2.src, src.size()) == src,
+          "static-scratch layout: dst or src differ");
+    CHECK(fetch(L2.route_idx, idx.size()) == idx, "static-scratch layout: routing copy differs");
+    int32_t f2 = -1;
+    uint64_t c1 = 0, c2 = 1;
+    MOE_OK_(moe_layout_read(&L, nullptr, &c1, st));
+    MOE_OK_(moe_layout_read(&L2, &f2, &c2, st));
+    CHECK(f2 == 0 && c1 == c2, "static-scratch layout: flags %d, checksum %llu vs %llu", f2,
+          static_cast<unsigned long long>(c2), static_cast<unsigned long long>(c1));
+  }
 
   std::vector<int32_t> seen(e, 0), placed_of_token(s, 0);
   std::vector<int> row_refs(static_cast<size_t>(rows), 0);

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_abi_version_and_status_names(lib):
     header = open(os.path.join(os.path.dirname(__file__), "..", "include", "moe_gate.h")).read()
     declared = int(re.search(r"#define MOE_ABI_VERSION (\d+)", header).group(1))
-    assert lib.moe_abi_version() == declared == M.ABI_VERSION == 5
+    assert lib.moe_abi_version() == declared == M.ABI_VERSION == 6
     for code, name in M.STATUS_NAMES.items():
         assert lib.moe_status_string(code).decode() == name
     assert lib.moe_status_string(99).decode() == "MOE_STATUS_UNKNOWN"
@@ -110,6 +110,29 @@ def test_layout_argument_checks(lib):
     bad = M.LayoutOptions(2, 1)
     assert lib.moe_dispatch_layout_ex(FAKE, 100, 8, 2, 0, ctypes.byref(bad), FAKE, need,
                                       ctypes.byref(st), None) == 1
+    assert st.magic == 0
+
+
+@no_gpu_only
+def test_static_scratch_layout_argument_checks(lib):
+    """The layout that keeps its tile tables in the library's static array needs only the
+    handle's share of a workspace, and refuses sizes whose tables exceed the array, both
+    before touching the device."""
+    st = M.LayoutStruct()
+
+    def handle_bytes(s, e, k, rows):
+        a = lambda n: (n + 255) // 256 * 256
+        return 2 * a(4 * e) + a(4 * (e + 1)) + 2 * a(4 * s * k) + a(4 * rows) + a(8) + a(4)
+
+    need = handle_bytes(100, 8, 2, 200)
+    assert need < M.workspace_bytes(100, 8, 2, 0)
+    f = lib.moe_dispatch_layout_static_scratch
+    assert f(FAKE, 100, 8, 2, 0, None, FAKE, need - 1, ctypes.byref(st), None) == 3
+    assert "workspace" in lib.moe_last_error().decode()
+    assert f(FAKE, 200000, 1024, 1, 0, None, FAKE, 1 << 30, ctypes.byref(st), None) == 2
+    assert "static scratch" in lib.moe_last_error().decode()
+    assert f(FAKE, 100, 8, 9, 0, None, FAKE, need, ctypes.byref(st), None) == 1  # k > e
+    assert f(FAKE, 100, 8, 2, 0, None, None, need, ctypes.byref(st), None) == 1
     assert st.magic == 0
 
 

@@ -50,6 +50,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 COLD_FLUSH_MIB = 1024
 COLD_PAIRS = 100
 COLD_WARMUP = 10
+ISOLATED_RUNS = 30  # each op of the step alone after a flush
 
 
 def kernel_source_digest() -> str:
@@ -367,6 +368,23 @@ def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None, 
                 per_op["_cold_dispatch"].append(a.elapsed_time(b) * 1e3)
                 per_op["_cold_combine"].append(b.elapsed_time(c) * 1e3)
         del flush
+    if flush_mib == 0 and variant != "expert_gemm":
+        # each op of the step alone, after a 1 GiB read of scratch outside its events (the
+        # per-kernel form of the cold pair: no op pays for lines an earlier op left dirty)
+        flush = torch.zeros((COLD_FLUSH_MIB << 20) // 4, dtype=torch.float32, device=dev)
+        for op, fn in ops:
+            key = "_isolated_" + op
+            per_op[key] = []
+            for i in range(COLD_WARMUP + ISOLATED_RUNS):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                flush.sum()
+                a.record()
+                fn()
+                b.record()
+                torch.cuda.synchronize()
+                if i >= COLD_WARMUP:
+                    per_op[key].append(a.elapsed_time(b) * 1e3)
+        del flush
     for op, fn in extra.get("unfused", []) + extra.get("layer", []):  # outside the timed step
         per_op[op] = []
         fn()  # the first call sets up the autograd graph and allocator
@@ -628,6 +646,7 @@ def main():
                                                             "_torch_grouped_mm_input_grad",
                                                             "_torch_grouped_mm_weight_grad")
                     if name in per_op}
+    isolated = {name[len("_isolated_"):]: per_op.pop(name) for name in list(per_op) if name.startswith("_isolated_")}
     ops = list(per_op)
     kernels = {}
     for op in ops:
@@ -654,6 +673,19 @@ def main():
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
                 "traffic": measured_traffic(w.name, args.variant).get(dominant),
                 "algorithmic_bytes": abytes[dominant]}
+    kernels_isolated = {}
+    for op, us_list in isolated.items():
+        med = float(np.median(us_list))
+        kernels_isolated[op] = {"us_median": round(med, 2), "us_p10": round(float(np.percentile(us_list, 10)), 2),
+                                "us_p90": round(float(np.percentile(us_list, 90)), 2),
+                                "GBps": round(abytes[op] / med / 1e3, 1),
+                                "frac_of_hbm_peak": round(abytes[op] / med / 1e3 / HBM_PEAK_GBPS, 4)}
+    if dominant in kernels_isolated:
+        roofline["isolated"] = {
+            "what": f"the same kernel alone, each of {ISOLATED_RUNS} runs after a {COLD_FLUSH_MIB} MiB read of "
+                    "scratch (median); in the step it also pays for evicting lines earlier kernels left dirty",
+            "achieved": kernels_isolated[dominant]["GBps"], "frac": kernels_isolated[dominant]["frac_of_hbm_peak"],
+            "us_median": kernels_isolated[dominant]["us_median"]}
     if args.variant == "expert_gemm":
         flops = 2 * kept * W.EXPERT_WIDTH * w.m
         for op in ("expert_gemm", "expert_gemm_unfused", "expert_gemm_wgrad", "expert_gemm_wgrad_narrow",
@@ -735,6 +767,7 @@ def main():
             "tokens_per_s": round(w.s / (float(np.mean(layer_us)) / 1e6), 1),
             "gemm_TFLOPs": round(3 * 2 * kept * W.EXPERT_WIDTH * w.m / float(np.mean(layer_us)) / 1e6, 1)},
         "kernels": kernels,
+        "kernels_isolated": kernels_isolated or None,
         "kept_routes": kept,
     }
     if not args.no_cpu_baseline:

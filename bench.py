@@ -53,12 +53,19 @@ COLD_WARMUP = 10
 ISOLATED_RUNS = 30  # each op of the step alone after a flush
 
 
-def kernel_source_digest() -> str:
-    """sha256 over the HIP sources and build flags the library is compiled from."""
+# sources of the grouped expert GEMM: only the expert_gemm variant runs their kernels
+GEMM_SOURCES = ("gemm.hip", "gemm_bwd.hip", "gemm_common.h")
+
+
+def kernel_source_digest(variant: str | None = None) -> str:
+    """sha256 over the HIP sources (and build flags) whose kernels a run of `variant`
+    launches: every source for the expert_gemm variant, all but the GEMM's otherwise."""
     import hashlib
     from combine_moe_gate_amd import _build
     h = hashlib.sha256()
     for path in sorted(_build.SOURCES + _build.HEADERS):
+        if variant != "expert_gemm" and os.path.basename(path) in GEMM_SOURCES:
+            continue
         with open(path, "rb") as f:
             h.update(f.read())
     h.update(" ".join(_build.FLAGS).encode())
@@ -79,7 +86,7 @@ def measured_traffic(workload: str, variant: str | None = None) -> dict:
                 traffic[parts[1]] = int(parts[2])
             elif len(parts) == 2 and parts[0] == "source_digest":
                 digest = parts[1]
-    return traffic if digest == kernel_source_digest() else {}
+    return traffic if digest == kernel_source_digest(variant) else {}
 
 
 def algorithmic_bytes(w: W.Workload, kept_routes: int, rows: int | None = None,
@@ -168,7 +175,8 @@ def to_dev(a, dtype, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None, flush_mib: int = 0):
+def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None, flush_mib: int = 0,
+            cold_pairs: int = COLD_PAIRS, isolated_runs: int = ISOLATED_RUNS):
     import torch
 
     import combine_moe_gate_amd as M
@@ -325,6 +333,15 @@ def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None, 
         for j, op in enumerate(names):
             per_op[op].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)  # microseconds
     if flush_mib == 0:
+        # the same eager step without the per-op events (only one event pair around all the
+        # steps): on launch-bound batches the events' own host time stretches the step
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            step()
+        b.record()
+        torch.cuda.synchronize()
+        per_op["_plain_step"] = [a.elapsed_time(b) * 1e3 / steps]
         # the same step captured once in a HIP graph and replayed, outside the timed region:
         # the host then launches one graph instead of each kernel (the path has no memsets,
         # allocations or host syncs, so it captures as it is)
@@ -355,7 +372,7 @@ def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None, 
         dsp = next(fn for op, fn in ops if op == "dispatch")
         cmb = next(fn for op, fn in ops if op == "combine")
         per_op["_cold_dispatch"], per_op["_cold_combine"] = [], []
-        for i in range(COLD_WARMUP + max(COLD_PAIRS, steps)):
+        for i in range(COLD_WARMUP + cold_pairs):
             a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
             flush.sum()
             a.record()
@@ -368,14 +385,14 @@ def run_gpu(w: W.Workload, steps: int, warmup: int, variant: str | None = None, 
                 per_op["_cold_dispatch"].append(a.elapsed_time(b) * 1e3)
                 per_op["_cold_combine"].append(b.elapsed_time(c) * 1e3)
         del flush
-    if flush_mib == 0 and variant != "expert_gemm":
+    if flush_mib == 0 and variant != "expert_gemm" and isolated_runs > 0:
         # each op of the step alone, after a 1 GiB read of scratch outside its events (the
         # per-kernel form of the cold pair: no op pays for lines an earlier op left dirty)
         flush = torch.zeros((COLD_FLUSH_MIB << 20) // 4, dtype=torch.float32, device=dev)
         for op, fn in ops:
             key = "_isolated_" + op
             per_op[key] = []
-            for i in range(COLD_WARMUP + ISOLATED_RUNS):
+            for i in range(COLD_WARMUP + isolated_runs):
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 flush.sum()
                 a.record()
@@ -615,6 +632,10 @@ def main():
     ap.add_argument("--flush-mib", type=int, default=0, metavar="MIB",
                     help="cold caches: read MIB MiB of scratch before each timed step, outside its "
                          "events (the step time is then summed from the events, without the flushes)")
+    ap.add_argument("--cold-pairs", type=int, default=None, metavar="N",
+                    help=f"timed cold-cache dispatch + combine pairs (default max({COLD_PAIRS}, --steps))")
+    ap.add_argument("--isolated-runs", type=int, default=ISOLATED_RUNS, metavar="N",
+                    help="runs of each op alone after a flush (0: none; short profiled runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run one plain device-to-device copy of MIB MiB "
                          "(a known-size reference for hardware memory counters)")
@@ -625,7 +646,11 @@ def main():
         sys.exit(2)
 
     w = W.WORKLOADS[args.workload]
-    elapsed, per_op, kept, rows, active = run_gpu(w, args.steps, args.warmup, args.variant, args.flush_mib)
+    cold_pairs = args.cold_pairs if args.cold_pairs is not None else max(COLD_PAIRS, args.steps)
+    if cold_pairs < 1:
+        ap.error("--cold-pairs must be at least 1")
+    elapsed, per_op, kept, rows, active = run_gpu(w, args.steps, args.warmup, args.variant, args.flush_mib,
+                                                  cold_pairs, args.isolated_runs)
     if args.calibrate_copy > 0:
         import torch
         src = torch.ones(args.calibrate_copy << 20, dtype=torch.uint8, device="cuda:0")
@@ -639,6 +664,7 @@ def main():
     copy_us = per_op.pop("_copy_reference")
     layer_us = per_op.pop("layer_train_step", None)
     graph_us = per_op.pop("_graph_step", None)
+    plain_us = per_op.pop("_plain_step", None)
     cold_d, cold_c = per_op.pop("_cold_dispatch", None), per_op.pop("_cold_combine", None)
     cold_d = None if not cold_d else cold_d
     dense_us = per_op.pop("_dense_gemm_reference", None)
@@ -682,7 +708,7 @@ def main():
                                 "frac_of_hbm_peak": round(abytes[op] / med / 1e3 / HBM_PEAK_GBPS, 4)}
     if dominant in kernels_isolated:
         roofline["isolated"] = {
-            "what": f"the same kernel alone, each of {ISOLATED_RUNS} runs after a {COLD_FLUSH_MIB} MiB read of "
+            "what": f"the same kernel alone, each of {args.isolated_runs} runs after a {COLD_FLUSH_MIB} MiB read of "
                     "scratch (median); in the step it also pays for evicting lines earlier kernels left dirty",
             "achieved": kernels_isolated[dominant]["GBps"], "frac": kernels_isolated[dominant]["frac_of_hbm_peak"],
             "us_median": kernels_isolated[dominant]["us_median"]}
@@ -755,6 +781,10 @@ def main():
             **{name: {"us": round(float(np.mean(v)), 2),
                       "TFLOPs": round(2 * kept * W.EXPERT_WIDTH * w.m / float(np.mean(v)) / 1e6, 1)}
                for name, v in grouped_refs.items()}},
+        "plain_step": None if plain_us is None else {
+            "what": "the same eager step, each kernel launched from Python as in the timed steps, but with one "
+                    "event pair around all the steps instead of events around each op",
+            "us": round(plain_us[0], 2), "tokens_per_s": round(w.s / (plain_us[0] / 1e6), 1)},
         "graph_step": None if graph_us is None else {
             "what": "the same step captured once in a HIP graph and replayed (HIP events per replay)",
             "us": round(float(np.mean(graph_us)), 2), "us_median": round(float(np.median(graph_us)), 2),

@@ -140,8 +140,13 @@ def _check(status: int) -> None:
         raise MoeError(status, lib().moe_last_error().decode())
 
 
-def _stream(t: torch.Tensor):
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+if hasattr(torch._C, "_cuda_getCurrentRawStream"):
+    def _stream(t: torch.Tensor):
+        """The current HIP stream of t's device, as the library takes it (void*)."""
+        return ctypes.c_void_p(torch._C._cuda_getCurrentRawStream(t.get_device()))
+else:  # older torch: the public (slower) route
+    def _stream(t: torch.Tensor):
+        return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
 def _ptr(t):
@@ -158,19 +163,26 @@ def _require_gpu(*tensors):
 
 def _expect(t, name: str, shape, dtype=None):
     """Check a tensor argument before any pointer reaches the library: its shape (None
-    matches any size in that place) and element type. The C ABI receives bare pointers
-    and cannot tell a short or mistyped buffer from a right one."""
+    matches any size in that place) and element type (one, or a tuple of allowed ones).
+    The C ABI receives bare pointers and cannot tell a short or mistyped buffer from a
+    right one."""
     if t is None:
         return
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
-    if t.dim() != len(shape) or any(want is not None and got != want for got, want in zip(t.shape, shape)):
+    got = t.shape
+    ok = len(got) == len(shape)
+    if ok:
+        for g, want in zip(got, shape):
+            if want is not None and g != want:
+                ok = False
+                break
+    if not ok:
         want = "[" + ", ".join("*" if d is None else str(d) for d in shape) + "]"
-        raise ValueError(f"{name} must have shape {want}, got {list(t.shape)}")
-    if dtype is not None:
-        allowed = dtype if isinstance(dtype, tuple) else (dtype,)
-        if t.dtype not in allowed:
-            raise ValueError(f"{name} must be {' or '.join(str(d) for d in allowed)}, got {t.dtype}")
+        raise ValueError(f"{name} must have shape {want}, got {list(got)}")
+    if dtype is not None and t.dtype is not dtype and (type(dtype) is not tuple or t.dtype not in dtype):
+        allowed = dtype if type(dtype) is tuple else (dtype,)
+        raise ValueError(f"{name} must be {' or '.join(str(d) for d in allowed)}, got {t.dtype}")
 
 
 _ROW_DTYPES = tuple(_DTYPE_CODE)

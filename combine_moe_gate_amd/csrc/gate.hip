@@ -1,6 +1,6 @@
 // Top-k gate and its backward on gfx950.
 //
-// One wave64 per token. The e logits of a row sit in registers, ceil(e/64) per lane,
+// The gate: one wave64 per token. The e logits of a row sit in registers, ceil(e/64) per lane,
 // as 32-bit order-preserving images of the float32 values (element i at lane i mod 64,
 // slot i / 64). Each of the k rounds takes the wave-wide maximum of the untaken keys
 // (DPP max steps plus four readlanes), then finds the lowest expert id holding it with
@@ -10,7 +10,11 @@
 // the full softmax renormalised over the selection: the full denominator cancels) --
 // DeepSpeed PR "MoE dispatch: fix silent Tutel + TP corruption, speed up native and
 // Tutel paths", part 1: the gate hands on per-route expert ids and gate values, not a
-// dense mask.
+// dense mask. (A 16-lane-row form with four tokens per wave, as the backward below uses,
+// measured slower here: its k selection rounds are long dependent chains within a wave,
+// while the wave-per-token grid fits on the chip at once.)
+//
+// The backward: one DPP row of 16 lanes per token for e <= 256 (a wave per token beyond).
 #include "internal.h"
 #include "moe_device.h"
 
@@ -126,6 +130,52 @@ __global__ __launch_bounds__(kBlock) void gate_topk_backward_kernel(
   }
 }
 
+// The gate backward with one DPP row per token (four tokens per wave), for e <= 256: the
+// row's lanes j < k hold route j; every lane gets all k (id, contribution) pairs from
+// its row and writes its experts' entries (r, r + 16, ...: 64 contiguous bytes per row
+// and store), summing repeated ids in route order.
+template <int VPR>
+__global__ __launch_bounds__(kBlock) void gate_topk_row_backward_kernel(
+    const int32_t* __restrict__ idx, const float* __restrict__ w, const float* __restrict__ gw,
+    int s, int e, int k, float* __restrict__ gl) {
+  const int lane = lane_id();
+  const int r = lane & 15;
+  const int base = lane & ~15;
+  const int t = (blockIdx.x * kWavesPerBlock + wave_in_block()) * 4 + (lane >> 4);
+  const bool live = t < s;
+  const bool active = live && r < k;
+  const size_t o = static_cast<size_t>(live ? t : 0) * k + r;
+  const int my_idx = active ? idx[o] : -1;
+  const double wj = active ? static_cast<double>(w[o]) : 0.0;
+  const double gj = active ? static_cast<double>(gw[o]) : 0.0;
+  const double dot = row_sum_f64(wj * gj);
+  const double contrib = active ? wj * (gj - dot) : 0.0;
+  const uint64_t cbits = __builtin_bit_cast(uint64_t, contrib);
+  const int c_lo = static_cast<int>(static_cast<uint32_t>(cbits));
+  const int c_hi = static_cast<int>(static_cast<uint32_t>(cbits >> 32));
+
+  double acc[VPR];
+#pragma unroll
+  for (int v = 0; v < VPR; ++v) acc[v] = 0.0;
+  for (int j = 0; j < k; ++j) {  // k is uniform
+    const int sel = __shfl(my_idx, base + j);
+    const uint64_t lo = static_cast<uint32_t>(__shfl(c_lo, base + j));
+    const uint64_t hi = static_cast<uint32_t>(__shfl(c_hi, base + j));
+    const double val = __builtin_bit_cast(double, (hi << 32) | lo);
+#pragma unroll
+    for (int v = 0; v < VPR; ++v)
+      if (sel == r + 16 * v) acc[v] += val;
+  }
+  if (live) {
+    float* out = gl + static_cast<size_t>(t) * e;
+#pragma unroll
+    for (int v = 0; v < VPR; ++v) {
+      const int i = r + 16 * v;
+      if (i < e) out[i] = static_cast<float>(acc[v]);
+    }
+  }
+}
+
 // Weights renormalised over each token's kept routes (dst >= 0): w' = w / S with S the
 // float64 sum of the kept weights in route order; 0 for dropped routes, and for every
 // route when nothing is kept. One thread per token.
@@ -187,6 +237,12 @@ static int values_per_lane(int e) {
   return v <= 1 ? 1 : v <= 2 ? 2 : v <= 4 ? 4 : v <= 8 ? 8 : 16;
 }
 
+// Values per lane of the 16-lane row backward kernel (e <= 256).
+static int values_per_row_lane(int e) {
+  const int v = (e + 15) / 16;
+  return v <= 1 ? 1 : v <= 2 ? 2 : v <= 4 ? 4 : v <= 8 ? 8 : 16;
+}
+
 hipError_t launch_gate_topk(const float* logits, int s, int e, int k, int32_t* idx, float* w,
                             hipStream_t stream) {
   if (s == 0) return hipSuccess;
@@ -204,11 +260,19 @@ hipError_t launch_gate_topk(const float* logits, int s, int e, int k, int32_t* i
 hipError_t launch_gate_topk_backward(const int32_t* idx, const float* w, const float* gw, int s,
                                      int e, int k, float* gl, hipStream_t stream) {
   if (s == 0) return hipSuccess;
+  if (e <= 256) {
+    const dim3 grid((s + 4 * kWavesPerBlock - 1) / (4 * kWavesPerBlock)), block(kBlock);
+    switch (values_per_row_lane(e)) {
+      case 1: gate_topk_row_backward_kernel<1><<<grid, block, 0, stream>>>(idx, w, gw, s, e, k, gl); break;
+      case 2: gate_topk_row_backward_kernel<2><<<grid, block, 0, stream>>>(idx, w, gw, s, e, k, gl); break;
+      case 4: gate_topk_row_backward_kernel<4><<<grid, block, 0, stream>>>(idx, w, gw, s, e, k, gl); break;
+      case 8: gate_topk_row_backward_kernel<8><<<grid, block, 0, stream>>>(idx, w, gw, s, e, k, gl); break;
+      default: gate_topk_row_backward_kernel<16><<<grid, block, 0, stream>>>(idx, w, gw, s, e, k, gl); break;
+    }
+    return hipGetLastError();
+  }
   const dim3 grid((s + kWavesPerBlock - 1) / kWavesPerBlock), block(kBlock);
   switch (values_per_lane(e)) {
-    case 1: gate_topk_backward_kernel<1><<<grid, block, 0, stream>>>(idx, w, gw, s, e, k, gl); break;
-    case 2: gate_topk_backward_kernel<2><<<grid, block, 0, stream>>>(idx, w, gw, s, e, k, gl); break;
-    case 4: gate_topk_backward_kernel<4><<<grid, block, 0, stream>>>(idx, w, gw, s, e, k, gl); break;
     case 8: gate_topk_backward_kernel<8><<<grid, block, 0, stream>>>(idx, w, gw, s, e, k, gl); break;
     default: gate_topk_backward_kernel<16><<<grid, block, 0, stream>>>(idx, w, gw, s, e, k, gl); break;
   }

@@ -161,6 +161,19 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return step(step(a, b), step(c, d));
 }
 
+// Sum over one DPP row (16 lanes), the result in every lane of the row: the four in-row
+// steps of the wave reductions above, without the cross-row readlanes. All lanes must be
+// active.
+__device__ __forceinline__ double row_sum_f64(double v) {
+  auto bits = [](double x) { return __builtin_bit_cast(uint64_t, x); };
+  auto val = [](uint64_t u) { return __builtin_bit_cast(double, u); };
+  v = v + val(dpp_move64<0xb1>(bits(v)));
+  v = v + val(dpp_move64<0x4e>(bits(v)));
+  v = v + val(dpp_move64<0x141>(bits(v)));
+  v = v + val(dpp_move64<0x140>(bits(v)));
+  return v;
+}
+
 // Maximum over the 64 lanes, returned uniformly.
 __device__ __forceinline__ uint64_t wave_max(uint64_t v) {
   return wave_reduce(v, [](uint64_t a, uint64_t b) { return a > b ? a : b; });

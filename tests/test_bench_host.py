@@ -61,6 +61,26 @@ def test_traffic_is_reported_only_for_the_sources_it_was_taken_on(tmp_path, monk
     assert bench.measured_traffic("zipf_skew_h4096", "expert_gemm") == {}  # no such summary
 
 
+def test_gemm_sources_only_change_the_gemm_variant_digest(monkeypatch):
+    from combine_moe_gate_amd import _build
+    real_open = open
+
+    def edited_gemm(path, mode="r", *a, **k):
+        f = real_open(path, mode, *a, **k)
+        if path.endswith("gemm.hip") and "b" in mode:
+            data = f.read() + b"// edit"
+            f.close()
+            import io
+            return io.BytesIO(data)
+        return f
+
+    before = (bench.kernel_source_digest(), bench.kernel_source_digest("expert_gemm"))
+    monkeypatch.setattr("builtins.open", edited_gemm)
+    after = (bench.kernel_source_digest(), bench.kernel_source_digest("expert_gemm"))
+    assert before[0] == after[0] and before[1] != after[1]
+    assert any(p.endswith("gemm.hip") for p in _build.SOURCES)
+
+
 def test_traffic_of_other_sources_is_dropped(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     _write_traffic(tmp_path, "0123456789abcdef")

@@ -501,14 +501,15 @@ def _cpu_model() -> str:
 
 
 def run_cpu_baseline(w: W.Workload, variant: str | None = None, step_seconds: float = 6.0,
-                     sample_tokens: int = 1024):
+                     sample_tokens: int = 1024, loop_tokens: int = 16):
     """The oracle, as it stands, on the host's CPU, single-threaded.
 
     value: the metric's scope. The vectorised oracle's dispatch + combine, given the
     layout, on the same full host arrays as the GPU, median of 3 (tokens = s). Parts:
     the whole step on the first `sample_tokens` tokens for about `step_seconds`; and the
     loop oracle (plain per-element Python loops) over the whole step of the tiny
-    capacity-bounded workload. The expert_gemm variant times its forward (float64
+    capacity-bounded workload, and its dispatch + combine on the first `loop_tokens`
+    tokens of this workload and of the 4096-token dropless one. The expert_gemm variant times its forward (float64
     matmul per expert) on a 128-token sample instead.
     """
     from threadpoolctl import threadpool_limits
@@ -614,8 +615,34 @@ def run_cpu_baseline(w: W.Workload, variant: str | None = None, step_seconds: fl
         "whole_step_tokens_per_s": round(tw.s / (t1 - t0), 1),
         "dispatch_combine_tokens_per_s": round(tw.s / (tb - ta), 1),
         "seconds": round(t1 - t0, 3)}
+    # and its dispatch + combine on the first tokens of this workload and of the 4096-token
+    # dropless one (full row width; the whole arrays would take the loops hours)
+    samples = {}
+    for name in dict.fromkeys([w.name, "dropless_top8_h2816"]):
+        samples[name] = _loop_oracle_sample(W.WORKLOADS[name], loop_tokens)
+    out["loop_oracle_samples"] = samples
     limit.unregister()
     return out
+
+
+def _loop_oracle_sample(w: W.Workload, n: int) -> dict:
+    """The loop oracle's dispatch + combine, given its layout, on the first n tokens of w."""
+    import oracle.loop as LO
+
+    inp = W.make_inputs(w)
+    n = min(n, w.s)
+    cap = w.capacity
+    if cap > 0:
+        cap = max(1, -(-cap * n // w.s))
+    idx, wt = LO.gate_topk(inp.logits[:n], w.k)
+    L = LO.dispatch_layout(idx, w.e, cap)
+    t0 = time.perf_counter()
+    E = LO.dispatch(L, inp.x[:n])
+    LO.combine(L, E, wt, w.dtype)
+    el = time.perf_counter() - t0
+    return {"tokens_per_s": round(n / el, 2), "seconds": round(el, 3),
+            "sample": f"first {n} of {w.s} tokens (m={w.m}, e={w.e}, k={w.k}, {w.dtype}"
+                      f"{', capacity scaled to ' + str(cap) if w.capacity > 0 else ''})"}
 
 
 def main():

@@ -120,3 +120,11 @@ def test_expert_gemm_bytes_count_only_the_experts_that_receive_rows():
     assert some["expert_gemm"] == w.s * row + 43 * wrow + K * W.EXPERT_WIDTH * 2 + K * 4
     # the weight gradient writes every expert's (zeros for the idle ones)
     assert all_e["expert_gemm_wgrad"] == some["expert_gemm_wgrad"]
+
+
+def test_loop_oracle_sample_times_the_first_tokens_with_the_capacity_scaled():
+    w = W.WORKLOADS["tiny_capacity_top2"]
+    r = bench._loop_oracle_sample(w, 4)
+    assert r["tokens_per_s"] > 0 and r["seconds"] > 0
+    # capacity 80 of 256 tokens, scaled to 4 tokens: ceil(80 * 4 / 256) = 2
+    assert r["sample"] == "first 4 of 256 tokens (m=64, e=8, k=2, f32, capacity scaled to 2)"

@@ -16,10 +16,14 @@
 // by direct-to-LDS loads into an XOR-swizzled layout (conflict-free 16-byte fragment
 // reads). With 64-element K steps every staged row segment is one whole 128-byte line:
 // each CU has a bounded number of L2 requests in flight, so whole-line requests double
-// the bytes that bound admits. STAGES K steps are staged at once: the loads of step
-// kt + STAGES - 1 are issued while step kt is multiplied. Lane l of an MFMA reads row
-// l%32, K elements 8*(l/32)..+7 of each operand (one ds_read_b128) and holds output rows
-// 8*(v/4) + 4*(l/32) + v%4, column l%32 for v = 0..15.
+// the bytes that bound admits. The token rows are staged SA K steps deep and the weights
+// SB (SA >= SB): the loads of step kt + SA - 1 (kt + SB - 1) are issued while step kt is
+// multiplied. Lane l of an MFMA reads row
+// l%32, K elements 8*(l/32)..+7 of each operand (one ds_read_b128). The weights are the
+// MFMA's first operand, so lane l holds token row l%32 and output features 8*(v/4) +
+// 4*(l/32) + v%4 for v = 0..15: four consecutive features, written to the LDS output
+// tile 8 bytes at a time (whole-row stores from there measured 1-3% faster than stores
+// straight from the accumulators, results bit-identical).
 //
 // The input-row gradient, grad_A[r] = grad_out[r] @ W[x], is the same product with K = n
 // and N = m and the weights read as [K][N] (BKN): that operand is staged K row by K row,
@@ -50,10 +54,14 @@
 namespace moe {
 
 constexpr int kBandRows = 8;  // row-blocks per band of the tile order
+// Byte pitch of a row of the output tile staged in LDS (256 features of 2 bytes plus 16:
+// successive rows start 4 banks apart).
+constexpr int kOutPitch = 256 * 2 + 16;
 
 // Waves are arranged 2 along the rows x NW along the columns of the tile; a K step is BK
-// elements (BK / 8 chunks of 16 bytes per staged row); STAGES K steps are staged at once.
-template <int WM, int WN, int NW, int BK, int STAGES>
+// elements (BK / 8 chunks of 16 bytes per staged row); SA K steps of the token rows (A) and
+// SB of the weights (B) are staged at once (SA >= SB).
+template <int WM, int WN, int NW, int BK, int SA, int SB>
 struct GemmShape {
   static constexpr int WAVES = 2 * NW, THREADS = WAVES * kWave;
   static constexpr int BM = 2 * WM, BN = NW * WN;
@@ -65,11 +73,18 @@ struct GemmShape {
   static constexpr int A_LOADS = BM / ROWS_PER_LOAD / WAVES;  // per wave per stage
   static constexpr int B_LOADS = BN / ROWS_PER_LOAD / WAVES;
   static constexpr int LOADS = A_LOADS + B_LOADS;
-  static constexpr int STAGE_BYTES = (BM + BN) * ROW_BYTES;
-  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int A_STAGE = BM * ROW_BYTES, B_STAGE = BN * ROW_BYTES;
+  static constexpr int STAGED_BYTES = SA * A_STAGE + SB * B_STAGE;
+  static constexpr int LDS_BYTES = STAGED_BYTES > BM * kOutPitch ? STAGED_BYTES : BM * kOutPitch;
+  // loads a wave issues between those of step j and the wait that publishes step j (the
+  // next step's, for the operands staged three deep)
+  static constexpr int AHEAD = (SA >= 3 ? A_LOADS : 0) + (SB >= 3 ? B_LOADS : 0);
   static_assert(A_LOADS * ROWS_PER_LOAD * WAVES == BM && B_LOADS * ROWS_PER_LOAD * WAVES == BN,
                 "stage split");
   static_assert(KS % 2 == 0, "fragment buffers alternate within a K step");
+  static_assert(BN * 2 + 16 <= kOutPitch, "output tile rows fit the staging pitch");
+  static_assert(SA >= SB && SB >= 2 && SA <= 3, "the token rows are staged at least as deep");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS of one workgroup");
   // XOR swizzle: slot p of staged row R holds chunk p ^ swz(R). The 16 lanes that one
   // 16-byte LDS read serves together read rows r .. r + 15 of one chunk; with this
   // swizzle they land in 16 different 16-byte groups of the 256-byte bank row.
@@ -130,7 +145,7 @@ __device__ __forceinline__ void clear_slots(const int (&c)[LOADS], int kt, int k
 
 // One workgroup per CU (its LDS stages take most of the CU's 160 KiB), NW / 2 waves per
 // SIMD: the register file is these waves', so the schedule may keep two fragment sets live.
-template <int DT, bool GATHER, bool SCALE, bool BKN, int WM, int WN, int NW, int BK, int STAGES>
+template <int DT, bool GATHER, bool SCALE, bool BKN, int WM, int WN, int NW, int BK, int SA, int SB>
 __global__ __launch_bounds__(2 * NW * kWave)
 __attribute__((amdgpu_waves_per_eu(NW / 2, NW / 2))) void expert_gemm_kernel(
     const chunk_t* __restrict__ a, const chunk_t* __restrict__ wts,
@@ -138,49 +153,42 @@ __attribute__((amdgpu_waves_per_eu(NW / 2, NW / 2))) void expert_gemm_kernel(
     const int32_t* __restrict__ src, const int32_t* __restrict__ kept,
     const int32_t* __restrict__ offsets, int e, int k, int m, int n, int col_blocks,
     int band_rows, uint16_t* __restrict__ out) {
-  using S = GemmShape<WM, WN, NW, BK, STAGES>;
+  using S = GemmShape<WM, WN, NW, BK, SA, SB>;
   static_assert(!BKN || (S::BN == 256 && BK == 64 && S::B_LOADS * 2 * S::WAVES == BK),
                 "a [K][N] operand stages 64 K rows of 512 bytes, two per load instruction");
-  extern __shared__ __attribute__((aligned(1024))) char lds[];  // [STAGES][BM + BN rows][ROW_BYTES]
-  __shared__ int32_t row_src[S::BM];
-  __shared__ float row_scale[S::BM];
-  __shared__ int32_t tile_info[3];
+  // [SA][BM rows][ROW_BYTES] token rows, then [SB][BN rows][ROW_BYTES] weights; the output
+  // tile reuses it at the end. No static LDS: the stages may take all 160 KiB.
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wv = wave_in_block();
 
-  if (wv == 0) {
-    const TileCoord tc = find_tile<S::BM>(blockIdx.x, e, kept, col_blocks, band_rows);
-    if (lane == 0) {
-      tile_info[0] = tc.expert;
-      tile_info[1] = tc.rb;
-      tile_info[2] = tc.cb;
-    }
-  }
-  __syncthreads();
-  const int x = tile_info[0];
+  // every wave finds the workgroup's tile itself (the same for all)
+  const TileCoord tc = find_tile<S::BM>(blockIdx.x, e, kept, col_blocks, band_rows);
+  const int x = tc.expert;
   if (x < 0) return;  // no tile: uniform per workgroup
-  const int rb = tile_info[1];
-  const int row0 = offsets[x] + rb * S::BM;
-  const int rem = kept[x] - rb * S::BM;
+  const int row0 = offsets[x] + tc.rb * S::BM;
+  const int rem = kept[x] - tc.rb * S::BM;
   const int nrows = rem < S::BM ? rem : S::BM;
-  const int col0 = tile_info[2] * S::BN;
+  const int col0 = tc.cb * S::BN;
+  const int wm = wv / NW, wn = wv % NW;  // this wave's part of the tile
 
-  for (int i = tid; i < S::BM; i += S::THREADS) {
-    // rows past the segment repeat its first row: their products land only in output
-    // rows that are never stored
-    const int r = row0 + (i < nrows ? i : 0);
-    const int t = src[r];
-    float sc = 1.0f;
+  // the route weight of each output row this lane stores (weights after the experts)
+  float row_sc[S::FM];
+#pragma unroll
+  for (int i = 0; i < S::FM; ++i) {
+    row_sc[i] = 1.0f;
     if constexpr (SCALE) {
-      for (int j = 0; j < k; ++j)
-        if (dst[static_cast<size_t>(t) * k + j] == r) sc = route_w[static_cast<size_t>(t) * k + j];
+      const int row = wm * WM + i * 32 + (lane & 31);
+      if (row < nrows) {
+        const int r = row0 + row;
+        const int t = src[r];
+        for (int j = 0; j < k; ++j)
+          if (dst[static_cast<size_t>(t) * k + j] == r) row_sc[i] = route_w[static_cast<size_t>(t) * k + j];
+      }
     }
-    row_src[i] = GATHER ? t : r;
-    row_scale[i] = sc;
   }
-  __syncthreads();
 
   const int kchunks = m / 8;  // 16-byte chunks per operand row
   const int nk = (m + BK - 1) / BK;
@@ -194,8 +202,11 @@ __attribute__((amdgpu_waves_per_eu(NW / 2, NW / 2))) void expert_gemm_kernel(
   int a_chunk[S::A_LOADS], b_chunk[S::B_LOADS];
 #pragma unroll
   for (int q = 0; q < S::A_LOADS; ++q) {
+    // rows past the segment repeat its first row: their products land only in output
+    // rows that are never stored
     const int r = (wv * S::A_LOADS + q) * S::ROWS_PER_LOAD + lane / S::CH;
-    a_rows[q] = a + static_cast<size_t>(row_src[r]) * kchunks;
+    const int rr = row0 + (r < nrows ? r : 0);
+    a_rows[q] = a + static_cast<size_t>(GATHER ? src[rr] : rr) * kchunks;
     a_chunk[q] = (lane % S::CH) ^ S::swz(r);
   }
 #pragma unroll
@@ -215,34 +226,31 @@ __attribute__((amdgpu_waves_per_eu(NW / 2, NW / 2))) void expert_gemm_kernel(
       b_chunk[q] = (lane % S::CH) ^ S::swz(r);
     }
   }
-  auto stage_a = [&](int buf) { return lds + buf * S::STAGE_BYTES + wv * S::A_LOADS * 1024; };
-  auto stage_b = [&](int buf) {
-    return lds + buf * S::STAGE_BYTES + S::BM * S::ROW_BYTES + wv * S::B_LOADS * 1024;
+  auto a_base = [&](int kt) { return lds + (kt % SA) * S::A_STAGE; };
+  auto b_base = [&](int kt) { return lds + SA * S::A_STAGE + (kt % SB) * S::B_STAGE; };
+  auto issue_a = [&](int kt) {
+    stage_rows<S::A_LOADS, S::CH>(a_rows, a_chunk, kt, kchunks, a_base(kt) + wv * S::A_LOADS * 1024);
   };
-  auto issue = [&](int kt) {
-    const int buf = kt % STAGES;
-    stage_rows<S::A_LOADS, S::CH>(a_rows, a_chunk, kt, kchunks, stage_a(buf));
-    if constexpr (BKN) stage_rows_kn<S::B_LOADS>(b_rows, b_chunk, kt, m, n / 8, stage_b(buf));
-    else stage_rows<S::B_LOADS, S::CH>(b_rows, b_chunk, kt, kchunks, stage_b(buf));
+  auto issue_b = [&](int kt) {
+    char* st = b_base(kt) + wv * S::B_LOADS * 1024;
+    if constexpr (BKN) stage_rows_kn<S::B_LOADS>(b_rows, b_chunk, kt, m, n / 8, st);
+    else stage_rows<S::B_LOADS, S::CH>(b_rows, b_chunk, kt, kchunks, st);
   };
-  // make stage kt visible to the workgroup: this wave's loads for it have landed (at most
-  // the loads of the stages issued after it remain), the K-tail slots are cleared, then
-  // every wave meets at the barrier
-  auto publish = [&](int kt, int issued_last) {
-    const int after = issued_last - kt;
-    if (STAGES <= 2 || after <= 0) __builtin_amdgcn_s_waitcnt(wait_vm(0));
-    else if (STAGES <= 3 || after == 1) __builtin_amdgcn_s_waitcnt(wait_vm(S::LOADS));
-    else __builtin_amdgcn_s_waitcnt(wait_vm(2 * S::LOADS));
+  // make step kt visible to the workgroup: this wave's loads for it have landed (only the
+  // loads issued after them, those of step kt + 1 staged three deep, may remain), the
+  // K-tail slots are cleared, then every wave meets at the barrier
+  auto publish = [&](int kt) {
+    if (S::AHEAD > 0 && kt + 1 < nk) __builtin_amdgcn_s_waitcnt(wait_vm(S::AHEAD));
+    else __builtin_amdgcn_s_waitcnt(wait_vm(0));
     if ((kt + 1) * BK > m) {
-      const int buf = kt % STAGES;
-      clear_slots<S::A_LOADS, S::CH>(a_chunk, kt, kchunks, stage_a(buf), lane);
-      if constexpr (!BKN) clear_slots<S::B_LOADS, S::CH>(b_chunk, kt, kchunks, stage_b(buf), lane);
+      clear_slots<S::A_LOADS, S::CH>(a_chunk, kt, kchunks, a_base(kt) + wv * S::A_LOADS * 1024, lane);
+      if constexpr (!BKN)
+        clear_slots<S::B_LOADS, S::CH>(b_chunk, kt, kchunks, b_base(kt) + wv * S::B_LOADS * 1024, lane);
     }
     __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);
     stage_barrier();
   };
 
-  const int wm = wv / NW, wn = wv % NW;  // this wave's part of the tile
   f32x16_t acc[S::FM][S::FN];
 #pragma unroll
   for (int i = 0; i < S::FM; ++i)
@@ -254,7 +262,7 @@ __attribute__((amdgpu_waves_per_eu(NW / 2, NW / 2))) void expert_gemm_kernel(
   // fragment addresses: row (lane % 32) of each 32-row MFMA tile, chunk 2 ks + lane / 32,
   // found at slot chunk ^ swz(row) = chunk ^ swz(lane % 32) (tiles start at multiples of 32)
   const int a_frag = (wm * WM + (lane & 31)) * S::ROW_BYTES;
-  const int b_frag = S::BM * S::ROW_BYTES + (wn * WN + (lane & 31)) * S::ROW_BYTES;
+  const int b_frag = (wn * WN + (lane & 31)) * S::ROW_BYTES;
   const int fswz = S::swz(lane & 31);
   // [K][N] weights: each fragment is two transposing reads. Lane j of 16-lane group g
   // points at K row 8 (g / 2) + j / 4 of the k16 step (and 4 rows further for the second
@@ -265,53 +273,54 @@ __attribute__((amdgpu_waves_per_eu(NW / 2, NW / 2))) void expert_gemm_kernel(
   const int tr_swz = 4 * ((lane & 15) >> 2);
   chunk_t fa[2][S::FM], fb[2][S::FN];
   auto read_frags = [&](int kt, int ks, int fbuf) {
-    const char* st = lds + (kt % STAGES) * S::STAGE_BYTES;
+    const char* sa = a_base(kt);
+    const char* sb = b_base(kt);
     const int slot = ((2 * ks + (lane >> 5)) ^ fswz) * 16;
 #pragma unroll
     for (int i = 0; i < S::FM; ++i)
-      fa[fbuf][i] = *reinterpret_cast<const chunk_t*>(st + a_frag + i * 32 * S::ROW_BYTES + slot);
+      fa[fbuf][i] = *reinterpret_cast<const chunk_t*>(sa + a_frag + i * 32 * S::ROW_BYTES + slot);
 #pragma unroll
     for (int jj = 0; jj < S::FN; ++jj) {
       if constexpr (BKN) {
         const int byte = (wn * WN + jj * 32 + tr_col) * 2;
-        const char* p = st + S::BM * S::ROW_BYTES + (ks * 16 + tr_row) * 512 + (((byte >> 4) ^ tr_swz) << 4) +
-                        (byte & 15);
+        const char* p = sb + (ks * 16 + tr_row) * 512 + (((byte >> 4) ^ tr_swz) << 4) + (byte & 15);
         const uint2 lo = read_tr16(p), hi = read_tr16(p + 4 * 512);
         fb[fbuf][jj] = chunk_t{lo.x, lo.y, hi.x, hi.y};
       } else {
-        fb[fbuf][jj] = *reinterpret_cast<const chunk_t*>(st + b_frag + jj * 32 * S::ROW_BYTES + slot);
+        fb[fbuf][jj] = *reinterpret_cast<const chunk_t*>(sb + b_frag + jj * 32 * S::ROW_BYTES + slot);
       }
     }
   };
+  // The weights are the MFMA's first operand, so each accumulator holds a 32-feature x
+  // 32-row block transposed: lane l has row l % 32 and features 8 (v / 4) + 4 (l / 32) +
+  // v % 4, four consecutive features per group of four values.
   auto mfmas = [&](int fbuf) {
 #pragma unroll
     for (int i = 0; i < S::FM; ++i)
 #pragma unroll
       for (int jj = 0; jj < S::FN; ++jj)
-        acc[i][jj] = mfma_32x32x16<DT>(fa[fbuf][i], fb[fbuf][jj], acc[i][jj]);
+        acc[i][jj] = mfma_32x32x16<DT>(fb[fbuf][jj], fa[fbuf][i], acc[i][jj]);
   };
 
-  // prologue: stages 0 .. min(STAGES - 2, nk - 1) in flight, stage 0 published, its
-  // first fragments read
-  int issued_last = -1;
-  for (int p = 0; p < STAGES - 1 && p < nk; ++p) {
-    issue(p);
-    issued_last = p;
+  // prologue: the first SB - 1 weight steps and SA - 1 token-row steps in flight (weights
+  // first at each step), step 0 published, its first fragments read
+  for (int p = 0; p < SA - 1 && p < nk; ++p) {
+    if (p < SB - 1) issue_b(p);
+    issue_a(p);
   }
-  publish(0, issued_last);
+  publish(0);
   read_frags(0, 0, 0);
 
-  // Per K step kt: issue the loads of step kt + STAGES - 1 (into the buffer step kt - 1
-  // used, which every wave finished reading before the last barrier). Each k16 step's
-  // fragments are read under the MFMAs of the one before; before the last k16 step's
-  // MFMAs, step kt + 1 is published (the barrier also tells every wave that step kt's
-  // buffer has been read out) and its first fragments are read. The scheduling fences
-  // keep each batch of reads ahead of the MFMAs that hide it.
+  // Per K step kt: issue the weights of step kt + SB - 1, then the token rows of step
+  // kt + SA - 1 (each into the buffer step kt - 1 used, which every wave finished reading
+  // before the last barrier). Each k16 step's fragments are read under the MFMAs of the
+  // one before; before the last k16 step's MFMAs, step kt + 1 is published (the barrier
+  // also tells every wave that step kt's buffers have been read out) and its first
+  // fragments are read. The scheduling fences keep each batch of reads ahead of the MFMAs
+  // that hide it.
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + STAGES - 1 < nk) {
-      issue(kt + STAGES - 1);
-      issued_last = kt + STAGES - 1;
-    }
+    if (kt + SB - 1 < nk) issue_b(kt + SB - 1);
+    if (kt + SA - 1 < nk) issue_a(kt + SA - 1);
 #pragma unroll
     for (int ks = 0; ks < S::KS; ++ks) {
       __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);  // this k16 step's fragments have landed
@@ -319,7 +328,7 @@ __attribute__((amdgpu_waves_per_eu(NW / 2, NW / 2))) void expert_gemm_kernel(
       if (ks + 1 < S::KS) {
         read_frags(kt, ks + 1, (ks + 1) & 1);
       } else if (kt + 1 < nk) {
-        publish(kt + 1, issued_last);
+        publish(kt + 1);
         __builtin_amdgcn_sched_barrier(0);
         read_frags(kt + 1, 0, 0);
       }
@@ -329,31 +338,54 @@ __attribute__((amdgpu_waves_per_eu(NW / 2, NW / 2))) void expert_gemm_kernel(
     }
   }
 
-  // epilogue: optional route weight (weights after the experts), one narrowing
+  // epilogue: optional route weight (weights after the experts), one narrowing. The
+  // tile goes through LDS (free once every wave has left the main loop): each lane writes
+  // its four-feature runs 8 bytes at a time, then the workgroup stores whole rows of the
+  // tile, 32 lanes per 512-byte row, with 16-byte stores (straight from the accumulators,
+  // an 8-byte store touches 32 rows and a 2-byte one 2: measured slower). n is a multiple
+  // of 8, so a run or a 16-byte chunk never crosses it.
+  __syncthreads();
+  char* ot = lds;  // [BM][kOutPitch bytes]
 #pragma unroll
   for (int i = 0; i < S::FM; ++i) {
+    const int row = wm * WM + i * 32 + (lane & 31);
+    const float sc = row_sc[i];
 #pragma unroll
     for (int jj = 0; jj < S::FN; ++jj) {
-      const int col = col0 + wn * WN + jj * 32 + (lane & 31);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (row < nrows && col < n) {
-          float f = acc[i][jj][v];
-          if constexpr (SCALE) f = __fmul_rn(row_scale[row], f);
-          out[static_cast<size_t>(row0 + row) * n + col] = narrow<DT>(f);
+      for (int g = 0; g < 4; ++g) {
+        const int col = wn * WN + jj * 32 + 8 * g + 4 * (lane >> 5);
+        float f[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          f[u] = acc[i][jj][4 * g + u];
+          if constexpr (SCALE) f[u] = __fmul_rn(sc, f[u]);
         }
+        *reinterpret_cast<uint2*>(ot + row * kOutPitch + col * 2) =
+            uint2{narrow2<DT>(f[0], f[1]), narrow2<DT>(f[2], f[3])};
       }
     }
+  }
+  __syncthreads();
+  constexpr int kRowChunks = S::BN * 2 / 16;
+#pragma unroll 4
+  for (int c = tid; c < S::BM * kRowChunks; c += S::THREADS) {
+    const int row = c / kRowChunks, ch = c % kRowChunks;
+    const int col = col0 + ch * 8;
+    if (row < nrows && col < n)
+      *reinterpret_cast<chunk_t*>(out + static_cast<size_t>(row0 + row) * n + col) =
+          *reinterpret_cast<const chunk_t*>(ot + row * kOutPitch + ch * 16);
   }
 }
 
 // Tile shape chosen per launch (eight waves, 64-element K steps either way): 256 x 256
-// tiles with two stages when experts average at least 512 rows (the fewest operand
-// bytes per MFMA), else 128 x 256 tiles with three stages (less padding in short
-// segments; the smaller stages leave LDS for a deeper pipeline).
-constexpr int kTallWM = 128, kTallWN = 64, kTallNW = 4, kTallBK = 64, kTallStages = 2;
-constexpr int kShortWM = 64, kShortWN = 64, kShortNW = 4, kShortBK = 64, kShortStages = 3;
+// tiles with both operands two steps deep when experts average at least 512 rows (the
+// fewest operand bytes per MFMA), else 128 x 256 tiles three deep (less padding in short
+// segments; the smaller stages leave LDS for a deeper pipeline). Staging the 256-row
+// tiles' token rows three deep (all 160 KiB of LDS) measured 2-4% slower in interleaved
+// runs on the Zipf, 32k-token and dropless workloads, forward and input-row gradient.
+constexpr int kTallWM = 128, kTallWN = 64, kTallNW = 4, kTallBK = 64, kTallSA = 2, kTallSB = 2;
+constexpr int kShortWM = 64, kShortWN = 64, kShortNW = 4, kShortBK = 64, kShortSA = 3, kShortSB = 3;
 
 static bool use_tall(const LayoutView& L) {
   return L.capacity > 0 ? L.capacity >= 512 : static_cast<int64_t>(L.s) * L.k >= 512LL * L.e;
@@ -381,11 +413,11 @@ int64_t expert_gemm_kn_grid(const LayoutView& L, int N) {
   return tile_grid(L, 2 * kTallWM, kTallNW * kTallWN, N);
 }
 
-template <int DT, bool GATHER, bool SCALE, bool BKN, int WM, int WN, int NW, int BK, int STAGES>
+template <int DT, bool GATHER, bool SCALE, bool BKN, int WM, int WN, int NW, int BK, int SA, int SB>
 static hipError_t gemm_launch(const LayoutView& L, const void* a, const void* w,
                               const float* route_w, int m, int n, void* out, hipStream_t stream) {
-  using S = GemmShape<WM, WN, NW, BK, STAGES>;
-  auto kern = expert_gemm_kernel<DT, GATHER, SCALE, BKN, WM, WN, NW, BK, STAGES>;
+  using S = GemmShape<WM, WN, NW, BK, SA, SB>;
+  auto kern = expert_gemm_kernel<DT, GATHER, SCALE, BKN, WM, WN, NW, BK, SA, SB>;
   // dynamic LDS above the 64 KiB default needs the per-kernel limit raised (idempotent)
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS_BYTES);
@@ -403,9 +435,9 @@ template <int DT, bool GATHER, bool SCALE, bool BKN = false>
 static hipError_t gemm_shape(const LayoutView& L, const void* a, const void* w,
                              const float* route_w, int m, int n, void* out, hipStream_t stream) {
   if (use_tall(L))
-    return gemm_launch<DT, GATHER, SCALE, BKN, kTallWM, kTallWN, kTallNW, kTallBK, kTallStages>(
+    return gemm_launch<DT, GATHER, SCALE, BKN, kTallWM, kTallWN, kTallNW, kTallBK, kTallSA, kTallSB>(
         L, a, w, route_w, m, n, out, stream);
-  return gemm_launch<DT, GATHER, SCALE, BKN, kShortWM, kShortWN, kShortNW, kShortBK, kShortStages>(
+  return gemm_launch<DT, GATHER, SCALE, BKN, kShortWM, kShortWN, kShortNW, kShortBK, kShortSA, kShortSB>(
       L, a, w, route_w, m, n, out, stream);
 }
 
@@ -437,9 +469,9 @@ hipError_t launch_expert_gemm_kn(const LayoutView& L, const void* a, const void*
   if (L.s > 0) {
     const hipError_t err =
         dtype == kBF16
-            ? gemm_launch<kBF16, false, false, true, kTallWM, kTallWN, kTallNW, kTallBK, kTallStages>(
+            ? gemm_launch<kBF16, false, false, true, kTallWM, kTallWN, kTallNW, kTallBK, kTallSA, kTallSB>(
                   L, a, w, nullptr, K, N, out, stream)
-            : gemm_launch<kF16, false, false, true, kTallWM, kTallWN, kTallNW, kTallBK, kTallStages>(
+            : gemm_launch<kF16, false, false, true, kTallWM, kTallWN, kTallNW, kTallBK, kTallSA, kTallSB>(
                   L, a, w, nullptr, K, N, out, stream);
     if (err != hipSuccess) return err;
   }

@@ -28,6 +28,13 @@ __device__ __forceinline__ uint16_t narrow(float v) {
   else return static_cast<uint16_t>(f32_to_f16_rne(v));
 }
 
+// Two values narrowed to a packed pair of the element type (a in the low half).
+template <int DT>
+__device__ __forceinline__ uint32_t narrow2(float a, float b) {
+  if constexpr (DT == kBF16) return f32x2_to_bf16x2_rne(a, b);
+  else return f32_to_f16_rne(a) | (f32_to_f16_rne(b) << 16);
+}
+
 // Inclusive wave scan of a non-negative int.
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
   const int lane = lane_id();

@@ -14,11 +14,16 @@
 //                counts of earlier ones), so first choices win capacity.
 //
 // No sorting and no order-dependent atomics; two launches over tiles of 256 items (one
-// when all items fit one tile: the place kernel then counts that tile itself):
+// when all items fit one tile: the place kernel then counts that tile itself, three when
+// there are more than kScanTiles tiles):
 //
 //   count  one workgroup per tile: LDS histogram of the tile's valid routes (integer
 //          atomic adds; the totals do not depend on their order), the tile's share of
 //          the routing checksum and its flag bits.
+//   scan   (more than kScanTiles tiles) one workgroup per expert turns its row of the
+//          tile table into exclusive prefixes over the tiles, in place, and writes the
+//          expert's total count: each place workgroup then reads one entry per expert
+//          instead of the whole table, whose size grows with the batch.
 //   place  one workgroup per tile again. Each workgroup first derives what it needs
 //          from the small, L2-resident tile tables: for every expert the sum over
 //          earlier tiles (its tile base) and over all tiles (the count), then an
@@ -168,10 +173,62 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t* __restrict__ va
   return total;
 }
 
+// Tile counts of more than this many tiles are scanned by their own launch (measured at
+// 512 and 1024 tiles: reading the whole table in every place workgroup costs more than the
+// extra launch).
+constexpr int kScanTiles = 256;
+
+// Exclusive prefix over the tiles of expert x's row of the tile table, in place, and the
+// expert's total into counts[x]. Thread i owns a contiguous run of tiles; the runs' sums
+// are scanned across the workgroup (integer sums: exact in any order).
+__global__ __launch_bounds__(kTileTokens) void layout_scan_kernel(int32_t* __restrict__ tile_counts,
+                                                                  int ntiles, int ntp,
+                                                                  int32_t* __restrict__ counts) {
+  __shared__ int32_t wave_tot[kTileTokens / kWave];
+  constexpr int kBatch = 8;
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  int32_t* row = tile_counts + static_cast<size_t>(blockIdx.x) * ntp;
+  const int per = (ntiles + kTileTokens - 1) / kTileTokens;
+  const int b0 = static_cast<int>(threadIdx.x) * per;
+  const int b1 = b0 + per < ntiles ? b0 + per : ntiles;
+  int32_t sum = 0;
+  for (int q = b0; q < b1; q += kBatch) {  // batches of independent loads
+    int32_t v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) v[u] = q + u < b1 ? row[q + u] : 0;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) sum += v[u];
+  }
+  int32_t incl = sum;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int32_t y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  if (lane == kWave - 1) wave_tot[wv] = incl;
+  __syncthreads();
+  int32_t run = incl - sum, total = 0;
+  for (int w = 0; w < kTileTokens / kWave; ++w) {
+    if (w < wv) run += wave_tot[w];
+    total += wave_tot[w];
+  }
+  for (int q = b0; q < b1; q += kBatch) {
+    int32_t v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) v[u] = q + u < b1 ? row[q + u] : 0;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (q + u < b1) row[q + u] = run;
+      run += v[u];
+    }
+  }
+  if (threadIdx.x == 0) counts[blockIdx.x] = total;
+}
+
 template <int KMAX, bool RM>
 __global__ __launch_bounds__(kTileTokens) void layout_place_kernel(
     const int32_t* __restrict__ idx, int s, int e, int k, int items, int capacity, int pad,
-    int32_t rows, int ntiles, int ntp, const int32_t* __restrict__ tile_counts,
+    int32_t rows, int ntiles, int ntp, bool prefixed, const int32_t* __restrict__ tile_counts,
     const uint64_t* __restrict__ tile_checksum, const int32_t* __restrict__ tile_flags,
     int32_t* __restrict__ counts, int32_t* __restrict__ kept_out, int32_t* __restrict__ offsets_out,
     uint64_t* __restrict__ checksum, int32_t* __restrict__ flags, int32_t* __restrict__ dst,
@@ -208,6 +265,16 @@ __global__ __launch_bounds__(kTileTokens) void layout_place_kernel(
   }
   if ((tile < ntiles || single) && item < items)
     item_flags = load_item<KMAX, RM>(idx, item, s, k, e, tok, ids, ok, pos);
+  // workgroup 0 publishes the checksum and flags: its first share of the tiles' values is
+  // loaded now, beside the routes
+  uint64_t tile_cks = 0;
+  int tile_flg = 0;
+  if (tile == 0 && !single && static_cast<int>(threadIdx.x) < ntiles) {
+    tile_cks = tile_checksum[threadIdx.x];
+    tile_flg = tile_flags[threadIdx.x];
+  }
+  if (tile < ntiles)  // cleared here, read after the barriers below
+    for (int i = threadIdx.x; i < kWaves * e; i += kTileTokens) lane_masks[i] = 0ull;
 
   // per expert: sum over earlier tiles and over all tiles. Row x of the expert-major
   // tile table is read with 16-byte loads; with e <= 128 several threads share a row
@@ -227,6 +294,17 @@ __global__ __launch_bounds__(kTileTokens) void layout_place_kernel(
     __syncthreads();
     for (int x = threadIdx.x; x < e; x += kTileTokens)
       off_s[x] = capacity > 0 ? capacity : (total_s[x] + pad - 1) / pad * pad;  // segment sizes
+  } else if (prefixed) {
+    // the scan launch left each tile's exclusive prefix in the table and the totals in
+    // counts (workgroups past the tiles, padding only, take the totals as their base)
+    for (int x = threadIdx.x; x < e; x += kTileTokens) {
+      const int32_t tot = counts[x];
+      base_s[x] = my_tile < ntiles ? tile_counts[static_cast<size_t>(x) * ntp + my_tile] : tot;
+      total_s[x] = tot;
+    }
+    __syncthreads();
+    for (int x = threadIdx.x; x < e; x += kTileTokens)
+      off_s[x] = capacity > 0 ? capacity : (total_s[x] + pad - 1) / pad * pad;  // segment sizes
   } else {
     const int P = e <= kTileTokens / 2 ? kTileTokens / e : 1;  // threads per expert
     const int nq = ntp / 4;                                      // int4 groups per row
@@ -237,14 +315,21 @@ __global__ __launch_bounds__(kTileTokens) void layout_place_kernel(
       const int4* row = reinterpret_cast<const int4*>(tile_counts + static_cast<size_t>(x) * ntp);
       int32_t before = 0, all = 0;
       const int q1 = (part + 1) * qlen < nq ? (part + 1) * qlen : nq;
-      for (int q = part * qlen; q < q1; ++q) {
-        const int4 c = row[q];
-        const int b = 4 * q;
-        const int32_t c0 = b < ntiles ? c.x : 0, c1 = b + 1 < ntiles ? c.y : 0;
-        const int32_t c2 = b + 2 < ntiles ? c.z : 0, c3 = b + 3 < ntiles ? c.w : 0;
-        before += (b < my_tile ? c0 : 0) + (b + 1 < my_tile ? c1 : 0) + (b + 2 < my_tile ? c2 : 0) +
-                  (b + 3 < my_tile ? c3 : 0);
-        all += c0 + c1 + c2 + c3;
+      // batches of independent loads (one dependent load per chunk costs a round trip each)
+      constexpr int kBatch = 8;
+      for (int q0 = part * qlen; q0 < q1; q0 += kBatch) {
+        int4 cb[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) cb[u] = q0 + u < q1 ? row[q0 + u] : make_int4(0, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int b = 4 * (q0 + u);
+          const int32_t c0 = b < ntiles ? cb[u].x : 0, c1 = b + 1 < ntiles ? cb[u].y : 0;
+          const int32_t c2 = b + 2 < ntiles ? cb[u].z : 0, c3 = b + 3 < ntiles ? cb[u].w : 0;
+          before += (b < my_tile ? c0 : 0) + (b + 1 < my_tile ? c1 : 0) + (b + 2 < my_tile ? c2 : 0) +
+                    (b + 3 < my_tile ? c3 : 0);
+          all += c0 + c1 + c2 + c3;
+        }
       }
       if (P > 1) {
         part_before[slot] = before;
@@ -278,7 +363,7 @@ __global__ __launch_bounds__(kTileTokens) void layout_place_kernel(
   if (tile == 0) {  // publish the layout's per-expert arrays, checksum and flags
     for (int x = threadIdx.x; x < e; x += kTileTokens) {
       const int32_t c = total_s[x];
-      counts[x] = c;
+      if (!prefixed) counts[x] = c;  // else the scan launch wrote them (other workgroups read them)
       kept_out[x] = capacity > 0 ? (c < capacity ? c : capacity) : c;
       offsets_out[x] = off_s[x];
     }
@@ -293,7 +378,9 @@ __global__ __launch_bounds__(kTileTokens) void layout_place_kernel(
       }
       f = item_flags;
     } else {
-      for (int b = threadIdx.x; b < ntiles; b += kTileTokens) {
+      cks = tile_cks;
+      f = tile_flg;
+      for (int b = threadIdx.x + kTileTokens; b < ntiles; b += kTileTokens) {
         cks += tile_checksum[b];
         f |= tile_flags[b];
       }
@@ -318,9 +405,6 @@ __global__ __launch_bounds__(kTileTokens) void layout_place_kernel(
   }
 
   if (tile < ntiles) {  // uniform per workgroup
-    for (int i = threadIdx.x; i < kWaves * e; i += kTileTokens) lane_masks[i] = 0ull;
-    __syncthreads();
-
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
       if (ok[j]) atomicOr(&lane_masks[wv * e + ids[j]], 1ull << lane);
@@ -376,6 +460,10 @@ static hipError_t launch_layout_k(const int32_t* idx, const LayoutView& L, hipSt
         idx, L.s, L.e, L.k, items, tile_row_length(ntiles), L.tile_counts, L.tile_checksum,
         L.tile_flags);
   }
+  const bool prefixed = ntiles > kScanTiles;
+  if (prefixed)
+    layout_scan_kernel<<<L.e, kTileTokens, 0, stream>>>(L.tile_counts, ntiles, tile_row_length(ntiles),
+                                                        L.counts);
   int grid = ntiles < 1 ? 1 : ntiles;
   if ((L.capacity > 0 || L.pad_multiple > 1) && grid < L.e + 1)
     grid = L.e + 1 < 1024 ? L.e + 1 : 1024;  // one workgroup per padded segment
@@ -383,7 +471,7 @@ static hipError_t launch_layout_k(const int32_t* idx, const LayoutView& L, hipSt
                      (3 * static_cast<size_t>(L.e) + 1) * sizeof(int32_t);
   layout_place_kernel<KMAX, RM><<<grid, kTileTokens, lds, stream>>>(
       idx, L.s, L.e, L.k, items, L.capacity, L.pad_multiple, static_cast<int32_t>(L.rows), ntiles,
-      tile_row_length(ntiles), L.tile_counts, L.tile_checksum, L.tile_flags, L.counts, L.kept, L.offsets, L.checksum,
+      tile_row_length(ntiles), prefixed, L.tile_counts, L.tile_checksum, L.tile_flags, L.counts, L.kept, L.offsets, L.checksum,
       L.flags, L.dst, L.src, L.route_idx);
   return hipGetLastError();
 }

@@ -119,6 +119,8 @@ LAYOUT_CASES = [
     (256, 40, 3, 7, "uniform"), (257, 64, 8, 0, "uniform"), (1000, 129, 5, 40, "uniform"),
     (3000, 1024, 16, 0, "uniform"), (3000, 1024, 16, 50, "uniform"), (2049, 16, 4, 1, "skew"),
     (5000, 8, 2, 0, "skew"), (5000, 8, 8, 1000, "skew"), (700, 2, 1, 0, "uniform"),
+    # more than 256 tiles: the tile table is scanned by its own launch
+    (70000, 64, 2, 0, "uniform"), (90000, 128, 8, 4000, "skew"),
 ]
 
 
@@ -131,7 +133,7 @@ def test_layout_random_cases(s, e, k, cap, routing):
     check_layout(Lg, oracle.dispatch_layout(idx, e, cap), f"s={s} e={e} k={k} c={cap}")
 
 
-@pytest.mark.parametrize("s", [600, 200])  # several tiles; one tile (no count launch)
+@pytest.mark.parametrize("s", [600, 200, 70000])  # several tiles; one (no count launch); > 256 (scanned)
 @pytest.mark.parametrize("cap", [0, 3])
 def test_layout_invalid_routes_are_flagged_and_skipped(cap, s):
     announce("layout invalid", cap, s)

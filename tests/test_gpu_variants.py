@@ -27,6 +27,8 @@ OPTION_CASES = [
     (1000, 40, 3, 30, True, 1), (1000, 40, 3, 0, True, 1), (257, 8, 8, 40, True, 1),
     (3000, 129, 5, 0, False, 16), (3000, 129, 5, 0, True, 128), (1, 3, 2, 0, False, 4),
     (0, 5, 2, 0, False, 8), (777, 1024, 16, 0, True, 1), (5000, 8, 2, 300, True, 1),
+    # more than 256 tiles of items (tokens, or routes in route-major order)
+    (40000, 128, 8, 0, True, 1), (70000, 129, 5, 0, False, 16), (9000, 40, 8, 1500, True, 1),
 ]
 
 

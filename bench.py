@@ -505,7 +505,8 @@ def run_cpu_baseline(w: W.Workload, variant: str | None = None, step_seconds: fl
     """The oracle, as it stands, on the host's CPU, single-threaded.
 
     value: the metric's scope. The vectorised oracle's dispatch + combine, given the
-    layout, on the same full host arrays as the GPU, median of 3 (tokens = s). Parts:
+    layout, on the same full host arrays as the GPU, median of 3 (tokens = s); beside it
+    the gate and the layout on the same arrays, each the median of 3. Parts:
     the whole step on the first `sample_tokens` tokens for about `step_seconds`; and the
     loop oracle (plain per-element Python loops) over the whole step of the tiny
     capacity-bounded workload, and its dispatch + combine on the first `loop_tokens`
@@ -524,8 +525,20 @@ def run_cpu_baseline(w: W.Workload, variant: str | None = None, step_seconds: fl
            "host": f"{_cpu_model()}, {os.cpu_count()} logical CPUs (one used)"}
 
     if variant != "expert_gemm":
-        idx, wt = oracle.gate_topk(inp.logits, w.k)
-        L = oracle.dispatch_layout(idx, w.e, w.capacity, **opts)
+        # the gate and the layout on the same full arrays, each the median of 3
+        tg, tl = [], []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            idx, wt = oracle.gate_topk(inp.logits, w.k)
+            t1 = time.perf_counter()
+            L = oracle.dispatch_layout(idx, w.e, w.capacity, **opts)
+            t2 = time.perf_counter()
+            tg.append(t1 - t0)
+            tl.append(t2 - t1)
+        out["gate"] = {"tokens_per_s": round(w.s / float(np.median(tg)), 1),
+                       "ms": round(float(np.median(tg)) * 1e3, 3)}
+        out["layout"] = {"tokens_per_s": round(w.s / float(np.median(tl)), 1),
+                         "ms": round(float(np.median(tl)) * 1e3, 3)}
         wc = oracle.renormalize_kept(L, wt) if variant == "renorm_kept" else wt
         times = []
         for _ in range(3):

@@ -58,10 +58,12 @@ def routing(name=None, s=None, e=None, k=None, seed=0):
     return torch.from_numpy(W.random_idx(rng, s, e, k)).cuda()
 
 
-# consecutive calls, each smaller than the one before: many tiles with the Zipf routing,
-# fewer tiles with a capacity drop, route-major priority, padded segments, and one tile
-# (where the build uses no tables at all)
+# consecutive calls, each smaller than the one before: more than 256 tiles (the tile table
+# scanned by its own launch), many tiles with the Zipf routing, fewer tiles with a capacity
+# drop, route-major priority, padded segments, and one tile (where the build uses no
+# tables at all)
 CALLS = [
+    ("s=70000 e=64 k=2 dropless, 274 tiles", dict(s=70000, e=64, k=2, seed=6), 64, 0, False, 1),
     ("zipf_skew_h4096 routing, dropless", dict(name="zipf_skew_h4096"), 128, 0, False, 1),
     ("s=3000 e=64 k=4 capacity 150", dict(s=3000, e=64, k=4, seed=1), 64, 150, False, 1),
     ("s=900 e=32 k=2 capacity 40 route-major", dict(s=900, e=32, k=2, seed=2), 32, 40, True, 1),

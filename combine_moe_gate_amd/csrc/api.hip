@@ -220,21 +220,37 @@ static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 namespace {
 
-// The current device's address of `scratch`, looked up once per device with that device
-// current (each GPU holds its own copy at its own address), then kept.
-moe_status_t scratch_address(void** out) {
+// The address of `scratch` on the device the stream belongs to (the current device for
+// the null stream), looked up once per device with that device current (each GPU holds
+// its own copy at its own address; the caller's current device is restored), then kept.
+moe_status_t scratch_address(hipStream_t stream, void** out) {
   int dev = -1;
-  hipError_t err = hipGetDevice(&dev);
-  if (err != hipSuccess) return hip_status(err, "moe_dispatch_layout_static_scratch: hipGetDevice");
+  hipError_t err = hipSuccess;
+  if (stream == nullptr) {
+    err = hipGetDevice(&dev);
+  } else {
+    hipDevice_t sdev = 0;
+    err = hipStreamGetDevice(stream, &sdev);
+    dev = static_cast<int>(sdev);
+  }
+  if (err != hipSuccess) return hip_status(err, "moe_dispatch_layout_static_scratch: the stream's device");
   if (dev < 0 || dev >= kMaxDevices)
     return fail(MOE_ERR_UNSUPPORTED, "device %d is beyond the %d devices the static scratch tracks",
                 dev, kMaxDevices);
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   if (g_scratch_addr[dev] == nullptr) {
+    int cur = -1;
+    err = hipGetDevice(&cur);
+    if (err != hipSuccess) return hip_status(err, "moe_dispatch_layout_static_scratch: hipGetDevice");
+    if (cur != dev && (err = hipSetDevice(dev)) != hipSuccess)
+      return hip_status(err, "moe_dispatch_layout_static_scratch: hipSetDevice");
     void* p = nullptr;
     err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t restore = cur != dev ? hipSetDevice(cur) : hipSuccess;
     if (err != hipSuccess)
       return hip_status(err, "moe_dispatch_layout_static_scratch: hipGetSymbolAddress(scratch)");
+    if (restore != hipSuccess)
+      return hip_status(restore, "moe_dispatch_layout_static_scratch: restoring the current device");
     if (p == nullptr)
       return fail(MOE_ERR_HIP, "moe_dispatch_layout_static_scratch: hipGetSymbolAddress gave NULL");
     g_scratch_addr[dev] = p;
@@ -341,7 +357,7 @@ static moe_status_t build_layout(const int32_t* topk_idx, int32_t s, int32_t e, 
                   "scratch array (fewer tokens or experts per call, or moe_dispatch_layout_ex)",
                   what, table_bytes, kStaticScratchBytes);
     void* base = nullptr;
-    MOE_TRY(scratch_address(&base));
+    MOE_TRY(scratch_address(static_cast<hipStream_t>(stream), &base));
     tables = static_cast<char*>(base);
   }
 

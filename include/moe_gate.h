@@ -238,7 +238,8 @@ moe_status_t moe_dispatch_layout_ex(const int32_t* topk_idx, int32_t s, int32_t 
  * allocation, no memset: every table entry the build reads it wrote earlier in the same
  * call. All calls on one GPU share its array, so two of these builds enqueued on
  * different streams of one GPU that overlap in time race; builds on one stream, and
- * every other entry point, are unaffected. The stream must belong to the current device.
+ * every other entry point, are unaffected. The array used is that of the stream's device
+ * (the current device for the null stream).
  */
 #define MOE_STATIC_SCRATCH_BYTES (2u << 20)
 #define MOE_LAYOUT_ALIGN_UP(n) ((((size_t)(n)) + 255u) / 256u * 256u)

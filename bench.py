@@ -55,16 +55,20 @@ ISOLATED_RUNS = 30  # each op of the step alone after a flush
 
 # sources of the grouped expert GEMM: only the expert_gemm variant runs their kernels
 GEMM_SOURCES = ("gemm.hip", "gemm_bwd.hip", "gemm_common.h")
+# host code only (argument checks, the workspace plan, the C declarations): no kernel
+HOST_SOURCES = ("api.hip", "moe_gate.h")
 
 
 def kernel_source_digest(variant: str | None = None) -> str:
     """sha256 over the HIP sources (and build flags) whose kernels a run of `variant`
-    launches: every source for the expert_gemm variant, all but the GEMM's otherwise."""
+    launches: every kernel source for the expert_gemm variant, all but the GEMM's
+    otherwise. Host-only files are left out: they change no kernel's traffic."""
     import hashlib
     from combine_moe_gate_amd import _build
     h = hashlib.sha256()
     for path in sorted(_build.SOURCES + _build.HEADERS):
-        if variant != "expert_gemm" and os.path.basename(path) in GEMM_SOURCES:
+        name = os.path.basename(path)
+        if name in HOST_SOURCES or (variant != "expert_gemm" and name in GEMM_SOURCES):
             continue
         with open(path, "rb") as f:
             h.update(f.read())

@@ -128,3 +128,20 @@ def test_loop_oracle_sample_times_the_first_tokens_with_the_capacity_scaled():
     assert r["tokens_per_s"] > 0 and r["seconds"] > 0
     # capacity 80 of 256 tokens, scaled to 4 tokens: ceil(80 * 4 / 256) = 2
     assert r["sample"] == "first 4 of 256 tokens (m=64, e=8, k=2, f32, capacity scaled to 2)"
+
+
+def test_host_only_sources_do_not_change_the_digest(monkeypatch):
+    real_open = open
+
+    def edited_host(path, mode="r", *a, **k):
+        f = real_open(path, mode, *a, **k)
+        if (path.endswith("api.hip") or path.endswith("moe_gate.h")) and "b" in mode:
+            data = f.read() + b"// edit"
+            f.close()
+            import io
+            return io.BytesIO(data)
+        return f
+
+    before = (bench.kernel_source_digest(), bench.kernel_source_digest("expert_gemm"))
+    monkeypatch.setattr("builtins.open", edited_host)
+    assert (bench.kernel_source_digest(), bench.kernel_source_digest("expert_gemm")) == before

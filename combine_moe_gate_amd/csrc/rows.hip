@@ -20,14 +20,14 @@
 //                     PR "MoE dispatch: fix silent Tutel + TP corruption, speed up
 //                     native and Tutel paths", part 3: fp32 accumulation; PR 8213's
 //                     review thread on combine weights: the weights are applied).
-//   dispatch backward the same kernel without weights (the gradient of a dispatch is
-//                     a combine, PR 8213 first commit).
+//   dispatch backward the same kernel without weights (dispatch and combine are adjoint,
+//                     PR 8213 first commit).
 //   combine backward  grad_y[t] read once (normal loads, like x in dispatch: measured
 //                     faster than nontemporal ones); each route gets the weighted copy in its row
 //                     and the dot product with its expert row accumulates in float64,
 //                     per wave, then across the workgroup's waves through LDS in a
-//                     fixed order (the gradient of a combine is a dispatch, plus the
-//                     weights' gradient of PR 8213's review-fix commit).
+//                     fixed order (the combine's adjoint, plus the weights' gradient of
+//                     PR 8213's review-fix commit).
 //
 //   weighted dispatch the combine backward's scatter without the dot: out[dst] = w * x
 //                     (the weights applied before the experts; PR 8213's score_apply).

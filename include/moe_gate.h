@@ -328,8 +328,8 @@ moe_status_t moe_combine(const moe_layout_t* layout, const void* expert_out,
                          void* stream);
 
 /*
- * (5) Combine backward ([DS-8213] first commit: the gradient of a combine is a dispatch;
- * review-fix commit: the weights' gradient is returned):
+ * (5) Combine backward ([DS-8213] first commit: dispatch and combine are adjoint, so this is
+ * a weighted dispatch; review-fix commit: the weights' gradient is returned):
  *   grad_expert_out[dst[t,j]] = topk_w[t,j] * grad_y[t] (float32 product, rounded to
  *   dtype); rows no route points at are zero.
  *   grad_w[t,j] = sum_m grad_y[t,m] * E[dst[t,j],m], accumulated in float64 and rounded
@@ -342,7 +342,7 @@ moe_status_t moe_combine_backward(const moe_layout_t* layout, const void* grad_y
                                   void* stream);
 
 /*
- * (5) Dispatch backward ([DS-8213] first commit: the gradient of a dispatch is a combine):
+ * (5) Dispatch backward ([DS-8213] first commit: the dispatch's adjoint, an unweighted combine):
  *   grad_x[t] = sum over placed routes j, in order, of grad_out[dst[t,j]], float32
  *   accumulation, rounded once to dtype.
  *   grad_out [rows, m];  grad_x [s, m].

@@ -348,8 +348,8 @@ def combine_backward(layout: Layout, grad_y: np.ndarray, expert_out: np.ndarray,
                      w: np.ndarray, dtype: str) -> tuple[np.ndarray, np.ndarray]:
     """Gradients of combine: a weighted dispatch of grad_y, and the weight gradient.
 
-    [DS-8213] first commit: the gradient of a combine is a dispatch on the same
-    handle. grad_E[dst[t,j]] = w[t,j] * grad_y[t] (float32 product, rounded to
+    [DS-8213] first commit: combine and dispatch are adjoint, so this backward is a
+    weighted dispatch on the same handle. grad_E[dst[t,j]] = w[t,j] * grad_y[t] (float32 product, rounded to
     the element type), rows no route points to are zero. [DS-8213] review-fix
     commit: the weights' gradient grad_w[t,j] = <grad_y[t], E[dst[t,j]]> must be
     returned (zero for a dropped route).
@@ -372,8 +372,8 @@ def combine_backward(layout: Layout, grad_y: np.ndarray, expert_out: np.ndarray,
 def dispatch_backward(layout: Layout, grad_out: np.ndarray, dtype: str) -> np.ndarray:
     """Gradient of dispatch: an unweighted combine of the buffer gradient.
 
-    [DS-8213] first commit: the gradient of a dispatch is a combine on the same
-    handle. grad_x[t] = sum over placed routes of grad_out[dst[t,j]], float32
+    [DS-8213] first commit: by the same adjointness this backward is an unweighted
+    combine on the same handle. grad_x[t] = sum over placed routes of grad_out[dst[t,j]], float32
     in route order, rounded once.
     """
     acc = _route_sum(layout, to_f32(grad_out, dtype), None)
@@ -516,7 +516,8 @@ def expert_gemm_dgrad(layout: Layout, grad_out: np.ndarray, weights: np.ndarray,
     is then the dispatch backward of grad_A (each token sums its routes' rows), the same
     route-order sum as every other dispatch backward. The sums are exact (float64), rounded
     to float32 as a float32 accumulator holds them, then once to the element type.
-    [DS-8213] first commit: the gradient of a dispatch is a combine on the same handle;
+    [DS-8213] first commit: the backward runs through the forward's handle (dispatch and
+    combine are adjoint);
     review-fix commit: the groups are the offsets' segments.
     Returns (grad_A, exact float64).
     """

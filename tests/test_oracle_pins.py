@@ -75,7 +75,7 @@ def brute_layout(idx, e, capacity):
 
 
 def dense_masks(layout, w):
-    """The dense [s, e, c] one-hot dispatch mask and combine weights of the old path."""
+    """The old path's dense dispatch mask ([s, e, c], one-hot) and its combine weights."""
     s, k, e = layout.s, layout.k, layout.e
     if layout.capacity > 0:
         c = layout.capacity

@@ -267,7 +267,8 @@ moe_status_t moe_dispatch(const moe_layout_t* layout, const void* x, int32_t m,
  * buffer as moe_dispatch, without rebuilding the layout. If topk_idx is not NULL it is
  * compared route by route with the routing the layout was built from, and any
  * difference sets MOE_FLAG_REPLAY_MISMATCH in the layout's flags (the copy is still
- * made from the saved layout).
+ * made from the saved layout). The bit is never cleared by a later replay: it stays set
+ * until the layout is built again in that workspace.
  */
 moe_status_t moe_dispatch_replay(const moe_layout_t* layout, const int32_t* topk_idx,
                                  const void* x, int32_t m, moe_dtype_t dtype, void* out,

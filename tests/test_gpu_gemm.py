@@ -173,10 +173,21 @@ def sampled_sub_layout(Lo: oracle.Layout, rows: np.ndarray):
     return sub, experts, rows
 
 
-def test_expert_gemm_full_workload_sampled():
-    """The headline workload's routing and rows at the benchmark's expert width; outputs
-    sampled at segment edges, tile edges and random rows are checked against the oracle."""
-    name = W.HEADLINE
+# full size: the headline (256-row tiles, Zipf segments), the f16 capacity workload
+# (256-row tiles over a padded [e, c] buffer) and the 4096-token dropless one (128-row tiles)
+FULL_GEMM_WORKLOADS = [W.HEADLINE, "gshard_capacity_drop", "dropless_top8_h2816"]
+
+
+def placed_rows(Lo: oracle.Layout, rng: np.random.Generator, count: int) -> list:
+    """Random placed rows (capacity buffers also hold padding rows, which no token fills)."""
+    placed = np.nonzero(Lo.src >= 0)[0]
+    return rng.choice(placed, min(count, len(placed)), replace=False).tolist()
+
+
+@pytest.mark.parametrize("name", FULL_GEMM_WORKLOADS)
+def test_expert_gemm_full_workload_sampled(name):
+    """A workload's routing and rows at the benchmark's expert width; outputs sampled at
+    segment edges, tile edges and random rows are checked against the oracle."""
     inp = W.make_inputs(name)
     w = inp.workload
     n = W.EXPERT_WIDTH
@@ -200,7 +211,7 @@ def test_expert_gemm_full_workload_sampled():
         for d in (0, 127, 128, kx - 1):
             if 0 <= d < kx:
                 pick.add(r0 + d)
-    pick.update(rng.choice(Lo.rows, 24, replace=False).tolist())
+    pick.update(placed_rows(Lo, rng, 24))
     rows = np.array(sorted(pick))
     sub, experts, rows = sampled_sub_layout(Lo, rows)
     got = to_host(fused.index_select(0, torch.from_numpy(rows).cuda()))
@@ -371,12 +382,12 @@ def test_expert_gemm_wgrad_empty_layout_zeroes_everything():
     assert int(out.view(torch.int32).abs().sum()) == 0
 
 
-def test_expert_gemm_wgrad_full_workload_sampled():
-    """The headline routing and rows at the benchmark's expert width; a block of sampled
+@pytest.mark.parametrize("name", FULL_GEMM_WORKLOADS)
+def test_expert_gemm_wgrad_full_workload_sampled(name):
+    """A workload's routing and rows at the benchmark's expert width; a block of sampled
     output features x input features of every expert is checked against the oracle (the
     gradient separates over output and input features, so the oracle runs on those
     columns only)."""
-    name = W.HEADLINE
     inp = W.make_inputs(name)
     w = inp.workload
     n = W.EXPERT_WIDTH
@@ -464,8 +475,8 @@ def test_expert_gemm_dgrad_integer_operands_bit_exact(dtype):
     assert_bits_equal(to_host(got), want, "integer operands")
 
 
-def test_expert_gemm_dgrad_full_workload_sampled():
-    name = W.HEADLINE
+@pytest.mark.parametrize("name", FULL_GEMM_WORKLOADS)
+def test_expert_gemm_dgrad_full_workload_sampled(name):
     inp = W.make_inputs(name)
     w = inp.workload
     n = W.EXPERT_WIDTH
@@ -484,7 +495,7 @@ def test_expert_gemm_dgrad_full_workload_sampled():
         for d in (0, 255, 256, kx - 1):
             if 0 <= d < kx:
                 pick.add(r0 + d)
-    pick.update(rng.choice(Lo.rows, 24, replace=False).tolist())
+    pick.update(placed_rows(Lo, rng, 24))
     sub, experts, rows = sampled_sub_layout(Lo, np.array(sorted(pick)))
     got = to_host(ga.index_select(0, torch.from_numpy(rows).cuda()))
     check_dgrad(got, sub, np.ascontiguousarray(g[rows]), np.ascontiguousarray(wts[experts]), w.dtype,

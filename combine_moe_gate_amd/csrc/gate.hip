@@ -3,11 +3,14 @@
 // The gate: one wave64 per token. The e logits of a row sit in registers, ceil(e/64) per lane,
 // as 32-bit order-preserving images of the float32 values (element i at lane i mod 64,
 // slot i / 64). Each of the k rounds takes the wave-wide maximum of the untaken keys
-// (DPP max steps plus four readlanes), then finds the lowest expert id holding it with
-// one ballot per slot (ids of slot v are all below those of slot v+1), so ties go to
-// the lower id; the owner marks it taken. The experts come out in descending order.
+// (DPP max steps plus four readlanes), then finds the lowest expert id holding it, so
+// ties go to the lower id, and the owner marks it taken. With up to 8 slots that is one
+// ballot per slot until one hits (ids of slot v are all below those of slot v+1); with 16
+// (e > 512), whose ballot loop the compiler leaves rolled, a wave-wide minimum of each
+// lane's lowest id holding the maximum (2.8x faster there, slower below). The experts come out in descending order.
 // The weights are a softmax over the k selected logits, formed in float64 (equal to
-// the full softmax renormalised over the selection: the full denominator cancels) --
+// the full softmax renormalised over the selection: the full denominator cancels), for
+// the workgroup's four tokens at once in one wave, one 16-lane row per token --
 // DeepSpeed PR "MoE dispatch: fix silent Tutel + TP corruption, speed up native and
 // Tutel paths", part 1: the gate hands on per-route expert ids and gate values, not a
 // dense mask. (A 16-lane-row form with four tokens per wave, as the backward below uses,
@@ -35,57 +38,78 @@ __global__ __launch_bounds__(kBlock) void gate_topk_kernel(const float* __restri
                                                            int s, int e, int k,
                                                            int32_t* __restrict__ idx_out,
                                                            float* __restrict__ w_out) {
+  // The softmax over each token's k selections runs once per workgroup, in wave 0: row q
+  // (16 lanes) of that wave takes token q of the workgroup, lane r its route r (k <= 16).
+  // Done in every wave instead, it would cost each token a whole wave's float64 work.
+  static_assert(kWavesPerBlock * 16 == kWave, "one 16-lane row per token of the workgroup");
+  __shared__ float sel_logit[kWavesPerBlock][16];
   const int lane = lane_id();
-  const int t = blockIdx.x * kWavesPerBlock + wave_in_block();
-  if (t >= s) return;
-  const float* row = logits + static_cast<size_t>(t) * e;
-
-  uint32_t key[VPL];
-  bool taken[VPL];
-#pragma unroll
-  for (int v = 0; v < VPL; ++v) {
-    const int i = lane + v * kWave;
-    taken[v] = i >= e;  // lanes past e never compete
-    key[v] = taken[v] ? 0u : ordered_key(row[i]);
-  }
-
-  int my_idx = 0;      // lane r keeps the r-th selection
-  uint32_t my_key = 0;
-  for (int r = 0; r < k; ++r) {
-    uint32_t best = 0;
+  const int wv = wave_in_block();
+  const int t0 = blockIdx.x * kWavesPerBlock;
+  const int t = t0 + wv;
+  if (t < s) {  // uniform per wave; every wave still meets the barrier below
+    const float* row = logits + static_cast<size_t>(t) * e;
+    uint32_t key[VPL];
+    bool taken[VPL];
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
-      const uint32_t kv = taken[v] ? 0u : key[v];
-      best = kv > best ? kv : best;
+      const int i = lane + v * kWave;
+      taken[v] = i >= e;  // lanes past e never compete
+      key[v] = taken[v] ? 0u : ordered_key(row[i]);
     }
-    best = wave_max_u32(best);
-    int sel = 0;
+
+    int my_idx = 0;  // lane r keeps the r-th selection
+    uint32_t my_key = 0;
+    for (int r = 0; r < k; ++r) {
+      uint32_t best = 0;
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const uint64_t hit = __ballot(!taken[v] && key[v] == best);
-      if (hit != 0ull) {  // uniform: the lowest id with the maximum is in slot v
-        const int owner = static_cast<int>(__builtin_ctzll(hit));
-        sel = owner + v * kWave;
-        if (lane == owner) taken[v] = true;
-        break;
+      for (int v = 0; v < VPL; ++v) {
+        const uint32_t kv = taken[v] ? 0u : key[v];
+        best = kv > best ? kv : best;
+      }
+      best = wave_max_u32(best);
+      int sel = 0;
+      if constexpr (VPL <= 8) {
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+          const uint64_t hit = __ballot(!taken[v] && key[v] == best);
+          if (hit != 0ull) {  // uniform: the lowest id with the maximum is in slot v
+            const int owner = static_cast<int>(__builtin_ctzll(hit));
+            sel = owner + v * kWave;
+            if (lane == owner) taken[v] = true;
+            break;
+          }
+        }
+      } else {  // 16 slots: each lane's lowest id holding the maximum, then their minimum
+        uint32_t mine = 0xffffffffu;
+#pragma unroll
+        for (int v = VPL - 1; v >= 0; --v)
+          if (!taken[v] && key[v] == best) mine = static_cast<uint32_t>(lane + v * kWave);
+        sel = static_cast<int>(wave_min_u32(mine));
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+          if (sel == lane + v * kWave) taken[v] = true;
+      }
+      if (lane == r) {
+        my_idx = sel;
+        my_key = best;
       }
     }
-    if (lane == r) {
-      my_idx = sel;
-      my_key = best;
+    if (lane < k) {
+      idx_out[static_cast<size_t>(t) * k + lane] = my_idx;
+      sel_logit[wv][lane] = key_to_float(my_key);
     }
   }
+  __syncthreads();
+  if (wv != 0) return;
 
-  const bool active = lane < k;
-  const float l = key_to_float(my_key);
-  const float l0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, l)));
-  const double ex = active ? exp(static_cast<double>(l) - static_cast<double>(l0)) : 0.0;
-  const double denom = wave_sum(ex);
-  if (active) {
-    const size_t o = static_cast<size_t>(t) * k + lane;
-    idx_out[o] = my_idx;
-    w_out[o] = static_cast<float>(ex / denom);
-  }
+  // w_r = exp(l_r - l_0) / sum_q exp(l_q - l_0) in float64, l_0 the largest selection
+  const int q = lane >> 4, r = lane & 15;
+  const bool active = t0 + q < s && r < k;
+  const double ex = active ? exp(static_cast<double>(sel_logit[q][r]) - static_cast<double>(sel_logit[q][0]))
+                           : 0.0;
+  const double denom = row_sum_f64(ex);  // all lanes active here
+  if (active) w_out[static_cast<size_t>(t0 + q) * k + r] = static_cast<float>(ex / denom);
 }
 
 // Gate backward: grad_logits[idx_j] = w_j (grad_w_j - sum_q w_q grad_w_q), float64,

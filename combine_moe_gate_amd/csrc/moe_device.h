@@ -161,6 +161,20 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return step(step(a, b), step(c, d));
 }
 
+// 32-bit minimum over the 64 lanes, returned uniformly (the same steps as the maximum).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  auto step = [](uint32_t x, uint32_t y) { return x < y ? x : y; };
+  v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xb1, 0xf, 0xf, false)));
+  v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4e, 0xf, 0xf, false)));
+  v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x141, 0xf, 0xf, false)));
+  v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x140, 0xf, 0xf, false)));
+  const uint32_t a = __builtin_amdgcn_readlane(static_cast<int>(v), 0);
+  const uint32_t b = __builtin_amdgcn_readlane(static_cast<int>(v), 16);
+  const uint32_t c = __builtin_amdgcn_readlane(static_cast<int>(v), 32);
+  const uint32_t d = __builtin_amdgcn_readlane(static_cast<int>(v), 48);
+  return step(step(a, b), step(c, d));
+}
+
 // Sum over one DPP row (16 lanes), the result in every lane of the row: the four in-row
 // steps of the wave reductions above, without the cross-row readlanes. All lanes must be
 // active.

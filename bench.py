@@ -24,6 +24,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -59,10 +60,21 @@ GEMM_SOURCES = ("gemm.hip", "gemm_bwd.hip", "gemm_common.h")
 HOST_SOURCES = ("api.hip", "moe_gate.h")
 
 
+_COMMENT = re.compile(rb"//[^\n]*|/\*.*?\*/", re.S)
+
+
+def source_code_bytes(text: bytes) -> bytes:
+    """A source's code without its comments and with runs of whitespace folded to one
+    space: what a digest of kernel code should see (the kernel sources hold no string
+    literals with comment markers)."""
+    return b" ".join(_COMMENT.sub(b" ", text).split())
+
+
 def kernel_source_digest(variant: str | None = None) -> str:
-    """sha256 over the HIP sources (and build flags) whose kernels a run of `variant`
-    launches: every kernel source for the expert_gemm variant, all but the GEMM's
-    otherwise. Host-only files are left out: they change no kernel's traffic."""
+    """sha256 over the code of the HIP sources (and the build flags) whose kernels a run
+    of `variant` launches: every kernel source for the expert_gemm variant, all but the
+    GEMM's otherwise. Host-only files are left out, and so are comments and layout:
+    neither changes a kernel's traffic."""
     import hashlib
     from combine_moe_gate_amd import _build
     h = hashlib.sha256()
@@ -71,7 +83,7 @@ def kernel_source_digest(variant: str | None = None) -> str:
         if name in HOST_SOURCES or (variant != "expert_gemm" and name in GEMM_SOURCES):
             continue
         with open(path, "rb") as f:
-            h.update(f.read())
+            h.update(source_code_bytes(f.read()))
     h.update(" ".join(_build.FLAGS).encode())
     return h.hexdigest()[:16]
 

@@ -7,7 +7,8 @@
 // ties go to the lower id, and the owner marks it taken. With up to 8 slots that is one
 // ballot per slot until one hits (ids of slot v are all below those of slot v+1); with 16
 // (e > 512), whose ballot loop the compiler leaves rolled, a wave-wide minimum of each
-// lane's lowest id holding the maximum (2.8x faster there, slower below). The experts come out in descending order.
+// lane's lowest id holding the maximum (2.8x faster there, slower below). The experts
+// come out in descending order.
 // The weights are a softmax over the k selected logits, formed in float64 (equal to
 // the full softmax renormalised over the selection: the full denominator cancels), for
 // the workgroup's four tokens at once in one wave, one 16-lane row per token --

@@ -68,7 +68,7 @@ def test_gemm_sources_only_change_the_gemm_variant_digest(monkeypatch):
     def edited_gemm(path, mode="r", *a, **k):
         f = real_open(path, mode, *a, **k)
         if path.endswith("gemm.hip") and "b" in mode:
-            data = f.read() + b"// edit"
+            data = f.read() + b"\nstatic int digest_probe;\n"
             f.close()
             import io
             return io.BytesIO(data)
@@ -136,7 +136,7 @@ def test_host_only_sources_do_not_change_the_digest(monkeypatch):
     def edited_host(path, mode="r", *a, **k):
         f = real_open(path, mode, *a, **k)
         if (path.endswith("api.hip") or path.endswith("moe_gate.h")) and "b" in mode:
-            data = f.read() + b"// edit"
+            data = f.read() + b"\nstatic int digest_probe;\n"
             f.close()
             import io
             return io.BytesIO(data)
@@ -145,3 +145,33 @@ def test_host_only_sources_do_not_change_the_digest(monkeypatch):
     before = (bench.kernel_source_digest(), bench.kernel_source_digest("expert_gemm"))
     monkeypatch.setattr("builtins.open", edited_host)
     assert (bench.kernel_source_digest(), bench.kernel_source_digest("expert_gemm")) == before
+
+
+def _digests_with_gate_edit(monkeypatch, tail: bytes):
+    real_open = open
+
+    def edited(path, mode="r", *a, **k):
+        f = real_open(path, mode, *a, **k)
+        if path.endswith("gate.hip") and "b" in mode:
+            data = f.read() + tail
+            f.close()
+            import io
+            return io.BytesIO(data)
+        return f
+
+    monkeypatch.setattr("builtins.open", edited)
+    out = (bench.kernel_source_digest(), bench.kernel_source_digest("expert_gemm"))
+    monkeypatch.undo()
+    return out
+
+
+def test_comments_and_layout_do_not_change_the_digest_but_code_does(monkeypatch):
+    before = (bench.kernel_source_digest(), bench.kernel_source_digest("expert_gemm"))
+    assert _digests_with_gate_edit(monkeypatch, b"\n// a note\n/* and a\n block */\n\n") == before
+    code = _digests_with_gate_edit(monkeypatch, b"\nstatic int digest_probe;\n")
+    assert code[0] != before[0] and code[1] != before[1]
+
+
+def test_source_code_bytes_drops_comments_and_folds_whitespace():
+    src = b"int a; // one\n/* two\n three */  int\tb;\n"
+    assert bench.source_code_bytes(src) == b"int a; int b;"

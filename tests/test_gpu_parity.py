@@ -75,7 +75,7 @@ def test_gate_matches_oracle_on_workload(name):
 def test_gate_ties_signed_zeros_and_shapes(e, k):
     announce("gate ties", e, k)
     rng = np.random.default_rng(e * 100 + k)
-    s = 300
+    s = 300 + (e + k) % 4  # the last workgroup of four tokens partly filled, in most cases
     logits = rng.integers(-2, 3, size=(s, e)).astype(np.float32)
     logits[rng.random((s, e)) < 0.2] = -0.0
     logits[:5] = 0.0  # all-equal rows
@@ -83,6 +83,20 @@ def test_gate_ties_signed_zeros_and_shapes(e, k):
     idx_o, wt_o = oracle.gate_topk(logits, k)
     assert_bits_equal(to_host(idx), idx_o, "idx")
     assert f32_ulps(to_host(wt), wt_o).max() <= 1
+
+
+@pytest.mark.parametrize("e,k", [(8, 2), (128, 8), (600, 16)])
+def test_gate_batches_smaller_than_a_workgroup(e, k):
+    """One to seven tokens: a workgroup forms the weights of its four tokens in one wave,
+    so a batch that leaves some of those four empty must still give every token's."""
+    announce("gate small batches", e, k)
+    rng = np.random.default_rng(e + 17 * k)
+    for s in range(1, 8):
+        logits = rng.standard_normal((s, e)).astype(np.float32)
+        idx, wt = M.moe_gate_topk(to_dev(logits), k)
+        idx_o, wt_o = oracle.gate_topk(logits, k)
+        assert_bits_equal(to_host(idx), idx_o, f"idx s={s}")
+        assert f32_ulps(to_host(wt), wt_o).max() <= 1, s
 
 
 def test_gate_backward_matches_oracle():

@@ -441,6 +441,47 @@ def test_several_live_layouts():
         assert_bits_equal(to_host(gx), oracle.dispatch_backward(Lo, oracle.dispatch(Lo, x), "bf16"), "gx")
 
 
+def _pipeline(logits, x, gy, k, e, cap):
+    """Forward and backward of the whole path on the current stream; every output kept."""
+    idx, wt = M.moe_gate_topk(logits, k)
+    L = M.moe_dispatch_layout(idx, e, cap)
+    buf = M.moe_dispatch(L, x)
+    y = M.moe_combine(L, buf, wt)
+    gE, gw = M.moe_combine_backward(L, gy, buf, wt)
+    gx = M.moe_dispatch_backward(L, gE)
+    gl = M.moe_gate_topk_backward(idx, wt, gw, e)
+    return {"idx": idx, "w": wt, "dst": L.dst, "src": L.src, "counts": L.counts,
+            "offsets": L.offsets, "buf": buf, "y": y, "gE": gE, "gw": gw, "gx": gx, "gl": gl}
+
+
+def test_two_streams_at_once_match_one_after_the_other():
+    """Two independent pipelines enqueued on two streams of default priority run
+    concurrently, each with its own workspace: no state is shared between calls, so
+    each stream's outputs equal, byte for byte, the same pipeline run alone."""
+    announce("two streams")
+    rng = np.random.default_rng(21)
+    s, e, k, m = 4096, 64, 4, 1024
+    ins = []
+    for cap in (0, 300):
+        logits = to_dev(W.routing_logits(rng, s, e, "uniform"))
+        x = to_dev(W.cast_input(rng.standard_normal((s, m)).astype(np.float32), "bf16"), "bf16")
+        gy = to_dev(W.cast_input(rng.standard_normal((s, m)).astype(np.float32), "bf16"), "bf16")
+        ins.append((logits, x, gy, k, e, cap))
+    alone = [_pipeline(*a) for a in ins]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    together = [None, None]
+    for i, st in enumerate(streams):
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            together[i] = _pipeline(*ins[i])
+    torch.cuda.synchronize()
+    for i in range(2):
+        for name, t in alone[i].items():
+            u = together[i][name]
+            assert torch.equal(t.contiguous().view(torch.uint8), u.contiguous().view(torch.uint8)), (i, name)
+
+
 @pytest.mark.parametrize("cap", [0, 4])
 def test_empty_batch(cap):
     announce("empty", cap)

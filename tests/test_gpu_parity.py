@@ -99,6 +99,27 @@ def test_gate_batches_smaller_than_a_workgroup(e, k):
         assert f32_ulps(to_host(wt), wt_o).max() <= 1, s
 
 
+def test_gate_random_shapes():
+    """60 seeded shapes: e from 1 to 1024 (one to sixteen logits per lane), k up to 16, s up
+    to 3000 (partly filled last workgroups), a third of them on a coarse grid of logits so
+    that ties between experts are common."""
+    for seed in range(60):
+        rng = np.random.default_rng(50_000 + seed)
+        e = int(rng.choice([1, 2, 7, 8, 63, 64, 65, 128, 129, 256, 300, 512, 513, 777, 1024]))
+        k = int(rng.integers(1, min(e, 16) + 1))
+        s = int(rng.integers(1, 3000))
+        announce("gate random", seed, s, e, k)
+        if rng.random() < 0.35:
+            logits = rng.integers(-3, 4, size=(s, e)).astype(np.float32)
+            logits[rng.random((s, e)) < 0.1] = -0.0
+        else:
+            logits = (rng.standard_normal((s, e)) * rng.choice([0.01, 1.0, 30.0])).astype(np.float32)
+        idx, wt = M.moe_gate_topk(to_dev(logits), k)
+        idx_o, wt_o = oracle.gate_topk(logits, k)
+        assert_bits_equal(to_host(idx), idx_o, f"idx seed {seed}")
+        assert f32_ulps(to_host(wt), wt_o).max() <= 1, seed
+
+
 def test_gate_backward_matches_oracle():
     announce("gate backward")
     rng = np.random.default_rng(9)
